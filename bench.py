@@ -1,0 +1,213 @@
+"""Benchmark of the fused MXFP4 quant + a4w4 GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload skinny]
+
+A step is one gemm_a4w4_fused call (dynamic quantisation of A, the
+block-scaled FP4 GEMM, bf16 store) on one batch of synthetic input; B is
+quantised and packed once beforehand (offline, untimed). Inputs are resident in
+HBM before the timed region. To measure HBM rather than the 256 MB Infinity
+Cache, the timed steps rotate through enough distinct operand sets (A, packed
+B, C) to exceed 512 MB. The K timed steps are captured once in a HIP graph and
+replayed between two HIP events on the launching stream, after W untimed warm-up
+steps. Prints ONE JSON line.
+
+The CPU oracle is timed beside it (the cpu_baseline leg, rank 0 only) on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+FP4_PEAK_TFLOPS = 10100.0   # MI355X dense MXFP4 matrix peak, TFLOP/s
+METRIC = "µs/call, TFLOP/s and HBM GB/s (% of peak) for quant+a4w4 GEMM, M=16..4096"
+ROTATE_BYTES = 512 << 20
+
+
+def alg_bytes(M, N, K):
+    """A bf16 read once + B codes + B scales + C bf16 written once (the quantised A is never stored)."""
+    return 2 * M * K + N * K // 2 + N * K // 32 + 2 * M * N
+
+
+def alg_flops(M, N, K):
+    return 2 * M * N * K
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default="skinny", choices=["tiny", "skinny", "stress", "square", "grouped"])
+    p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--warm-cache", action="store_true", help="reuse one operand set (Infinity Cache resident)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="time an eager launch loop instead of a graph replay")
+    return p.parse_args()
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(w, unit, budget_s=20.0):
+    """Time the oracle (untuned) on a bounded sample of the workload, scaled to the metric's unit."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    name = w["name"]
+    if name == "grouped":
+        a, b = w["A"][0], w["B"][0]
+    else:
+        a, b = w["A"], w["B"]
+    M, K = a.shape
+    N = b.shape[0]
+    bq, bs = oracle.quant_mx(b)  # B's quantisation is offline for the GPU too: excluded
+    rows = np.arange(min(M, 64))
+    sample_desc = (f"oracle gemm_ref (quant A, dequant A and B, fp64 matmul, bf16 round) on rows 0..{len(rows) - 1} "
+                   f"of A against the full B (N={N}, K={K})")
+    times = []
+    t_end = time.perf_counter() + budget_s
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm_ref(a[rows], bq, bs)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() > t_end or len(times) >= 10:
+            break
+    t = float(np.median(times))
+    m = len(rows)
+    value = alg_flops(m, N, K) / t / 1e12 if unit == "TFLOP/s" else alg_bytes(m, N, K) / t / 1e9
+    return dict(value=round(value, 6), unit=unit, cores=int(threads), kind="oracle",
+                sample=f"{sample_desc}; median of {len(times)} runs, {t * 1e3:.1f} ms each")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build measures the single-GPU "
+              "kernel and has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mxfp4_block_scaled_02_amd import ops, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    name = args.workload
+    seed = synth.default_seed(name) if args.seed is None else args.seed
+    log(f"[bench] workload={name} seed={seed}: generating inputs")
+    w = synth.workload(name, seed)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def prep_b(b_bits):
+        bq, bs = ops.quant(bf16(b_bits))  # offline weight quantisation on the GPU (same kernel family)
+        return ops.pack_B(bq, bs)
+
+    if name == "grouped":
+        Ms, N, K = w["Ms"], w["N"], w["K"]
+        total_bytes = sum(alg_bytes(m, N, K) for m in Ms)
+        total_flops = sum(alg_flops(m, N, K) for m in Ms)
+        a0 = [bf16(x) for x in w["A"]]
+        b0 = [prep_b(x) for x in w["B"]]
+        set_bytes = sum(x.numel() * 2 for x in a0) + sum(x.numel() for x in b0) + sum(2 * m * N for m in Ms)
+    else:
+        M, N, K = w["M"], w["N"], w["K"]
+        total_bytes, total_flops = alg_bytes(M, N, K), alg_flops(M, N, K)
+        a0, b0 = bf16(w["A"]), prep_b(w["B"])
+        set_bytes = a0.numel() * 2 + b0.numel() + 2 * M * N
+    R = 1 if args.warm_cache else max(1, math.ceil(ROTATE_BYTES / set_bytes))
+    R = min(R, args.steps)
+    log(f"[bench] operand set {set_bytes / 1e6:.2f} MB, rotating {R} sets")
+    sets = []
+    for r in range(R):
+        if name == "grouped":
+            a = [x.clone() for x in a0] if r else a0
+            b = [x.clone() for x in b0] if r else b0
+            c = [torch.empty((m, N), dtype=torch.bfloat16, device=dev) for m in Ms]
+        else:
+            a = a0.clone() if r else a0
+            b = b0.clone() if r else b0
+            c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        sets.append((a, b, c))
+
+    def step(i):
+        a, b, c = sets[i % R]
+        if name == "grouped":
+            ops.grouped_gemm(a, b, N, out_list=c)
+        else:
+            ops.gemm(a, b, N, out=c)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    if args.no_graph:
+        runner = lambda: [step(i) for i in range(args.steps)]  # noqa: E731
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.steps):
+                step(i)
+        torch.cuda.synchronize()
+        g.replay()  # one untimed replay
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        runner = g.replay
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    runner()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    us = ms_step * 1e3
+    gbs = total_bytes / (ms_step * 1e-3) / 1e9
+    tflops = total_flops / (ms_step * 1e-3) / 1e12
+
+    if name == "square":
+        bound, achieved, peak, unit = "mfma", tflops, FP4_PEAK_TFLOPS, "TFLOP/s"
+    elif name == "grouped":
+        if total_flops / (FP4_PEAK_TFLOPS * 1e12) > total_bytes / (HBM_PEAK_GBS * 1e9):
+            bound, achieved, peak, unit = "mfma", tflops, FP4_PEAK_TFLOPS, "TFLOP/s"
+        else:
+            bound, achieved, peak, unit = "hbm", gbs, HBM_PEAK_GBS, "GB/s"
+    else:
+        bound, achieved, peak, unit = "hbm", gbs, HBM_PEAK_GBS, "GB/s"
+    value = achieved
+    cfg = dict(workload=name, seed=seed, cache="warm (1 set)" if R == 1 else f"cold ({R} rotated operand sets)",
+               timing="hip graph replay" if not args.no_graph else "eager launch loop")
+    if name == "grouped":
+        cfg.update(G=len(Ms), Ms=Ms, N=N, K=K)
+    else:
+        cfg.update(M=M, N=N, K=K)
+    out = dict(metric=METRIC, value=round(value, 3), unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,
+               ms_per_step=round(ms_step, 6), higher_is_better=True, scaling="weak", vs_baseline=None,
+               dtype="mxfp4 (e2m1 x e8m0, fp32 accumulate, bf16 out)", data="synthetic", config=cfg,
+               us_per_call=round(us, 3), tflops=round(tflops, 3), hbm_gbs=round(gbs, 2),
+               roofline=dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
+                             frac=round(achieved / peak, 4), traffic=None,
+                             algorithmic_bytes=total_bytes, algorithmic_flops=total_flops))
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(w, unit)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,144 @@
+/*
+ * mxfp4.h -- C ABI of libmxfp4.so: dynamic MXFP4 quantisation of a bf16
+ * activation fused with a block-scaled FP4 GEMM, for MI355X (gfx950).
+ *
+ * Format (MXFP4, OCP Microscaling Formats v1.0): each element is an E2M1 code
+ * (bit 3 sign, bits 0-2 magnitude index into {0, 0.5, 1, 1.5, 2, 3, 4, 6}),
+ * two codes per byte with the first (even k) element in the low nibble; one
+ * E8M0 scale byte s per 32 consecutive elements along K, value 2^(s-127).
+ * Quantisation rule: scale exponent floor(log2(amax)) - 2 clamped to
+ * [-127, 127], byte 127 for an all-zero block; each element x/2^e rounded to
+ * the nearest E2M1 value, ties to the even code, saturating at +-6; the sign of
+ * zero is kept. Sources: kernelbot amd-mxfp4-mm submission 517169 (module
+ * docstring: E2M1 grid, per-1x32 scales, low nibble first; the fused
+ * quant + GEMM plan), submission 683203 (docstring: scale byte 127 = 2^0,
+ * allocation-free hot path), the OCP MX v1.0 specification (shared-exponent
+ * rule).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers unless stated otherwise; the caller owns
+ *    all memory. The library allocates nothing and holds no device state.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work
+ *    is enqueued on it asynchronously; no call synchronises.
+ *  - All arguments are validated before any HIP call. On a validation error
+ *    the call returns a non-zero status, launches nothing and leaves every
+ *    output untouched. A failed launch returns MXFP4_ERR_HIP. Faults inside a
+ *    kernel surface at the caller's next synchronising HIP call.
+ *  - bf16 tensors are row-major with a row stride in ELEMENTS; byte tensors
+ *    (packed fp4x2, E8M0 scales) have row strides in BYTES.
+ *  - Inputs must be finite; NaN or Inf input gives unspecified output.
+ */
+#ifndef MXFP4_H
+#define MXFP4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MXFP4_OK = 0,
+  MXFP4_ERR_NULL = 1,            /* a required pointer is NULL                          */
+  MXFP4_ERR_SHAPE = 2,           /* M, N or K < 1, K % 32 != 0, a stride < row length,   */
+                                 /* or a size beyond the supported range                */
+  MXFP4_ERR_ALIGN = 3,           /* a pointer or row stride breaks the stated alignment  */
+  MXFP4_ERR_WORKSPACE = 4,       /* workspace NULL or smaller than *_workspace_bytes()   */
+  MXFP4_ERR_TOO_MANY_GROUPS = 5, /* G < 1 or G > MXFP4_MAX_GROUPS                        */
+  MXFP4_ERR_HIP = 6,             /* the HIP runtime rejected a launch                    */
+  MXFP4_ERR_BUFFER = 7           /* an output buffer is smaller than the size required   */
+} mxfp4_status;
+
+/* Static, human-readable name of a status code (never NULL). */
+const char* mxfp4_status_str(int status);
+
+/* ---------------------------------------------------------------------------
+ * mxfp4_quant -- quantise a bf16 matrix X[M, K] to MXFP4 along K.
+ * The standalone form of the quantisation steps of the fused path (page
+ * 683203, ``_quant_shuffled``: one program per tile of A writing fp4x2 and
+ * E8M0 bytes; here the scales are stored row-major, not shuffled).
+ *   x : bf16 [M, K], row stride ldx elements (ldx >= K). x and ldx*2 must be
+ *       multiples of 16 bytes.
+ *   q : out, fp4x2 [M, K/2], row stride ldq bytes (ldq >= K/2). q and ldq
+ *       must be multiples of 16 bytes.
+ *   s : out, E8M0 [M, K/32], row stride lds bytes (lds >= K/32), no alignment.
+ *   K % 32 == 0, M >= 1, K >= 32.
+ * ------------------------------------------------------------------------- */
+int mxfp4_quant(const void* x, int64_t ldx, void* q, int64_t ldq, void* s, int64_t lds,
+                int64_t M, int64_t K, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mxfp4_pack_B -- one-time, offline repacking of a quantised weight B[N, K]
+ * into the library's MFMA-fragment layout (the idea of page 683203's scale
+ * shuffle and page 496271's pre-arranged scale layout: lay the data out the way
+ * the matrix instruction's lanes consume it, so that each wave fetches its
+ * operand with one coalesced load).
+ *   bq  : fp4x2 [N, K/2], contiguous (row stride K/2 bytes), 16-byte aligned.
+ *   bs  : E8M0 [N, K/32], contiguous (row stride K/32 bytes).
+ *   out : mxfp4_pack_B_bytes(N, K) bytes, 16-byte aligned; out_bytes is its
+ *         size. Padding (N up to a multiple of 16, K up to a multiple of 128)
+ *         holds code 0 and scale byte 127.
+ * Layout of `out` (opaque to callers; stated for completeness):
+ *   NT = ceil(N/16), KT = ceil(K/128), KG = ceil(KT/4).
+ *   Codes: fragment (t, j), t < NT, j < KT, is 1024 bytes at ((t*KT + j)*1024):
+ *     bytes [16*l, 16*l+16) hold row 16t + l%16, elements
+ *     k in [128j + 32(l/16), +32), for lane l = 0..63.
+ *   Scales, at offset NT*KT*1024: dword (t, g, l) at ((t*KG + g)*64 + l)*4
+ *     holds in byte i the scale of row 16t + l%16, k-chunk 4(4g+i) + l/16.
+ * ------------------------------------------------------------------------- */
+size_t mxfp4_pack_B_bytes(int64_t N, int64_t K);
+int mxfp4_pack_B(const void* bq, const void* bs, int64_t N, int64_t K, void* out, size_t out_bytes,
+                 void* stream);
+
+/* ---------------------------------------------------------------------------
+ * gemm_a4w4_fused -- C[M, N] = Q(A) . B^T in one launch: A is quantised to
+ * MXFP4 per 1x32 block along K inside the GEMM kernel (the quantised A never
+ * reaches global memory), multiplied with the packed MXFP4 B on the scaled
+ * FP4 matrix cores with fp32 accumulation, and rounded to bf16 (nearest,
+ * ties to even). Page 517169 module docstring (the fused plan: load a bf16
+ * tile, quantise on chip, dot against B, fp32 accumulate, bf16 store).
+ *   A  : bf16 [M, K], row stride lda elements (lda >= K); A and lda*2 must be
+ *        multiples of 16 bytes.
+ *   Bp : output of mxfp4_pack_B(N, K).
+ *   C  : out, bf16 [M, N], row stride ldc elements (ldc >= N), 2-byte aligned.
+ *   workspace : device scratch of at least gemm_a4w4_workspace_bytes(M, N, K)
+ *        bytes (may be NULL when that size is 0), 256-byte aligned, ZEROED BY
+ *        THE CALLER ONCE after allocation; every call leaves it zeroed again.
+ *        Calls that may run concurrently need distinct workspaces.
+ * ------------------------------------------------------------------------- */
+size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
+int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M,
+                    int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * grouped_gemm_a4w4 -- G independent fused problems C_g = Q(A_g) . B_g^T that
+ * share N and K, in ONE launch (page 496271, ``custom_kernel``: a list of
+ * per-group problems; there one launch per group, here a single launch whose
+ * workgroups are spread over all groups' output tiles).
+ *   groups : HOST array of G descriptors, read during the call only. Per
+ *            group the same rules as gemm_a4w4_fused apply to A, lda, Bp, C,
+ *            ldc; M >= 1.
+ *   1 <= G <= MXFP4_MAX_GROUPS.
+ *   workspace : as for gemm_a4w4_fused, sized by
+ *            grouped_gemm_a4w4_workspace_bytes().
+ * ------------------------------------------------------------------------- */
+#define MXFP4_MAX_GROUPS 32
+typedef struct {
+  const void* A;
+  int64_t lda;
+  const void* Bp;
+  void* C;
+  int64_t ldc;
+  int64_t M;
+} mxfp4_group;
+
+size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K);
+int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP4_H */

@@ -1,0 +1,69 @@
+// mxfp4_quant: standalone per-1x32 MXFP4 quantisation of a bf16 matrix
+// (kernelbot amd-mxfp4-mm submission 683203, ``_quant_shuffled``: a tile of A
+// in, fp4x2 codes and E8M0 bytes out, with row tails masked; here scales are
+// stored row-major). One thread quantises one 32-element block with the same
+// register routine the fused GEMM uses.
+#include "host_common.hpp"
+#include "mx_device.hpp"
+
+namespace {
+
+struct QuantArgs {
+  const uint16_t* x;
+  int64_t ldx;
+  uint8_t* q;
+  int64_t ldq;
+  uint8_t* s;
+  int64_t lds;
+  int64_t M;
+  int64_t G;  // blocks per row, K/32
+};
+
+__global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= a.M * a.G) return;
+  const int64_t r = t / a.G, g = t - r * a.G;
+  const uint16_t* src = a.x + r * a.ldx + 32 * g;
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint4 v = mx::ldg16(src + 8 * i);
+    w[4 * i + 0] = v.x;
+    w[4 * i + 1] = v.y;
+    w[4 * i + 2] = v.z;
+    w[4 * i + 3] = v.w;
+  }
+  uint32_t q[4], sb;
+  mx::quant32(w, q, sb);
+  *reinterpret_cast<uint4*>(a.q + r * a.ldq + 16 * g) = make_uint4(q[0], q[1], q[2], q[3]);
+  a.s[r * a.lds + g] = (uint8_t)sb;
+}
+
+}  // namespace
+
+extern "C" const char* mxfp4_status_str(int status) {
+  switch (status) {
+    case MXFP4_OK: return "MXFP4_OK";
+    case MXFP4_ERR_NULL: return "MXFP4_ERR_NULL: a required pointer is NULL";
+    case MXFP4_ERR_SHAPE: return "MXFP4_ERR_SHAPE: bad M/N/K or row stride";
+    case MXFP4_ERR_ALIGN: return "MXFP4_ERR_ALIGN: pointer or row stride not suitably aligned";
+    case MXFP4_ERR_WORKSPACE: return "MXFP4_ERR_WORKSPACE: workspace missing or too small";
+    case MXFP4_ERR_TOO_MANY_GROUPS: return "MXFP4_ERR_TOO_MANY_GROUPS: G outside [1, MXFP4_MAX_GROUPS]";
+    case MXFP4_ERR_HIP: return "MXFP4_ERR_HIP: the HIP runtime rejected a launch";
+    case MXFP4_ERR_BUFFER: return "MXFP4_ERR_BUFFER: output buffer too small";
+    default: return "unknown mxfp4 status";
+  }
+}
+
+extern "C" int mxfp4_quant(const void* x, int64_t ldx, void* q, int64_t ldq, void* s, int64_t lds, int64_t M,
+                           int64_t K, void* stream) {
+  if (!x || !q || !s) return MXFP4_ERR_NULL;
+  if (M < 1 || K < 32 || K % 32 != 0 || M > mxh::kMaxDim || K > mxh::kMaxDim) return MXFP4_ERR_SHAPE;
+  if (ldx < K || ldq < K / 2 || lds < K / 32) return MXFP4_ERR_SHAPE;
+  if (!mxh::aligned(x, 16) || (ldx * 2) % 16 != 0 || !mxh::aligned(q, 16) || ldq % 16 != 0) return MXFP4_ERR_ALIGN;
+  QuantArgs a{(const uint16_t*)x, ldx, (uint8_t*)q, ldq, (uint8_t*)s, lds, M, K / 32};
+  const int64_t n = M * (K / 32);
+  void* args[] = {&a};
+  return mxh::launch_status(hipLaunchKernel((const void*)quant_kernel, dim3((unsigned)mxh::cdiv(n, 256)), dim3(256),
+                                            args, 0, (hipStream_t)stream));
+}

@@ -1,0 +1,165 @@
+"""Thin ctypes binding of libmxfp4.so (C ABI in include/mxfp4.h).
+
+Argument marshalling only: torch supplies device memory and the current
+stream; every step of the computation runs in the library's HIP kernels. There
+is no fallback: if the library is missing or a call returns a non-zero status,
+these functions raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so")
+_lib = None
+_lock = threading.Lock()
+
+MXFP4_MAX_GROUPS = 32
+STATUS = {0: "MXFP4_OK", 1: "MXFP4_ERR_NULL", 2: "MXFP4_ERR_SHAPE", 3: "MXFP4_ERR_ALIGN", 4: "MXFP4_ERR_WORKSPACE",
+          5: "MXFP4_ERR_TOO_MANY_GROUPS", 6: "MXFP4_ERR_HIP", 7: "MXFP4_ERR_BUFFER"}
+EXPORTED = ["mxfp4_status_str", "mxfp4_quant", "mxfp4_pack_B_bytes", "mxfp4_pack_B", "gemm_a4w4_workspace_bytes",
+            "gemm_a4w4_fused", "grouped_gemm_a4w4_workspace_bytes", "grouped_gemm_a4w4"]
+
+
+class Mxfp4Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {lib().mxfp4_status_str(status).decode()} (status {status})")
+
+
+class Group(ctypes.Structure):
+    """mirror of mxfp4_group"""
+    _fields_ = [("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("Bp", ctypes.c_void_p), ("C", ctypes.c_void_p),
+                ("ldc", ctypes.c_int64), ("M", ctypes.c_int64)]
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmxfp4.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(f"{_LIB_PATH} is not built; run `python -m mxfp4_block_scaled_02_amd.build`")
+        L = ctypes.CDLL(_LIB_PATH)
+        vp, i64, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+        L.mxfp4_status_str.argtypes, L.mxfp4_status_str.restype = [i32], ctypes.c_char_p
+        L.mxfp4_quant.argtypes, L.mxfp4_quant.restype = [vp, i64, vp, i64, vp, i64, i64, i64, vp], i32
+        L.mxfp4_pack_B_bytes.argtypes, L.mxfp4_pack_B_bytes.restype = [i64, i64], sz
+        L.mxfp4_pack_B.argtypes, L.mxfp4_pack_B.restype = [vp, vp, i64, i64, vp, sz, vp], i32
+        L.gemm_a4w4_workspace_bytes.argtypes, L.gemm_a4w4_workspace_bytes.restype = [i64, i64, i64], sz
+        L.gemm_a4w4_fused.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+        L.gemm_a4w4_fused.restype = i32
+        L.grouped_gemm_a4w4_workspace_bytes.argtypes = [ctypes.POINTER(Group), i32, i64, i64]
+        L.grouped_gemm_a4w4_workspace_bytes.restype = sz
+        L.grouped_gemm_a4w4.argtypes = [ctypes.POINTER(Group), i32, i64, i64, vp, sz, vp]
+        L.grouped_gemm_a4w4.restype = i32
+        _lib = L
+        return L
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise Mxfp4Error(status, where)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _require(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit column stride")
+
+
+# Workspace per device: zeroed once at allocation, grown on demand. The library
+# leaves it zeroed after every call, so it is reused without clearing.
+_ws: dict = {}
+
+
+def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    buf = _ws.get(key)
+    if nbytes > 0 and (buf is None or buf.numel() < nbytes):
+        buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        _ws[key] = buf
+    return buf
+
+
+def quant(x: torch.Tensor):
+    """bf16 [M, K] -> (q uint8 [M, K/2], s uint8 [M, K/32])."""
+    _require(x, torch.bfloat16, "x")
+    M, K = x.shape
+    q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    s = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    _check(lib().mxfp4_quant(x.data_ptr(), x.stride(0), q.data_ptr(), q.stride(0), s.data_ptr(), s.stride(0), M, K,
+                             _stream(x)), "mxfp4_quant")
+    return q, s
+
+
+def pack_B_bytes(N: int, K: int) -> int:
+    return int(lib().mxfp4_pack_B_bytes(N, K))
+
+
+def pack_B(bq: torch.Tensor, bs: torch.Tensor) -> torch.Tensor:
+    """fp4x2 [N, K/2] + E8M0 [N, K/32] (both contiguous uint8) -> packed uint8 buffer."""
+    _require(bq, torch.uint8, "bq")
+    _require(bs, torch.uint8, "bs")
+    N, KH = bq.shape
+    K = 2 * KH
+    if not (bq.is_contiguous() and bs.is_contiguous()) or bs.shape != (N, K // 32):
+        raise ValueError("bq [N, K/2] and bs [N, K/32] must be contiguous and agree")
+    out = torch.empty(pack_B_bytes(N, K), dtype=torch.uint8, device=bq.device)
+    _check(lib().mxfp4_pack_B(bq.data_ptr(), bs.data_ptr(), N, K, out.data_ptr(), out.numel(), _stream(bq)),
+           "mxfp4_pack_B")
+    return out
+
+
+def gemm(a: torch.Tensor, bp: torch.Tensor, N: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """C[M, N] = Q(A) . B^T in one fused launch; A bf16 [M, K], bp from pack_B."""
+    _require(a, torch.bfloat16, "a")
+    M, K = a.shape
+    if bp.numel() < pack_B_bytes(N, K):
+        raise ValueError("packed B is smaller than pack_B_bytes(N, K)")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    _require(out, torch.bfloat16, "out")
+    wsz = int(lib().gemm_a4w4_workspace_bytes(M, N, K))
+    ws = workspace(a.device, wsz)
+    _check(lib().gemm_a4w4_fused(a.data_ptr(), a.stride(0), bp.data_ptr(), out.data_ptr(), out.stride(0), M, N, K,
+                                 ws.data_ptr() if wsz else None, ws.numel() if wsz else 0, _stream(a)),
+           "gemm_a4w4_fused")
+    return out
+
+
+def grouped_gemm(a_list, bp_list, N: int, out_list=None):
+    """One launch over all groups: C_g = Q(A_g) . B_g^T for shared N, K."""
+    G = len(a_list)
+    if G != len(bp_list):
+        raise ValueError("a_list and bp_list differ in length")
+    if G < 1 or G > MXFP4_MAX_GROUPS:
+        raise ValueError(f"G must be in [1, {MXFP4_MAX_GROUPS}]")
+    K = a_list[0].shape[1]
+    if out_list is None:
+        out_list = [torch.empty((a.shape[0], N), dtype=torch.bfloat16, device=a.device) for a in a_list]
+    arr = (Group * G)()
+    for g, (a, bp, c) in enumerate(zip(a_list, bp_list, out_list)):
+        _require(a, torch.bfloat16, "a_g")
+        _require(c, torch.bfloat16, "c_g")
+        if a.shape[1] != K:
+            raise ValueError("all groups share K")
+        arr[g] = Group(a.data_ptr(), a.stride(0), bp.data_ptr(), c.data_ptr(), c.stride(0), a.shape[0])
+    wsz = int(lib().grouped_gemm_a4w4_workspace_bytes(arr, G, N, K))
+    ws = workspace(a_list[0].device, wsz)
+    _check(lib().grouped_gemm_a4w4(arr, G, N, K, ws.data_ptr() if wsz else None, ws.numel() if wsz else 0,
+                                   _stream(a_list[0])), "grouped_gemm_a4w4")
+    return out_list

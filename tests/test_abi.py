@@ -1,0 +1,118 @@
+"""The C ABI without a GPU: every declared symbol is exported, size queries
+follow the documented layout, and every validation error is returned before any
+HIP call (nothing is launched, so no device is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mxfp4_block_scaled_02_amd import ops
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "mxfp4.h")
+
+
+def cdiv(a, b):
+    return (a + b - 1) // b
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert set(names) == set(ops.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = ops.lib()
+    for name in declared_functions():
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    L = ops.lib()
+    for code, name in ops.STATUS.items():
+        assert L.mxfp4_status_str(code).decode().startswith(name)
+    assert L.mxfp4_status_str(99) == b"unknown mxfp4 status"
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (16, 128), (17, 160), (2112, 7168), (4096, 7168), (7168, 2048)])
+def test_pack_B_bytes_formula(N, K):
+    NT, KT = cdiv(N, 16), cdiv(K, 128)
+    KG = cdiv(KT, 4)
+    assert ops.lib().mxfp4_pack_B_bytes(N, K) == NT * KT * 1024 + NT * KG * 256
+
+
+@pytest.mark.parametrize("N,K", [(0, 32), (16, 0), (16, 48), (-1, 64)])
+def test_pack_B_bytes_invalid_is_zero(N, K):
+    assert ops.lib().mxfp4_pack_B_bytes(N, K) == 0
+
+
+def test_workspace_sizes_are_consistent():
+    L = ops.lib()
+    assert L.gemm_a4w4_workspace_bytes(0, 16, 32) == 0
+    for M, N, K in [(4, 256, 512), (16, 2112, 7168), (64, 7168, 2048), (4096, 4096, 7168)]:
+        w = L.gemm_a4w4_workspace_bytes(M, N, K)
+        assert w % 256 == 0
+
+
+P = 1 << 20  # a fake, 256-byte aligned "device pointer": validation never dereferences it
+OK_Q = dict(x=P, ldx=64, q=P, ldq=32, s=P, lds=2, M=4, K=64)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(x=None), 1), (dict(q=None), 1), (dict(s=None), 1),
+    (dict(M=0), 2), (dict(K=0), 2), (dict(K=48), 2), (dict(ldx=32), 2), (dict(ldq=16), 2), (dict(lds=1), 2),
+    (dict(x=P + 2), 3), (dict(q=P + 8), 3), (dict(ldx=68), 3), (dict(ldq=40), 3),
+])
+def test_quant_validation(change, status):
+    a = dict(OK_Q, **change)
+    got = ops.lib().mxfp4_quant(a["x"], a["ldx"], a["q"], a["ldq"], a["s"], a["lds"], a["M"], a["K"], None)
+    assert got == status
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(bq=None), 1), (dict(out=None), 1), (dict(N=0), 2), (dict(K=40), 2),
+    (dict(bq=P + 4), 3), (dict(out=P + 1), 3), (dict(out_bytes=1000), 7),
+])
+def test_pack_B_validation(change, status):
+    a = dict(dict(bq=P, bs=P, N=16, K=128, out=P, out_bytes=1024 + 256), **change)
+    got = ops.lib().mxfp4_pack_B(a["bq"], a["bs"], a["N"], a["K"], a["out"], a["out_bytes"], None)
+    assert got == status
+
+
+OK_G = dict(A=P, lda=7168, Bp=P, C=P, ldc=2112, M=16, N=2112, K=7168, ws=P, wsb=1 << 30)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(A=None), 1), (dict(Bp=None), 1), (dict(C=None), 1),
+    (dict(M=0), 2), (dict(N=0), 2), (dict(K=7000), 2), (dict(lda=7000), 2), (dict(ldc=2000), 2),
+    (dict(M=1 << 31), 2),
+    (dict(A=P + 2), 3), (dict(lda=7172), 3), (dict(Bp=P + 8), 3), (dict(C=P + 1), 3),
+    (dict(ws=None), 4), (dict(wsb=16), 4), (dict(ws=P + 64), 4),
+])
+def test_gemm_validation(change, status):
+    a = dict(OK_G, **change)
+    got = ops.lib().gemm_a4w4_fused(a["A"], a["lda"], a["Bp"], a["C"], a["ldc"], a["M"], a["N"], a["K"], a["ws"],
+                                    a["wsb"], None)
+    assert got == status
+
+
+def test_grouped_validation():
+    L = ops.lib()
+    g = (ops.Group * 2)()
+    g[0] = ops.Group(P, 7168, P, P, 4096, 128)
+    g[1] = ops.Group(P, 7168, P, P, 4096, 0)  # bad M in group 1
+    assert L.grouped_gemm_a4w4(g, 2, 4096, 7168, None, 0, None) == 2
+    assert L.grouped_gemm_a4w4(g, 0, 4096, 7168, None, 0, None) == 5
+    assert L.grouped_gemm_a4w4(g, 33, 4096, 7168, None, 0, None) == 5
+    assert L.grouped_gemm_a4w4(None, 1, 4096, 7168, None, 0, None) == 1
+    g[1] = ops.Group(P, 7168, None, P, 4096, 64)
+    assert L.grouped_gemm_a4w4(g, 2, 4096, 7168, None, 0, None) == 1
+    g[1] = ops.Group(P + 2, 7168, P, P, 4096, 64)
+    assert L.grouped_gemm_a4w4(g, 2, 4096, 7168, None, 0, None) == 3
