@@ -77,15 +77,16 @@ int mxfp4_quant(const void* x, int64_t ldx, void* q, int64_t ldq, void* s, int64
  *   bq  : fp4x2 [N, K/2], contiguous (row stride K/2 bytes), 16-byte aligned.
  *   bs  : E8M0 [N, K/32], contiguous (row stride K/32 bytes).
  *   out : mxfp4_pack_B_bytes(N, K) bytes, 16-byte aligned; out_bytes is its
- *         size. Padding (N up to a multiple of 16, K up to a multiple of 128)
+ *         size. Padding (N up to a multiple of 32, K up to a multiple of 64)
  *         holds code 0 and scale byte 127.
  * Layout of `out` (opaque to callers; stated for completeness):
- *   NT = ceil(N/16), KT = ceil(K/128), KG = ceil(KT/4).
- *   Codes: fragment (t, j), t < NT, j < KT, is 1024 bytes at ((t*KT + j)*1024):
- *     bytes [16*l, 16*l+16) hold row 16t + l%16, elements
- *     k in [128j + 32(l/16), +32), for lane l = 0..63.
- *   Scales, at offset NT*KT*1024: dword (t, g, l) at ((t*KG + g)*64 + l)*4
- *     holds in byte i the scale of row 16t + l%16, k-chunk 4(4g+i) + l/16.
+ *   NT = ceil(N/32), KU = ceil(K/64), KG = ceil(KU/4).
+ *   Codes: unit (t, u), t < NT, u < KU, is 1024 bytes at ((t*KU + u)*1024):
+ *     bytes [16*l, 16*l+16) hold row 32t + l%32, elements
+ *     k in [64u + 32(l/32), +32), for lane l = 0..63.
+ *   Scales, at offset NT*KU*1024: dword (t, g, l) at ((t*KG + g)*64 + l)*4
+ *     holds in byte i the scale of row 32t + l%32, 32-element chunk
+ *     2(4g+i) + l/32.
  * ------------------------------------------------------------------------- */
 size_t mxfp4_pack_B_bytes(int64_t N, int64_t K);
 int mxfp4_pack_B(const void* bq, const void* bs, int64_t N, int64_t K, void* out, size_t out_bytes,

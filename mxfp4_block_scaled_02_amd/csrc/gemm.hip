@@ -1,36 +1,44 @@
 // gemm_a4w4_fused / grouped_gemm_a4w4: C = Q(A) . B^T with the MXFP4
-// quantisation of A done in registers inside the GEMM, so the quantised A never
+// quantisation of A done on chip inside the GEMM, so the quantised A never
 // reaches global memory (kernelbot amd-mxfp4-mm submission 517169, module
 // docstring: the two-kernel pipeline writes A_q to HBM and reads it back; the
 // fix loads a bf16 tile, quantises on chip, feeds the block-scaled dot,
 // accumulates in fp32 and stores bf16).
 //
-// Work decomposition. A wave owns a (16*MW) x (16*NW) block of C and a range of
-// 128-wide K steps. Per K step every lane loads the 32 bf16 of its own MFMA A
-// slot (row l%16, k-chunk l/16) -- exactly one MXFP4 block -- so amax, the E8M0
-// byte and the E2M1 codes are computed by that lane alone with no cross-lane
-// traffic, and the lane's scale byte is the matrix instruction's A scale. B
-// comes pre-packed in fragment order: one 16-byte load per lane per 16x128 block.
-// Four waves per workgroup either split the workgroup's K range (WK = 4, skinny
-// M; partial sums reduced through LDS) or tile M x N (WK = 1). Across
-// workgroups K may be split S ways (split-K as in page 683203's call of the
-// assembly GEMM with a k-split argument); the partial tiles go to the caller's
-// workspace and the last workgroup to arrive on a tile (an atomic counter) adds
-// them in fixed order 0..S-1, writes bf16 and resets the counter, all in the
-// same launch.
+// Both kernels load A with fully coalesced 16-byte accesses: a 32-element
+// MXFP4 block then lies in the four lanes of a lane quad, which combine their
+// partial maxima with two DPP steps and each convert their 8 elements
+// (mx::quant8_quad). The codes are written to LDS in the lane order of the
+// scaled matrix instruction, with an XOR swizzle that keeps both the quad
+// writes and the operand reads free of bank conflicts. B arrives pre-packed in
+// 32x64 operand units (mxfp4_pack_B), one 16-byte load per lane per unit.
+//
+// Two kernels:
+//  * skinny (M <= 64): a 1024-thread workgroup owns MS rows x 16*NB columns of C
+//    over the whole K; its 16 waves split K, each quantises its own A slice into
+//    a private LDS operand tile and runs the 16x16x128 instruction, and the 16
+//    partial tiles are summed in LDS. No cross-workgroup reduction: on this GPU a
+//    split-K hand-off through memory costs several microseconds, more than the
+//    whole skinny GEMM.
+//  * tiled (larger M): a 256-thread workgroup owns a 128 x 512 tile of C. Per
+//    128-wide K step the workgroup quantises the 128x128 bf16 A block once into a
+//    double-buffered LDS tile; each of the 4 waves computes 128 x 128 of C with
+//    the 32x32x64 instruction from that shared A and its own B units, which
+//    stream from global memory straight into registers one K step ahead.
+//    Workgroups are ordered so that the ones sharing an XCD (and its L2) share A
+//    rows and B columns.
+#include <type_traits>
+
 #include "host_common.hpp"
 #include "mx_device.hpp"
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
-
 struct Operand {
   const uint16_t* A;
   int64_t lda;
-  const uint8_t* Bfrag;    // packed codes, fragment (t, j) at (t*KT + j)*1024
-  const uint32_t* Bscale;  // packed scale dwords, (t, g, lane) at (t*KG + g)*64 + lane
+  const uint8_t* Bunit;    // packed codes: unit (t, u) at (t*KU + u)*1024
+  const uint32_t* Bscale;  // packed scale dwords: (t, g, lane) at (t*KG + g)*64 + lane
   uint16_t* C;
   int64_t ldc;
   int M;
@@ -38,166 +46,339 @@ struct Operand {
 };
 
 struct Dims {
-  int N, K, KT, NT16, KG;
+  int N, K;
+  int KT;    // 128-wide K steps, ceil(K/128)
+  int KU;    // 64-wide packed units, ceil(K/64)
+  int NT32;  // 32-column packed tiles, ceil(N/32)
+  int KG;    // scale dword groups, ceil(KU/4)
 };
 
-template <int MW, int NW>
-__device__ __forceinline__ void wave_mainloop(const Operand& p, const Dims& d, int m0, int n0, int jb, int je,
-                                              mx::v4f (&acc)[MW][NW]) {
-  const int l = threadIdx.x & 63, r = l & 15, c = l >> 4;
-  for (int j = jb; j < je; ++j) {
-    uint4 bq[NW];
-    uint32_t bsc[NW];
-#pragma unroll
-    for (int t = 0; t < NW; ++t) {
-      const int n16 = (n0 >> 4) + t;
-      if (n16 < d.NT16) {
-        bq[t] = mx::ldg16(p.Bfrag + (((int64_t)n16 * d.KT + j) * 64 + l) * 16);
-        bsc[t] = p.Bscale[((int64_t)n16 * d.KG + (j >> 2)) * 64 + l] >> (8 * (j & 3));
-      } else {
-        bq[t] = make_uint4(0u, 0u, 0u, 0u);
-        bsc[t] = mx::kScaleOne;
-      }
-    }
-    const int kk = 128 * j + 32 * c;
-#pragma unroll
-    for (int i = 0; i < MW; ++i) {
-      const int row = m0 + 16 * i + r;
-      uint32_t w[16];
-      if (row < p.M && kk < d.K) {
-        const uint16_t* src = p.A + (int64_t)row * p.lda + kk;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint4 v = mx::ldg16(src + 8 * q);
-          w[4 * q + 0] = v.x;
-          w[4 * q + 1] = v.y;
-          w[4 * q + 2] = v.z;
-          w[4 * q + 3] = v.w;
-        }
-      } else {
-#pragma unroll
-        for (int q = 0; q < 16; ++q) w[q] = 0u;
-      }
-      uint32_t qa[4], sa;
-      mx::quant32(w, qa, sa);
-      const uint4 a4 = make_uint4(qa[0], qa[1], qa[2], qa[3]);
-#pragma unroll
-      for (int t = 0; t < NW; ++t) acc[i][t] = mx::mfma_fp4(a4, bq[t], acc[i][t], sa, bsc[t]);
-    }
-  }
+// Buffer resource over [base, base + bytes): raw buffer loads outside it return
+// zeros, which implements the M/N/K tails without branches. Offsets passed to the
+// loads are per-lane VGPR offsets; a moving window is made by advancing the base
+// (scalar arithmetic), so the hardware range check always sees the full offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
+}
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+}
+__device__ __forceinline__ void to_words(const uint4& v, uint32_t (&w)[4]) {
+  w[0] = v.x;
+  w[1] = v.y;
+  w[2] = v.z;
+  w[3] = v.w;
 }
 
-// Store a wave's accumulators as bf16 with M/N masks.
-template <int MW, int NW>
-__device__ __forceinline__ void store_c(const Operand& p, int N, int m0, int n0, const mx::v4f (&acc)[MW][NW]) {
+// Window of A for 128-wide K step j of the row tile starting at m0: in-range
+// bytes run to the end of row M-1's K elements. Elements k >= K of rows below
+// the last are in range but are not A (next row or caller padding); the K-tail
+// step zeroes them explicitly.
+struct AWindow {
+  const uint8_t* base;  // A + m0*lda
+  int64_t bytes;        // extent from base
+  __device__ __forceinline__ __amdgpu_buffer_rsrc_t at(int j) const {
+    return make_rsrc(base + (int64_t)j * 256, bytes - (int64_t)j * 256);
+  }
+};
+__device__ __forceinline__ AWindow a_window(const Operand& p, int K, int m0) {
+  AWindow w;
+  w.base = reinterpret_cast<const uint8_t*>(p.A) + (int64_t)m0 * p.lda * 2;
+  w.bytes = m0 < p.M ? ((int64_t)(p.M - 1 - m0) * p.lda + K) * 2 : 0;
+  return w;
+}
+
+// ---------------------------------------------------------------------------
+// Skinny kernel
+// ---------------------------------------------------------------------------
+constexpr int kSkWaves = 16;
+
+// 16-byte LDS slot of the 16x16x128 A operand element (row < 16, 32-k chunk < 4).
+// The MFMA lane for it is chunk*16 + row; the XOR keeps a quad write pass (4
+// rows x 4 chunks x 4 dwords) and each 16-lane operand read conflict-free.
+__device__ __forceinline__ int slot16(int row, int chunk) { return chunk * 16 + (row ^ (chunk << 2)); }
+
+template <int MS, int NB, int PF>
+__global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, Dims d) {
+  static_assert(MS == 4 || MS == 8 || MS == 16, "rows per workgroup");
+  constexpr int PIECES = MS / 4;  // 16-byte A pieces per lane per K step
+  __shared__ __align__(16) uint32_t sAq[kSkWaves][64 * 4];  // per-wave A operand codes
+  __shared__ uint8_t sAs[kSkWaves][64];                    // per-wave A operand scales
+  __shared__ float red[kSkWaves][NB * 4][64];              // partial C tiles
+
   const int l = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
+  const int m0 = blockIdx.y * MS, T0 = blockIdx.x * NB;
+  const int jb = d.KT * wave / kSkWaves, je = d.KT * (wave + 1) / kSkWaves;
+
+  // Rows MS..15 of the operand are never written: zero codes, neutral scales.
 #pragma unroll
-  for (int i = 0; i < MW; ++i)
+  for (int x = 0; x < 4; ++x) sAq[wave][x * 64 + l] = 0u;
+  sAs[wave][l] = (uint8_t)mx::kScaleOne;
+
+  mx::v4f acc[NB];
 #pragma unroll
-    for (int t = 0; t < NW; ++t) {
-      const int col = n0 + 16 * t + (l & 15);
+  for (int t = 0; t < NB; ++t) acc[t] = mx::v4f{0.f, 0.f, 0.f, 0.f};
+
+  // Per-lane constants. A piece h: row 4h + l/16 of the tile, 8 elements at
+  // 8*(l%16) of the K step (a wave pass covers 4 whole rows: coalesced).
+  const AWindow aw = a_window(p, d.K, m0);
+  uint32_t aoff[PIECES];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = m0 + 16 * i + 4 * (l >> 4) + e;
-        if (row < p.M && col < N) p.C[(int64_t)row * p.ldc + col] = mx::f32_to_bf16(acc[i][t][e]);
+  for (int h = 0; h < PIECES; ++h) aoff[h] = (uint32_t)(((4 * h + (l >> 4)) * p.lda + 8 * (l & 15)) * 2);
+  // LDS dword this lane writes for piece h, and the operand slot it reads.
+  const int chunk = (l & 15) >> 2, sub = l & 3;
+  int wslot[PIECES];
+#pragma unroll
+  for (int h = 0; h < PIECES; ++h) wslot[h] = slot16(4 * h + (l >> 4), chunk);
+  const int aslot = slot16(l & 15, l >> 4);
+  // B operand of 16-column tile T at step j: lane l reads unit 2j + (l/16)/2 of
+  // packed tile T/2 at unit lane ((l/16)%2)*32 + 16*(T%2) + l%16.
+  const int s16 = l >> 4;
+  uint32_t boff[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t)
+    boff[t] = (uint32_t)((s16 >> 1) * 1024 + (((s16 & 1) * 32 + ((T0 + t) & 1) * 16 + (l & 15)) * 16));
+  const int tail_k = d.K - 128 * (d.KT - 1);  // valid elements in the last K step
+
+  for (int j0 = jb; j0 < je; j0 += PF) {
+    uint32_t w[PF][PIECES][4];
+    uint4 bq[PF][NB];
+    uint32_t bs[PF][NB];
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int j = j0 + s;
+      if (j < je) {
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const int t32 = (T0 + t) >> 1;
+          const bool ok = t32 < d.NT32;
+          const uint8_t* ub = p.Bunit + ((int64_t)t32 * d.KU + 2 * j) * 1024;
+          bq[s][t] = bload16(make_rsrc(ub, ok ? (int64_t)(d.KU - 2 * j) * 1024 : 0), boff[t]);
+          const uint32_t* sbp = p.Bscale + ((int64_t)t32 * d.KG + (j >> 1)) * 64;
+          bs[s][t] = bload4(make_rsrc(sbp, ok ? 256 : 0), (uint32_t)(((s16 & 1) * 32 + ((T0 + t) & 1) * 16 + (l & 15)) * 4));
+        }
+        const __amdgpu_buffer_rsrc_t ar = aw.at(j);
+#pragma unroll
+        for (int h = 0; h < PIECES; ++h) to_words(bload16(ar, aoff[h]), w[s][h]);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+      const int j = j0 + s;
+      if (j < je) {
+        if (j == d.KT - 1 && tail_k < 128) {  // K tail: elements past K are not A
+#pragma unroll
+          for (int h = 0; h < PIECES; ++h)
+            if (8 * (l & 15) >= tail_k) w[s][h][0] = w[s][h][1] = w[s][h][2] = w[s][h][3] = 0u;
+        }
+#pragma unroll
+        for (int h = 0; h < PIECES; ++h) {
+          uint32_t sb;
+          const uint32_t code = mx::quant8_quad(w[s][h], sb);
+          sAq[wave][wslot[h] * 4 + sub] = code;
+          sAs[wave][wslot[h]] = (uint8_t)sb;  // the quad's four lanes store the same byte
+        }
+        // LDS operations of one wave complete in order: the reads see the writes.
+        const uint4 a = *reinterpret_cast<const uint4*>(&sAq[wave][aslot * 4]);
+        const uint32_t sa = sAs[wave][aslot];
+        const int bsh = 8 * ((2 * j + (l >> 5)) & 3);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) acc[t] = mx::mfma_fp4(a, bq[s][t], acc[t], sa, bs[s][t] >> bsh);
+      }
+    }
+  }
+
+  // Sum the 16 waves' partial tiles in LDS and store bf16.
+#pragma unroll
+  for (int t = 0; t < NB; ++t)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) red[wave][t * 4 + e][l] = acc[t][e];
+  __syncthreads();
+  constexpr int OUT = NB * 256;
+  for (int o = threadIdx.x; o < OUT; o += kSkWaves * 64) {
+    const int slot = o >> 6, ll = o & 63, t = slot >> 2, e = slot & 3;
+    const int r = 4 * (ll >> 4) + e;
+    if (r >= MS) continue;
+    float sum = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < kSkWaves; ++w2) sum += red[w2][slot][ll];
+    const int row = m0 + r, col = (T0 + t) * 16 + (ll & 15);
+    if (row < p.M && col < d.N) p.C[(int64_t)row * p.ldc + col] = mx::f32_to_bf16(sum);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel
+// ---------------------------------------------------------------------------
+constexpr int kTBM = 128, kTBN = 512, kTThreads = 256;
+
+// A bijection on [0, G) giving each of the 8 XCDs (workgroup id mod 8) a
+// contiguous run of tiles, so the tiles sharing an L2 share A rows / B columns.
+__device__ __forceinline__ int xcd_remap(int id, int G) {
+  const int full = G & ~7;
+  if (id >= full) return id;
+  return (id & 7) * (full >> 3) + (id >> 3);
+}
+
+// 16-byte LDS slot, within one 32x64 operand block, of unit lane `lane`
+// (row lane%32, chunk lane/32) at 64-k half `ks` of a 128-k step; the XOR with the
+// 32-element chunk index (2*ks + lane/32) keeps quad writes and operand reads
+// conflict-free.
+__device__ __forceinline__ int slot32(int lane, int ks) { return lane ^ ((((ks << 1) | (lane >> 5)) & 3) << 2); }
+
+// LDS of the tiled kernel (dwords): A operand codes [buffer][64-k half][32-row
+// tile][64 lanes x 4] and A scales [buffer][64-k half][lane] (byte = 32-row tile).
+struct TiledSmem {
+  uint32_t a[2][2][4][256];
+  uint32_t as[2][2][64];
+};
+
+__device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int mt, int nt, TiledSmem& sm) {
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
+  const int m0 = mt * kTBM;
+  const int t0 = nt * (kTBN / 32) + wave * 4;  // this wave's first 32-column packed tile
+
+  mx::v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
+
+  // Thread tid owns pieces P = 256h + tid (h < 8) of the 128 x 16 pieces of a K
+  // step: row 16h + tid/16, elements 8*(tid%16) .. +7. A wave's pass covers 4
+  // whole rows (coalesced) and each lane quad holds one 32-element block.
+  const AWindow aw = a_window(p, d.K, m0);
+  const uint32_t aoff0 = (uint32_t)(((tid >> 4) * p.lda + 8 * (tid & 15)) * 2);
+  const uint32_t arow16 = (uint32_t)(16 * p.lda * 2);
+  const int chunk = (tid & 15) >> 2, sub = tid & 3, qks = chunk >> 1;
+  // LDS dword written for piece h: block (buf, ks, i = h/2), slot of unit lane
+  // (chunk%2)*32 + 16*(h%2) + tid/16 (its XOR term is chunk << 2).
+  const int wbase = (qks * 4) * 256 + ((chunk & 1) * 32 + ((tid >> 4) ^ (chunk << 2))) * 4 + sub;
+  const int sbase = (qks * 64 + (chunk & 1) * 32 + (tid >> 4)) * 4;
+  const int tail_k = d.K - 128 * (d.KT - 1);
+
+  uint32_t raw[8][4];
+  auto load_a = [&](int j) {
+    const __amdgpu_buffer_rsrc_t ar = aw.at(j);
+#pragma unroll
+    for (int h = 0; h < 8; ++h) to_words(bload16(ar, aoff0 + (uint32_t)h * arow16), raw[h]);
+  };
+  auto quant_store = [&](int j, int buf) {
+    if (j == d.KT - 1 && tail_k < 128 && 8 * (tid & 15) >= tail_k) {  // K tail: not A
+#pragma unroll
+      for (int h = 0; h < 8; ++h) raw[h][0] = raw[h][1] = raw[h][2] = raw[h][3] = 0u;
+    }
+    uint32_t* const sa_base = &sm.a[buf][0][0][0];
+    uint8_t* const ss_base = reinterpret_cast<uint8_t*>(&sm.as[buf][0][0]);
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      uint32_t sb;
+      const uint32_t code = mx::quant8_quad(raw[h], sb);
+      sa_base[wbase + (h >> 1) * 256 + (h & 1) * 64] = code;
+      ss_base[sbase + (h & 1) * 64 + (h >> 1)] = (uint8_t)sb;  // the quad stores the same byte
+    }
+  };
+  // B of step j: units 2j (ks 0) and 2j+1 (ks 1) of this wave's 4 packed tiles,
+  // lane l's 16 bytes of each, and the tiles' scale dwords.
+  auto load_b = [&](int j, uint4 (&b)[2][4], uint32_t (&sc)[4]) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int t32 = t0 + t;
+      const bool ok = t32 < d.NT32;
+      const __amdgpu_buffer_rsrc_t br =
+          make_rsrc(p.Bunit + ((int64_t)t32 * d.KU + 2 * j) * 1024, ok ? (int64_t)(d.KU - 2 * j) * 1024 : 0);
+      b[0][t] = bload16(br, (uint32_t)l * 16);
+      b[1][t] = bload16(br, (uint32_t)l * 16 + 1024);
+      sc[t] = bload4(make_rsrc(p.Bscale + ((int64_t)t32 * d.KG + (j >> 1)) * 64, ok ? 256 : 0), (uint32_t)l * 4);
+    }
+  };
+  auto compute = [&](int j, const uint4 (&b)[2][4], const uint32_t (&sc)[4]) {
+    const int buf = j & 1;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int bsh = 8 * ((2 * j + ks) & 3);
+      const uint32_t sa = sm.as[buf][ks][l];
+      const int sl = slot32(l, ks) * 4;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&sm.a[buf][ks][i][sl]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t sb = sc[t] >> bsh;
+          switch (i) {  // A scale byte = 32-row tile; folds once unrolled
+            case 0: acc[i][t] = mx::mfma32_fp4<0, 0>(a, b[ks][t], acc[i][t], sa, sb); break;
+            case 1: acc[i][t] = mx::mfma32_fp4<1, 0>(a, b[ks][t], acc[i][t], sa, sb); break;
+            case 2: acc[i][t] = mx::mfma32_fp4<2, 0>(a, b[ks][t], acc[i][t], sa, sb); break;
+            default: acc[i][t] = mx::mfma32_fp4<3, 0>(a, b[ks][t], acc[i][t], sa, sb); break;
+          }
+        }
+      }
+    }
+  };
+  // One K step j: B(j+1) is loaded into the other register set while step j
+  // computes; the bf16 A of step j+2 is loaded after the quantisation of A(j+1)
+  // into the other LDS buffer, so every load has about a whole step to land.
+  // FULL marks steps where j+2 < KT (no bounds tests).
+  auto step = [&](auto full, int j, const uint4 (&bc)[2][4], const uint32_t (&scc)[4], uint4 (&bn)[2][4],
+                  uint32_t (&scn)[4]) {
+    constexpr bool FULL = decltype(full)::value;
+    if (FULL || j + 1 < d.KT) load_b(j + 1, bn, scn);
+    __syncthreads();  // A(j) is complete; every wave is past its reads of the other buffer
+    compute(j, bc, scc);
+    if (FULL || j + 1 < d.KT) {
+      quant_store(j + 1, (j + 1) & 1);
+      if (FULL || j + 2 < d.KT) load_a(j + 2);
+    }
+  };
+
+  uint4 b0[2][4], b1[2][4];
+  uint32_t s0[4], s1[4];
+  load_a(0);
+  load_b(0, b0, s0);
+  quant_store(0, 0);
+  if (d.KT > 1) load_a(1);
+  int j = 0;
+  for (; j + 3 < d.KT; j += 2) {  // steady state: straight-line, B sets alternate
+    step(std::true_type{}, j, b0, s0, b1, s1);
+    step(std::true_type{}, j + 1, b1, s1, b0, s0);
+  }
+  for (; j < d.KT; j += 2) {
+    step(std::false_type{}, j, b0, s0, b1, s1);
+    if (j + 1 < d.KT) step(std::false_type{}, j + 1, b1, s1, b0, s0);
+  }
+
+  // acc[i][t] register r of lane l: row 32i + 8(r/4) + 4(l/32) + r%4, column 32t + l%32.
+  const int rl = m0 + 4 * (l >> 5);
+  const int c0 = t0 * 32 + (l & 31);
+  uint16_t* const cb = p.C + (int64_t)rl * p.ldc + c0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int ro = 32 * i + 8 * (r >> 2) + (r & 3);
+      if (rl + ro < p.M) {
+        uint16_t* const crow = cb + (int64_t)ro * p.ldc;
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          if (c0 + 32 * t < d.N) crow[32 * t] = mx::f32_to_bf16(acc[i][t][r]);
       }
     }
 }
 
-// One workgroup's tile: main loop, intra-workgroup K reduction, split-K
-// reduction across workgroups, bf16 store.
-template <int MW, int NW, int WM, int WN, int WK>
-__device__ __forceinline__ void gemm_tile(const Operand& p, const Dims& d, int mtile, int ntile, int s, int S,
-                                          int64_t tile_id, float* partial, uint32_t* counters) {
-  static_assert(WM * WN * WK == kWaves, "four waves per workgroup");
-  constexpr int BM = 16 * MW * WM, BN = 16 * NW * WN, NACC = MW * NW * 4;
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int wk = wave % WK, wn = (wave / WK) % WN, wm = wave / (WK * WN);
-  const int m0 = mtile * BM + wm * 16 * MW, n0 = ntile * BN + wn * 16 * NW;
-  const int parts = S * WK, part = s * WK + wk;
-  const int jb = (int)((int64_t)d.KT * part / parts), je = (int)((int64_t)d.KT * (part + 1) / parts);
-
-  mx::v4f acc[MW][NW];
-#pragma unroll
-  for (int i = 0; i < MW; ++i)
-#pragma unroll
-    for (int t = 0; t < NW; ++t) acc[i][t] = mx::v4f{0.f, 0.f, 0.f, 0.f};
-  wave_mainloop<MW, NW>(p, d, m0, n0, jb, je, acc);
-
-  if constexpr (WK > 1) {
-    __shared__ float red[(WK - 1) * WM * WN][NACC][64];
-    const int slot = (wk - 1) * WM * WN + wm * WN + wn;
-    if (wk > 0) {
-#pragma unroll
-      for (int i = 0; i < MW; ++i)
-#pragma unroll
-        for (int t = 0; t < NW; ++t)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) red[slot][(i * NW + t) * 4 + e][l] = acc[i][t][e];
-    }
-    __syncthreads();
-    if (wk == 0) {
-      for (int k2 = 1; k2 < WK; ++k2) {
-        const int sl = (k2 - 1) * WM * WN + wm * WN + wn;
-#pragma unroll
-        for (int i = 0; i < MW; ++i)
-#pragma unroll
-          for (int t = 0; t < NW; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[i][t][e] += red[sl][(i * NW + t) * 4 + e][l];
-      }
-    }
-  }
-
-  if (S == 1) {
-    if (wk == 0) store_c<MW, NW>(p, d.N, m0, n0, acc);
-    return;
-  }
-
-  // Split-K across workgroups: publish this split's partial tile, then the last
-  // arriver sums all S partials in order and writes C.
-  constexpr int TILE = BM * BN;
-  const int64_t wslot = (int64_t)((wm * WN + wn) * NACC) * 64;
-  if (wk == 0) {
-    float* dst = partial + (tile_id * S + s) * TILE + wslot;
-#pragma unroll
-    for (int i = 0; i < MW; ++i)
-#pragma unroll
-      for (int t = 0; t < NW; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) dst[((i * NW + t) * 4 + e) * 64 + l] = acc[i][t][e];
-  }
-  __threadfence();
-  __syncthreads();
-  __shared__ int is_last;
-  if (threadIdx.x == 0) is_last = (atomicAdd(&counters[tile_id], 1u) == (uint32_t)(S - 1));
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  if (wk == 0) {
-#pragma unroll
-    for (int i = 0; i < MW; ++i)
-#pragma unroll
-      for (int t = 0; t < NW; ++t) acc[i][t] = mx::v4f{0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < S; ++s2) {
-      const float* src = partial + (tile_id * S + s2) * TILE + wslot;
-#pragma unroll
-      for (int i = 0; i < MW; ++i)
-#pragma unroll
-        for (int t = 0; t < NW; ++t)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][t][e] += src[((i * NW + t) * 4 + e) * 64 + l];
-    }
-    store_c<MW, NW>(p, d.N, m0, n0, acc);
-  }
-  if (threadIdx.x == 0) counters[tile_id] = 0u;
-}
-
-template <int MW, int NW, int WM, int WN, int WK>
-__global__ __launch_bounds__(kThreads) void gemm_fused_kernel(Operand p, Dims d, int S, float* partial,
-                                                               uint32_t* counters) {
-  const int64_t tile_id = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-  gemm_tile<MW, NW, WM, WN, WK>(p, d, blockIdx.y, blockIdx.x, blockIdx.z, S, tile_id, partial, counters);
+__global__ __launch_bounds__(kTThreads) void gemm_tiled_kernel(Operand p, Dims d, int ntiles_n) {
+  __shared__ __align__(16) TiledSmem sm;
+  const int v = xcd_remap(blockIdx.x, gridDim.x);
+  tiled_tile(p, d, v / ntiles_n, v % ntiles_n, sm);
 }
 
 struct GroupedArgs {
@@ -207,63 +388,21 @@ struct GroupedArgs {
   int ntiles_n;
 };
 
-template <int MW, int NW, int WM, int WN, int WK>
-__global__ __launch_bounds__(kThreads) void gemm_grouped_kernel(GroupedArgs a, Dims d) {
-  const int id = blockIdx.x;
+__global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, Dims d) {
+  const int v = xcd_remap(blockIdx.x, gridDim.x);
   int g = 0;
-  while (g + 1 < a.G && a.tile_start[g + 1] <= id) ++g;
-  const int local = id - a.tile_start[g];
-  gemm_tile<MW, NW, WM, WN, WK>(a.g[g], d, local / a.ntiles_n, local % a.ntiles_n, 0, 1, 0, nullptr, nullptr);
+  while (g + 1 < a.G && a.tile_start[g + 1] <= v) ++g;
+  const int local = v - a.tile_start[g];
+  __shared__ __align__(16) TiledSmem sm;
+  tiled_tile(a.g[g], d, local / a.ntiles_n, local % a.ntiles_n, sm);
 }
 
 // ---------------------------------------------------------------------------
-// Host side: plan, workspace size, launch.
+// Host side
 // ---------------------------------------------------------------------------
-enum Variant { kSkinny1, kSkinny2, kSkinny4, kTiled };
-
-struct Plan {
-  Variant v;
-  int BM, BN, S;
-  int64_t mtiles, ntiles;
-  size_t ws_bytes;
-};
-
-constexpr int kMaxSplit = 16;
-
-Plan make_plan(int64_t M, int64_t N, int64_t K) {
-  Plan pl{};
-  const int64_t KT = mxh::cdiv(K, 128);
-  if (M <= 64) {
-    pl.v = M <= 16 ? kSkinny1 : (M <= 32 ? kSkinny2 : kSkinny4);
-    pl.BM = M <= 16 ? 16 : (M <= 32 ? 32 : 64);
-    pl.BN = 64;
-  } else {
-    pl.v = kTiled;
-    pl.BM = 128;
-    pl.BN = 128;
-  }
-  pl.mtiles = mxh::cdiv(M, pl.BM);
-  pl.ntiles = mxh::cdiv(N, pl.BN);
-  pl.S = 1;
-  if (pl.v != kTiled) {
-    const int64_t tiles = pl.mtiles * pl.ntiles;
-    int64_t S = mxh::cdiv(256, tiles);
-    S = S > KT / 4 ? KT / 4 : S;
-    S = S > kMaxSplit ? kMaxSplit : S;
-    pl.S = S < 1 ? 1 : (int)S;
-  }
-  pl.ws_bytes = 0;
-  if (pl.S > 1) {
-    const size_t tiles = (size_t)(pl.mtiles * pl.ntiles);
-    const size_t counter_bytes = (tiles * 4 + 255) / 256 * 256;
-    pl.ws_bytes = counter_bytes + tiles * (size_t)pl.S * pl.BM * pl.BN * 4;
-  }
-  return pl;
-}
-
 Dims make_dims(int64_t N, int64_t K) {
   const mxh::PackedGeom g(N, K);
-  return Dims{(int)N, (int)K, (int)g.KT, (int)g.NT, (int)g.KG};
+  return Dims{(int)N, (int)K, (int)mxh::cdiv(K, 128), (int)g.KU, (int)g.NT, (int)g.KG};
 }
 
 Operand make_operand(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M, int64_t N,
@@ -272,7 +411,7 @@ Operand make_operand(const void* A, int64_t lda, const void* Bp, void* C, int64_
   Operand o{};
   o.A = (const uint16_t*)A;
   o.lda = lda;
-  o.Bfrag = (const uint8_t*)Bp;
+  o.Bunit = (const uint8_t*)Bp;
   o.Bscale = (const uint32_t*)((const uint8_t*)Bp + g.code_bytes);
   o.C = (uint16_t*)C;
   o.ldc = ldc;
@@ -291,47 +430,80 @@ int check_problem(const void* A, int64_t lda, const void* Bp, const void* C, int
   return MXFP4_OK;
 }
 
-template <int MW, int NW, int WM, int WN, int WK>
-hipError_t launch_fused(const Plan& pl, const Operand& o, const Dims& d, void* ws, hipStream_t st) {
-  uint32_t* counters = (uint32_t*)ws;
-  float* partial = nullptr;
-  if (pl.S > 1) {
-    const size_t tiles = (size_t)(pl.mtiles * pl.ntiles);
-    partial = (float*)((uint8_t*)ws + (tiles * 4 + 255) / 256 * 256);
+template <int MS, int NB, int PF>
+hipError_t launch_skinny(const Operand& o, const Dims& d, int64_t M, hipStream_t st) {
+  Operand op = o;
+  Dims dd = d;
+  void* args[] = {&op, &dd};
+  const dim3 grid((unsigned)mxh::cdiv(mxh::cdiv(d.N, 16), NB), (unsigned)mxh::cdiv(M, MS));
+  return hipLaunchKernel((const void*)gemm_skinny_kernel<MS, NB, PF>, grid, dim3(kSkWaves * 64), args, 0, st);
+}
+
+// Skinny tile shape (rows MS x 16*NB columns per workgroup). Every workgroup
+// reads its MS rows of bf16 A over the whole K plus its columns of packed B, and
+// the busiest CU sets the time; pick the shape with the fewest bytes on it,
+// counting 256 CUs with one 1024-thread workgroup each at a time.
+struct SkinnyShape {
+  int MS, NB;
+};
+SkinnyShape choose_skinny(int64_t M, int64_t N, int64_t K) {
+  static const SkinnyShape cand[] = {{4, 1}, {4, 2}, {4, 4}, {8, 1}, {8, 2}, {8, 4}, {16, 1}, {16, 2}, {16, 4}};
+  SkinnyShape best = {16, 1};
+  double best_cost = -1.0;
+  for (const SkinnyShape& c : cand) {
+    if (c.MS > 4 && M <= c.MS / 2) continue;  // do not pad M by more than 2x
+    const int64_t wgs = mxh::cdiv(mxh::cdiv(N, 16), c.NB) * mxh::cdiv(M, c.MS);
+    const double per_wg = (double)c.MS * K * 2.0 + (double)c.NB * 16 * K / 2.0;
+    const double cost = (double)mxh::cdiv(wgs, 256) * per_wg;
+    if (best_cost < 0 || cost < best_cost) {
+      best_cost = cost;
+      best = c;
+    }
+  }
+  return best;
+}
+
+hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+  if (M <= 64) {
+    const SkinnyShape sh = choose_skinny(M, N, K);
+    switch (sh.MS * 16 + sh.NB) {
+      case 4 * 16 + 1: return launch_skinny<4, 1, 4>(o, d, M, st);
+      case 4 * 16 + 2: return launch_skinny<4, 2, 4>(o, d, M, st);
+      case 4 * 16 + 4: return launch_skinny<4, 4, 2>(o, d, M, st);
+      case 8 * 16 + 1: return launch_skinny<8, 1, 4>(o, d, M, st);
+      case 8 * 16 + 2: return launch_skinny<8, 2, 4>(o, d, M, st);
+      case 8 * 16 + 4: return launch_skinny<8, 4, 2>(o, d, M, st);
+      case 16 * 16 + 1: return launch_skinny<16, 1, 2>(o, d, M, st);
+      case 16 * 16 + 2: return launch_skinny<16, 2, 2>(o, d, M, st);
+      default: return launch_skinny<16, 4, 2>(o, d, M, st);
+    }
   }
   Operand op = o;
   Dims dd = d;
-  int S = pl.S;
-  void* args[] = {&op, &dd, &S, &partial, &counters};
-  return hipLaunchKernel((const void*)gemm_fused_kernel<MW, NW, WM, WN, WK>,
-                         dim3((unsigned)pl.ntiles, (unsigned)pl.mtiles, (unsigned)pl.S), dim3(kThreads), args, 0, st);
+  int ntn = (int)mxh::cdiv(N, kTBN);
+  void* args[] = {&op, &dd, &ntn};
+  const int64_t tiles = mxh::cdiv(M, kTBM) * ntn;
+  return hipLaunchKernel((const void*)gemm_tiled_kernel, dim3((unsigned)tiles), dim3(kTThreads), args, 0, st);
 }
 
 }  // namespace
 
 extern "C" size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || M > mxh::kMaxDim || N > mxh::kMaxDim || K > mxh::kMaxDim) return 0;
-  return make_plan(M, N, K).ws_bytes;
+  (void)M;
+  (void)N;
+  (void)K;
+  return 0;  // every output tile is reduced inside one workgroup
 }
 
 extern "C" int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M, int64_t N,
                                int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_problem(A, lda, Bp, C, ldc, M, N, K);
+  (void)workspace;
+  (void)workspace_bytes;
+  const int st = check_problem(A, lda, Bp, C, ldc, M, N, K);
   if (st != MXFP4_OK) return st;
-  const Plan pl = make_plan(M, N, K);
-  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !mxh::aligned(workspace, 256)))
-    return MXFP4_ERR_WORKSPACE;
+  if (mxh::cdiv(M, kTBM) * mxh::cdiv(N, kTBN) > INT32_MAX) return MXFP4_ERR_SHAPE;
   const Operand o = make_operand(A, lda, Bp, C, ldc, M, N, K);
-  const Dims d = make_dims(N, K);
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e;
-  switch (pl.v) {
-    case kSkinny1: e = launch_fused<1, 4, 1, 1, 4>(pl, o, d, workspace, s); break;
-    case kSkinny2: e = launch_fused<2, 4, 1, 1, 4>(pl, o, d, workspace, s); break;
-    case kSkinny4: e = launch_fused<4, 4, 1, 1, 4>(pl, o, d, workspace, s); break;
-    default: e = launch_fused<4, 4, 2, 2, 1>(pl, o, d, workspace, s); break;
-  }
-  return mxh::launch_status(e);
+  return mxh::launch_status(launch_gemm(o, make_dims(N, K), M, N, K, (hipStream_t)stream));
 }
 
 extern "C" size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K) {
@@ -339,7 +511,7 @@ extern "C" size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, i
   (void)G;
   (void)N;
   (void)K;
-  return 0;  // one tile per workgroup over the full K: no split-K partials
+  return 0;
 }
 
 extern "C" int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,
@@ -349,8 +521,7 @@ extern "C" int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, in
   if (!groups) return MXFP4_ERR_NULL;
   if (G < 1 || G > MXFP4_MAX_GROUPS) return MXFP4_ERR_TOO_MANY_GROUPS;
   GroupedArgs a{};
-  constexpr int BM = 128, BN = 128;
-  const int64_t ntn = mxh::cdiv(N, BN);
+  const int64_t ntn = mxh::cdiv(N, kTBN);
   int64_t total = 0;
   for (int g = 0; g < G; ++g) {
     const mxfp4_group& q = groups[g];
@@ -358,7 +529,7 @@ extern "C" int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, in
     if (st != MXFP4_OK) return st;
     a.g[g] = make_operand(q.A, q.lda, q.Bp, q.C, q.ldc, q.M, N, K);
     a.tile_start[g] = (int)total;
-    total += mxh::cdiv(q.M, BM) * ntn;
+    total += mxh::cdiv(q.M, kTBM) * ntn;
     if (total > INT32_MAX) return MXFP4_ERR_SHAPE;
   }
   a.tile_start[G] = (int)total;
@@ -366,6 +537,6 @@ extern "C" int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, in
   a.ntiles_n = (int)ntn;
   Dims d = make_dims(N, K);
   void* args[] = {&a, &d};
-  return mxh::launch_status(hipLaunchKernel((const void*)gemm_grouped_kernel<4, 4, 2, 2, 1>, dim3((unsigned)total),
-                                            dim3(kThreads), args, 0, (hipStream_t)stream));
+  return mxh::launch_status(hipLaunchKernel((const void*)gemm_grouped_kernel, dim3((unsigned)total),
+                                            dim3(kTThreads), args, 0, (hipStream_t)stream));
 }

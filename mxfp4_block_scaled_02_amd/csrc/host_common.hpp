@@ -16,14 +16,16 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 inline int launch_status(hipError_t e) { return e == hipSuccess ? MXFP4_OK : MXFP4_ERR_HIP; }
 
-// Packed-B geometry (see mxfp4_pack_B in include/mxfp4.h).
+// Packed-B geometry (see mxfp4_pack_B in include/mxfp4.h): 1 KB units of
+// 32 columns x 64 k, NT = ceil(N/32) column tiles, KU = ceil(K/64) k units,
+// KG = ceil(KU/4) scale groups.
 struct PackedGeom {
-  int64_t NT, KT, KG;
+  int64_t NT, KU, KG;
   size_t code_bytes, scale_bytes;
   PackedGeom(int64_t N, int64_t K)
-      : NT(cdiv(N, 16)), KT(cdiv(K, 128)), KG(cdiv(cdiv(K, 128), 4)),
-        code_bytes((size_t)(cdiv(N, 16) * cdiv(K, 128)) * 1024u),
-        scale_bytes((size_t)(cdiv(N, 16) * cdiv(cdiv(K, 128), 4)) * 256u) {}
+      : NT(cdiv(N, 32)), KU(cdiv(K, 64)), KG(cdiv(cdiv(K, 64), 4)),
+        code_bytes((size_t)(cdiv(N, 32) * cdiv(K, 64)) * 1024u),
+        scale_bytes((size_t)(cdiv(N, 32) * cdiv(cdiv(K, 64), 4)) * 256u) {}
   size_t total() const { return code_bytes + scale_bytes; }
 };
 

@@ -22,6 +22,7 @@ namespace mx {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef unsigned short v2u16 __attribute__((ext_vector_type(2)));
 
@@ -78,6 +79,30 @@ __device__ __forceinline__ void quant32(const uint32_t (&w)[16], uint32_t (&q)[4
   }
 }
 
+// Quantise the 8 bf16 held by this lane (w[i]: elements 2i, 2i+1) as one quarter
+// of a 32-element MXFP4 block spread over the 4 lanes of an aligned lane quad
+// (lanes 4a .. 4a+3, all active). The block's amax is the max of the four lanes'
+// maxima, combined with two quad-permute DPP steps, so every lane of the quad
+// derives the same E8M0 byte. Returns this lane's 8 E2M1 codes (element 2i in
+// the low nibble of byte i).
+__device__ __forceinline__ uint32_t quant8_quad(const uint32_t (&w)[4], uint32_t& sbyte) {
+  const v2u16 m2 = __builtin_elementwise_max(__builtin_elementwise_max(abs_pair(w[0]), abs_pair(w[1])),
+                                             __builtin_elementwise_max(abs_pair(w[2]), abs_pair(w[3])));
+  uint32_t a = m2[0] > m2[1] ? m2[0] : m2[1];
+  uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
+  a = a > o ? a : o;
+  o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  a = a > o ? a : o;
+  sbyte = e8m0_from_amax_bits(a);
+  const float scale = __builtin_bit_cast(float, sbyte << 23);
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, w[0]), scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, w[1]), scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, w[2]), scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, w[3]), scale, 3);
+  return r;
+}
+
 // acc += (A * 2^(sa-127)) . (B * 2^(sb-127))^T over one 16x16x128 step.
 // SA/SB select which byte of the 32-bit scale registers is used.
 template <int SA = 0, int SB = 0>
@@ -86,6 +111,18 @@ __device__ __forceinline__ v4f mfma_fp4(const uint4& a, const uint4& b, v4f acc,
   const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, kFmtFp4, kFmtFp4, SA, (int)sa, SB,
                                                           (int)sb);
+}
+
+// acc += A . B^T over one 32x32x64 step (V_MFMA_SCALE_F32_32X32X64_F8F6F4, E2M1
+// operands). Lane l holds row (column of B) l%32 and k-chunk l/32 of its 32x64
+// operand plus that block's scale byte; result register r of lane l is
+// D[8*(r/4) + 4*(l/32) + r%4][l%32].
+template <int SA = 0, int SB = 0>
+__device__ __forceinline__ v16f mfma32_fp4(const uint4& a, const uint4& b, v16f acc, uint32_t sa, uint32_t sb) {
+  const v8i av = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+  const v8i bv = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, kFmtFp4, kFmtFp4, SA, (int)sa, SB,
+                                                         (int)sb);
 }
 
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN).

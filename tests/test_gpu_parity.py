@@ -106,18 +106,18 @@ def host_pack(bq, bs):
     """The layout stated in include/mxfp4.h, written out with NumPy indexing."""
     N, KH = bq.shape
     K = 2 * KH
-    NT, KT = -(-N // 16), -(-K // 128)
-    KG = -(-KT // 4)
-    Np, Kp = NT * 16, KT * 128
+    NT, KU = -(-N // 32), -(-K // 64)
+    KG = -(-KU // 4)
+    Np, Kp = NT * 32, KU * 64
     codes = np.zeros((Np, Kp // 2), np.uint8)
     codes[:N, :K // 2] = bq
-    # fragment (t, j), lane l: row 16t + l%16, bytes (128j + 32(l/16))/2 .. +16
-    frag = codes.reshape(NT, 16, KT, 4, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
-    sc = np.full((Np, KG * 16), 127, np.uint8)
+    # unit (t, u), lane l: row 32t + l%32, bytes (64u + 32(l/32))/2 .. +16
+    units = codes.reshape(NT, 32, KU, 2, 16).transpose(0, 2, 3, 1, 4).reshape(-1)
+    sc = np.full((Np, KG * 8), 127, np.uint8)
     sc[:N, :K // 32] = bs
-    # dword (t, g, l): byte i = scale[16t + l%16, 4(4g+i) + l/16]
-    scal = sc.reshape(NT, 16, KG, 4, 4).transpose(0, 2, 4, 1, 3).reshape(-1)
-    return np.concatenate([frag, scal])
+    # dword (t, g, l): byte i = scale[32t + l%32, 2(4g+i) + l/32]
+    scal = sc.reshape(NT, 32, KG, 4, 2).transpose(0, 2, 4, 1, 3).reshape(-1)
+    return np.concatenate([units, scal])
 
 
 @pytest.mark.parametrize("N,K", [(37, 352), (16, 128), (2112, 7168), (5, 32)])
