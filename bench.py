@@ -32,6 +32,10 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 FP4_PEAK_TFLOPS = 10100.0   # MI355X dense MXFP4 matrix peak, TFLOP/s
 METRIC = "µs/call, TFLOP/s and HBM GB/s (% of peak) for quant+a4w4 GEMM, M=16..4096"
 ROTATE_BYTES = 512 << 20
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["mxfp4_block_scaled_02_amd/csrc/gemm.hip", "mxfp4_block_scaled_02_amd/csrc/mx_device.hpp",
+                  "mxfp4_block_scaled_02_amd/csrc/host_common.hpp"]
+COPY_BYTES = 256 << 20  # plain device copy used to calibrate the FETCH_SIZE / WRITE_SIZE counters
 
 
 def alg_bytes(M, N, K):
@@ -53,14 +57,82 @@ def parse():
     p.add_argument("--warm-cache", action="store_true", help="reuse one operand set (Infinity Cache resident)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="time an eager launch loop instead of a graph replay")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run plain device copies of a known size (counter calibration)")
+    p.add_argument("--summarize-stats", metavar="DIR", help="print a summary of rocprofv3 --stats CSV output")
+    p.add_argument("--summarize-pmc", nargs=3, metavar=("WORKLOAD_DIR", "COPY_DIR", "KERNEL"),
+                   help="turn FETCH_SIZE/WRITE_SIZE runs into the traffic record for KERNEL")
     return p.parse_args()
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(name):
+    """HBM bytes per launch from the committed counter record, or None if the kernel changed since."""
+    path = os.path.join(PROFILES, f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True):
+        with open(path) as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize_stats(directory):
+    rows = _csv_rows(directory, "kernel_stats.csv")
+    print("| kernel | calls | avg µs | min µs | max µs | share % |")
+    print("|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        print(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+              f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.1f} |")
+
+
+def summarize_pmc(workload_dir, copy_dir, kernel):
+    """KiB per dispatch of FETCH_SIZE and WRITE_SIZE for KERNEL, scaled by the copy calibration."""
+    def per_dispatch(directory, match):
+        vals = {}
+        for r in _csv_rows(directory, "counter_collection.csv"):
+            if match in r["Kernel_Name"]:
+                vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in vals.items()}, {k: len(v) for k, v in vals.items()}
+    kv, kn = per_dispatch(workload_dir, kernel)
+    cv, cn = per_dispatch(copy_dir, "copy")  # torch's device copy kernel
+    expected_kib = COPY_BYTES / 1024
+    out = {"kernel": kernel, "kernel_source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES}
+    total = 0.0
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        factor = expected_kib / cv[c] if cv.get(c) else None
+        out[c] = {"kib_per_dispatch": kv.get(c), "dispatches": kn.get(c), "copy_kib": cv.get(c),
+                  "copy_factor": factor}
+        if kv.get(c) is not None and factor:
+            total += kv[c] * factor * 1024
+    out["bytes_per_launch"] = round(total)
+    print(json.dumps(out, indent=1))
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, unit, budget_s=20.0):
+def cpu_baseline(w, unit, budget_s=12.0):
     """Time the oracle (untuned) on a bounded sample of the workload, scaled to the metric's unit."""
     import oracle
     try:
@@ -85,7 +157,7 @@ def cpu_baseline(w, unit, budget_s=20.0):
         t0 = time.perf_counter()
         oracle.gemm_ref(a[rows], bq, bs)
         times.append(time.perf_counter() - t0)
-        if time.perf_counter() > t_end or len(times) >= 10:
+        if time.perf_counter() > t_end or len(times) >= 200:
             break
     t = float(np.median(times))
     m = len(rows)
@@ -94,8 +166,27 @@ def cpu_baseline(w, unit, budget_s=20.0):
                 sample=f"{sample_desc}; median of {len(times)} runs, {t * 1e3:.1f} ms each")
 
 
+def copy_calibration():
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES, "launches": 5}))
+
+
 def main():
     args = parse()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build measures the single-GPU "
               "kernel and has no multi-GPU path.", file=sys.stderr)
@@ -201,7 +292,7 @@ def main():
                dtype="mxfp4 (e2m1 x e8m0, fp32 accumulate, bf16 out)", data="synthetic", config=cfg,
                us_per_call=round(us, 3), tflops=round(tflops, 3), hbm_gbs=round(gbs, 2),
                roofline=dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
-                             frac=round(achieved / peak, 4), traffic=None,
+                             frac=round(achieved / peak, 4), traffic=recorded_traffic(name),
                              algorithmic_bytes=total_bytes, algorithmic_flops=total_flops))
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
