@@ -20,11 +20,14 @@
 //    partial tiles are summed in LDS. No cross-workgroup reduction: on this GPU a
 //    split-K hand-off through memory costs several microseconds, more than the
 //    whole skinny GEMM.
-//  * tiled (larger M): a 256-thread workgroup owns a 128 x 512 tile of C. Per
-//    128-wide K step the workgroup quantises the 128x128 bf16 A block once into a
-//    double-buffered LDS tile; each of the 4 waves computes 128 x 128 of C with
-//    the 32x32x64 instruction from that shared A and its own B units, which
-//    stream from global memory straight into registers one K step ahead.
+//  * tiled (larger M): a 512-thread workgroup (8 waves, one per CU) owns a
+//    128 x 512 tile of C. Per 128-wide K step the workgroup quantises the
+//    128x128 bf16 A block once into a double-buffered LDS tile; wave w computes
+//    all 128 rows x columns [64w, 64w+64) with the 32x32x64 instruction from that
+//    shared A and its own B units, which stream from global memory straight into
+//    registers one K step ahead. The two waves sharing a SIMD run their matrix
+//    and quantisation phases in opposite orders so the two overlap. The C tile
+//    leaves through a per-wave LDS staging block as 16-byte row stores.
 //    Workgroups are ordered so that the ones sharing an XCD (and its L2) share A
 //    rows and B columns.
 #include <type_traits>
@@ -54,20 +57,23 @@ struct Dims {
 };
 
 // Buffer resource over [base, base + bytes): raw buffer loads outside it return
-// zeros, which implements the M/N/K tails without branches. Offsets passed to the
-// loads are per-lane VGPR offsets; a moving window is made by advancing the base
-// (scalar arithmetic), so the hardware range check always sees the full offset.
+// zeros, which implements the M and N tails without branches. Each resource is
+// built once per tile; the K position moves through the scalar offset of the
+// load. The layouts below are chosen so that correctness does not depend on
+// whether the range check includes that scalar offset: out-of-range rows and
+// tiles are out of range by their per-lane offset alone, and elements past K are
+// either zeroed explicitly (A) or never loaded (B).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
   const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
-__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff) {
-  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, 0, 0);
+__device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
 __device__ __forceinline__ void to_words(const uint4& v, uint32_t (&w)[4]) {
   w[0] = v.x;
@@ -147,6 +153,21 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, D
     boff[t] = (uint32_t)((s16 >> 1) * 1024 + (((s16 & 1) * 32 + ((T0 + t) & 1) * 16 + (l & 15)) * 16));
   const int tail_k = d.K - 128 * (d.KT - 1);  // valid elements in the last K step
 
+  // Resources built once: A rows of the tile, and per 16-column tile its packed
+  // 32-column tile's code units and scale dwords (empty past the packed N).
+  const __amdgpu_buffer_rsrc_t ar = aw.at(0);
+  __amdgpu_buffer_rsrc_t brs[NB], bss[NB];
+  uint32_t soff[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t) {
+    const int t32 = (T0 + t) >> 1;
+    const bool ok = t32 < d.NT32;
+    brs[t] = make_rsrc(p.Bunit + (int64_t)t32 * d.KU * 1024, ok ? (int64_t)d.KU * 1024 : 0);
+    bss[t] = make_rsrc(p.Bscale + (int64_t)t32 * d.KG * 64, ok ? (int64_t)d.KG * 256 : 0);
+    soff[t] = (uint32_t)(((s16 & 1) * 32 + ((T0 + t) & 1) * 16 + (l & 15)) * 4);
+  }
+  const bool hi_unit = (s16 >> 1) != 0;  // lanes 32..63 read the step's second unit
+
   for (int j0 = jb; j0 < je; j0 += PF) {
     uint32_t w[PF][PIECES][4];
     uint4 bq[PF][NB];
@@ -155,18 +176,19 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, D
     for (int s = 0; s < PF; ++s) {
       const int j = j0 + s;
       if (j < je) {
+        const bool last_odd = 2 * j + 1 >= d.KU;  // odd K/64: the second unit does not exist
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
-          const int t32 = (T0 + t) >> 1;
-          const bool ok = t32 < d.NT32;
-          const uint8_t* ub = p.Bunit + ((int64_t)t32 * d.KU + 2 * j) * 1024;
-          bq[s][t] = bload16(make_rsrc(ub, ok ? (int64_t)(d.KU - 2 * j) * 1024 : 0), boff[t]);
-          const uint32_t* sbp = p.Bscale + ((int64_t)t32 * d.KG + (j >> 1)) * 64;
-          bs[s][t] = bload4(make_rsrc(sbp, ok ? 256 : 0), (uint32_t)(((s16 & 1) * 32 + ((T0 + t) & 1) * 16 + (l & 15)) * 4));
+          if (!last_odd) {
+            bq[s][t] = bload16(brs[t], boff[t], (uint32_t)j * 2048);
+          } else {
+            bq[s][t] = make_uint4(0u, 0u, 0u, 0u);
+            if (!hi_unit) bq[s][t] = bload16(brs[t], boff[t], (uint32_t)j * 2048);
+          }
+          bs[s][t] = bload4(bss[t], soff[t], (uint32_t)(j >> 1) * 256);
         }
-        const __amdgpu_buffer_rsrc_t ar = aw.at(j);
 #pragma unroll
-        for (int h = 0; h < PIECES; ++h) to_words(bload16(ar, aoff[h]), w[s][h]);
+        for (int h = 0; h < PIECES; ++h) to_words(bload16(ar, aoff[h], (uint32_t)j * 256), w[s][h]);
       }
     }
 #pragma unroll
@@ -217,7 +239,10 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, D
 // ---------------------------------------------------------------------------
 // Tiled kernel
 // ---------------------------------------------------------------------------
-constexpr int kTBM = 128, kTBN = 512, kTThreads = 256;
+// 512 threads (8 waves, two per SIMD so one wave's quantisation overlaps the
+// other's matrix instructions) own a 128 x 512 tile of C; wave w computes all
+// 128 rows x columns [64w, 64w+64) with 4 x 2 32x32x64 accumulators.
+constexpr int kTBM = 128, kTBN = 512, kTThreads = 512, kTWaves = kTThreads / 64;
 
 // A bijection on [0, G) giving each of the 8 XCDs (workgroup id mod 8) a
 // contiguous run of tiles, so the tiles sharing an L2 share A rows / B columns.
@@ -233,76 +258,98 @@ __device__ __forceinline__ int xcd_remap(int id, int G) {
 // conflict-free.
 __device__ __forceinline__ int slot32(int lane, int ks) { return lane ^ ((((ks << 1) | (lane >> 5)) & 3) << 2); }
 
+// Epilogue C staging block of one wave: 32 rows x 64 bf16 (32 dwords per row).
+// The 16-dword halves of rows with bit 2 set are swapped, which puts the 4 rows
+// of one packed write (rows a, a+1, a+4, a+5) and the 2 rows of one 16-lane read
+// phase on disjoint banks.
+constexpr int kCPitch = 32;
+__device__ __forceinline__ int cst_at(int row, int dword) { return row * kCPitch + (dword ^ (((row >> 2) & 1) << 4)); }
+
 // LDS of the tiled kernel (dwords): A operand codes [buffer][64-k half][32-row
-// tile][64 lanes x 4] and A scales [buffer][64-k half][lane] (byte = 32-row tile).
+// tile][64 lanes x 4], A scales [buffer][64-k half][lane] (byte = 32-row tile),
+// and a per-wave staging block for the C epilogue.
 struct TiledSmem {
   uint32_t a[2][2][4][256];
   uint32_t as[2][2][64];
+  uint32_t cst[kTWaves][32 * kCPitch];  // per-wave C staging, 32 rows x 64 bf16
 };
 
 __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int mt, int nt, TiledSmem& sm) {
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
   const int m0 = mt * kTBM;
-  const int t0 = nt * (kTBN / 32) + wave * 4;  // this wave's first 32-column packed tile
+  const int t0 = nt * (kTBN / 32) + wave * 2;  // this wave's first 32-column packed tile
 
-  mx::v16f acc[4][4];
+  mx::v16f acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][t][e] = 0.f;
 
-  // Thread tid owns pieces P = 256h + tid (h < 8) of the 128 x 16 pieces of a K
-  // step: row 16h + tid/16, elements 8*(tid%16) .. +7. A wave's pass covers 4
-  // whole rows (coalesced) and each lane quad holds one 32-element block.
+  // Thread tid owns pieces P = 512h + tid (h < 4) of the 128 x 16 pieces of a K
+  // step: row 32h + tid/16, elements 8*(tid%16) .. +7. Piece h lies in 32-row
+  // tile h; a wave's pass covers 4 whole rows (coalesced) and each lane quad
+  // holds one 32-element block.
   const AWindow aw = a_window(p, d.K, m0);
+  const __amdgpu_buffer_rsrc_t ar = aw.at(0);
   const uint32_t aoff0 = (uint32_t)(((tid >> 4) * p.lda + 8 * (tid & 15)) * 2);
-  const uint32_t arow16 = (uint32_t)(16 * p.lda * 2);
+  const uint32_t arow32 = (uint32_t)(32 * p.lda * 2);
   const int chunk = (tid & 15) >> 2, sub = tid & 3, qks = chunk >> 1;
-  // LDS dword written for piece h: block (buf, ks, i = h/2), slot of unit lane
-  // (chunk%2)*32 + 16*(h%2) + tid/16 (its XOR term is chunk << 2).
+  // LDS dword written for piece h: block (buf, ks, i = h), slot of unit lane
+  // (chunk%2)*32 + tid/16 (its XOR term is chunk << 2).
   const int wbase = (qks * 4) * 256 + ((chunk & 1) * 32 + ((tid >> 4) ^ (chunk << 2))) * 4 + sub;
   const int sbase = (qks * 64 + (chunk & 1) * 32 + (tid >> 4)) * 4;
   const int tail_k = d.K - 128 * (d.KT - 1);
 
-  uint32_t raw[8][4];
+  uint32_t raw[4][4];
   auto load_a = [&](int j) {
-    const __amdgpu_buffer_rsrc_t ar = aw.at(j);
 #pragma unroll
-    for (int h = 0; h < 8; ++h) to_words(bload16(ar, aoff0 + (uint32_t)h * arow16), raw[h]);
+    for (int h = 0; h < 4; ++h) to_words(bload16(ar, aoff0 + (uint32_t)h * arow32, (uint32_t)j * 256), raw[h]);
   };
   auto quant_store = [&](int j, int buf) {
     if (j == d.KT - 1 && tail_k < 128 && 8 * (tid & 15) >= tail_k) {  // K tail: not A
 #pragma unroll
-      for (int h = 0; h < 8; ++h) raw[h][0] = raw[h][1] = raw[h][2] = raw[h][3] = 0u;
+      for (int h = 0; h < 4; ++h) raw[h][0] = raw[h][1] = raw[h][2] = raw[h][3] = 0u;
     }
     uint32_t* const sa_base = &sm.a[buf][0][0][0];
     uint8_t* const ss_base = reinterpret_cast<uint8_t*>(&sm.as[buf][0][0]);
 #pragma unroll
-    for (int h = 0; h < 8; ++h) {
+    for (int h = 0; h < 4; ++h) {
       uint32_t sb;
       const uint32_t code = mx::quant8_quad(raw[h], sb);
-      sa_base[wbase + (h >> 1) * 256 + (h & 1) * 64] = code;
-      ss_base[sbase + (h & 1) * 64 + (h >> 1)] = (uint8_t)sb;  // the quad stores the same byte
+      sa_base[wbase + h * 256] = code;
+      ss_base[sbase + h] = (uint8_t)sb;  // the quad stores the same byte
     }
   };
-  // B of step j: units 2j (ks 0) and 2j+1 (ks 1) of this wave's 4 packed tiles,
-  // lane l's 16 bytes of each, and the tiles' scale dwords.
-  auto load_b = [&](int j, uint4 (&b)[2][4], uint32_t (&sc)[4]) {
+  __amdgpu_buffer_rsrc_t brs[2], bss[2];  // per packed tile: code units, scale dwords
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int t32 = t0 + t;
-      const bool ok = t32 < d.NT32;
-      const __amdgpu_buffer_rsrc_t br =
-          make_rsrc(p.Bunit + ((int64_t)t32 * d.KU + 2 * j) * 1024, ok ? (int64_t)(d.KU - 2 * j) * 1024 : 0);
-      b[0][t] = bload16(br, (uint32_t)l * 16);
-      b[1][t] = bload16(br, (uint32_t)l * 16 + 1024);
-      sc[t] = bload4(make_rsrc(p.Bscale + ((int64_t)t32 * d.KG + (j >> 1)) * 64, ok ? 256 : 0), (uint32_t)l * 4);
+  for (int t = 0; t < 2; ++t) {
+    const int t32 = t0 + t;
+    const bool ok = t32 < d.NT32;  // past the packed N: empty resource, loads give 0
+    brs[t] = make_rsrc(p.Bunit + (int64_t)t32 * d.KU * 1024, ok ? (int64_t)d.KU * 1024 : 0);
+    bss[t] = make_rsrc(p.Bscale + (int64_t)t32 * d.KG * 64, ok ? (int64_t)d.KG * 256 : 0);
+  }
+  // B of step j: units 2j (ks 0) and 2j+1 (ks 1) of this wave's 2 packed tiles,
+  // lane l's 16 bytes of each, and the tiles' scale dwords.
+  // `full`: both units exist (every step but the last), so no branch splits the
+  // load sequence.
+  auto load_b = [&](auto full, int j, uint4 (&b)[2][2], uint32_t (&sc)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      b[0][t] = bload16(brs[t], (uint32_t)l * 16, (uint32_t)j * 2048);
+      sc[t] = bload4(bss[t], (uint32_t)l * 4, (uint32_t)(j >> 1) * 256);
+    }
+    if (decltype(full)::value || 2 * j + 1 < d.KU) {  // the last step of an odd K/64 has one unit: never read past it
+#pragma unroll
+      for (int t = 0; t < 2; ++t) b[1][t] = bload16(brs[t], (uint32_t)l * 16 + 1024, (uint32_t)j * 2048);
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) b[1][t] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
-  auto compute = [&](int j, const uint4 (&b)[2][4], const uint32_t (&sc)[4]) {
+  auto compute = [&](int j, const uint4 (&b)[2][2], const uint32_t (&sc)[2]) {
     const int buf = j & 1;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
@@ -313,7 +360,7 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
       for (int i = 0; i < 4; ++i) {
         const uint4 a = *reinterpret_cast<const uint4*>(&sm.a[buf][ks][i][sl]);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < 2; ++t) {
           const uint32_t sb = sc[t] >> bsh;
           switch (i) {  // A scale byte = 32-row tile; folds once unrolled
             case 0: acc[i][t] = mx::mfma32_fp4<0, 0>(a, b[ks][t], acc[i][t], sa, sb); break;
@@ -325,54 +372,120 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
       }
     }
   };
-  // One K step j: B(j+1) is loaded into the other register set while step j
-  // computes; the bf16 A of step j+2 is loaded after the quantisation of A(j+1)
-  // into the other LDS buffer, so every load has about a whole step to land.
-  // FULL marks steps where j+2 < KT (no bounds tests).
-  auto step = [&](auto full, int j, const uint4 (&bc)[2][4], const uint32_t (&scc)[4], uint4 (&bn)[2][4],
-                  uint32_t (&scn)[4]) {
-    constexpr bool FULL = decltype(full)::value;
-    if (FULL || j + 1 < d.KT) load_b(j + 1, bn, scn);
+  // Quantise the raw bf16 A(j+1) into LDS buffer (j+1)&1 (steady state: no K tail).
+  auto quant_next = [&](int j) {
+    uint32_t* const sa_base = &sm.a[(j + 1) & 1][0][0][0];
+    uint8_t* const ss_base = reinterpret_cast<uint8_t*>(&sm.as[(j + 1) & 1][0][0]);
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      uint32_t sb;
+      const uint32_t code = mx::quant8_quad(raw[h], sb);
+      sa_base[wbase + h * 256] = code;
+      ss_base[sbase + h] = (uint8_t)sb;  // the quad stores the same byte
+    }
+  };
+  // Steady-state K step j (j + 2 < KT). B(j+1) is loaded into the other register
+  // set while step j computes; A(j+1) is quantised into the other LDS buffer and
+  // the bf16 A of step j+2 is requested. The two waves that share a SIMD (w and
+  // w+4) take the matrix and the quantisation phases in opposite orders, so that
+  // one wave's MFMAs run while the other wave's VALU quantisation runs.
+  uint4 bcur[2][2], bnxt[2][2];
+  uint32_t scur[2], snxt[2];
+  auto full_step = [&](auto mfma_first, int j) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(std::true_type{}, j + 1, bnxt, snxt);
     __syncthreads();  // A(j) is complete; every wave is past its reads of the other buffer
-    compute(j, bc, scc);
-    if (FULL || j + 1 < d.KT) {
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (decltype(mfma_first)::value) {
+      compute(j, bcur, scur);
+      __builtin_amdgcn_sched_barrier(0);
+      quant_next(j);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(j + 2);
+    } else {
+      quant_next(j);
+      __builtin_amdgcn_sched_barrier(0);
+      load_a(j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(j, bcur, scur);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bcur[0][t] = bnxt[0][t];
+      bcur[1][t] = bnxt[1][t];
+      scur[t] = snxt[t];
+    }
+  };
+  // Generic step for the last two K steps (bounds tests, K tail).
+  auto tail_step = [&](int j) {
+    if (j + 1 < d.KT) load_b(std::false_type{}, j + 1, bnxt, snxt);
+    __syncthreads();
+    compute(j, bcur, scur);
+    if (j + 1 < d.KT) {
       quant_store(j + 1, (j + 1) & 1);
-      if (FULL || j + 2 < d.KT) load_a(j + 2);
+      if (j + 2 < d.KT) load_a(j + 2);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bcur[0][t] = bnxt[0][t];
+        bcur[1][t] = bnxt[1][t];
+        scur[t] = snxt[t];
+      }
     }
   };
 
-  uint4 b0[2][4], b1[2][4];
-  uint32_t s0[4], s1[4];
   load_a(0);
-  load_b(0, b0, s0);
+  load_b(std::false_type{}, 0, bcur, scur);
   quant_store(0, 0);
   if (d.KT > 1) load_a(1);
   int j = 0;
-  for (; j + 3 < d.KT; j += 2) {  // steady state: straight-line, B sets alternate
-    step(std::true_type{}, j, b0, s0, b1, s1);
-    step(std::true_type{}, j + 1, b1, s1, b0, s0);
+  if (wave < kTWaves / 2) {  // uniform; each order is its own straight-line loop
+    for (; j + 2 < d.KT; ++j) full_step(std::true_type{}, j);
+  } else {
+    for (; j + 2 < d.KT; ++j) full_step(std::false_type{}, j);
   }
-  for (; j < d.KT; j += 2) {
-    step(std::false_type{}, j, b0, s0, b1, s1);
-    if (j + 1 < d.KT) step(std::false_type{}, j + 1, b1, s1, b0, s0);
-  }
+  for (; j < d.KT; ++j) tail_step(j);
 
-  // acc[i][t] register r of lane l: row 32i + 8(r/4) + 4(l/32) + r%4, column 32t + l%32.
-  const int rl = m0 + 4 * (l >> 5);
-  const int c0 = t0 * 32 + (l & 31);
-  uint16_t* const cb = p.C + (int64_t)rl * p.ldc + c0;
+  // Epilogue. acc[i][t] register r of lane l holds row 32i + 8(r/4) + 4(l/32) + r%4,
+  // column 32t + l%32 of this wave's 128 x 64 block. Per 32-row tile i: lane pairs
+  // (l, l^1) trade halves of their packed bf16 pairs so that each lane holds two
+  // adjacent columns of one row, the wave writes the 32 x 64 bf16 block to its
+  // LDS staging area, reads it back by rows and stores 16 bytes per lane.
+  uint32_t* const cst = sm.cst[wave];
+  const int odd = l & 1;
+  const int n0 = t0 * 32;  // first column of this wave's block
+  const bool vec = ((reinterpret_cast<uintptr_t>(p.C) & 15u) == 0) && ((p.ldc & 7) == 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int ro = 32 * i + 8 * (r >> 2) + (r & 3);
-      if (rl + ro < p.M) {
-        uint16_t* const crow = cb + (int64_t)ro * p.ldc;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-          if (c0 + 32 * t < d.N) crow[32 * t] = mx::f32_to_bf16(acc[i][t][r]);
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t pk = mx::pack_bf16x2(acc[i][t][2 * k], acc[i][t][2 * k + 1]);
+        const uint32_t q = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)pk, 0xB1, 0xF, 0xF, false);  // lane l^1
+        const uint32_t w = odd ? ((q >> 16) | (pk & 0xffff0000u)) : ((pk & 0xffffu) | (q << 16));
+        const int row = 8 * (k >> 1) + 4 * (l >> 5) + 2 * (k & 1) + odd;
+        cst[cst_at(row, 16 * t + ((l & 31) >> 1))] = w;
+      }
+    // LDS operations of one wave complete in order: the reads below see the writes.
+#pragma unroll
+    for (int qr = 0; qr < 4; ++qr) {
+      const int row = 8 * qr + (l >> 3), c8 = (l & 7) * 8;
+      const uint4 v = *reinterpret_cast<const uint4*>(&cst[cst_at(row, c8 / 2)]);
+      const int grow = m0 + 32 * i + row, gcol = n0 + c8;
+      if (grow < p.M) {
+        uint16_t* const dst = p.C + (int64_t)grow * p.ldc + gcol;
+        if (vec && gcol + 8 <= d.N) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+          const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (gcol + e < d.N) dst[e] = (uint16_t)(wv[e >> 1] >> (16 * (e & 1)));
+        }
       }
     }
+  }
 }
 
 __global__ __launch_bounds__(kTThreads) void gemm_tiled_kernel(Operand p, Dims d, int ntiles_n) {

@@ -133,6 +133,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 -> packed bf16 pair (lo = a, hi = b), round to nearest even: the gfx950
+// packed convert.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  const v2f f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, v2bf));
+}
+
 __device__ __forceinline__ uint4 ldg16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 }  // namespace mx
