@@ -106,7 +106,12 @@ int mxfp4_pack_B(const void* bq, const void* bs, int64_t N, int64_t K, void* out
  *   workspace : device scratch of at least gemm_a4w4_workspace_bytes(M, N, K)
  *        bytes (may be NULL when that size is 0), 256-byte aligned, ZEROED BY
  *        THE CALLER ONCE after allocation; every call leaves it zeroed again.
- *        Calls that may run concurrently need distinct workspaces.
+ *        Calls that may run concurrently need distinct workspaces. It is used
+ *        for M <= 16, where K is split over workgroups (page 683203, direct
+ *        GEMM call: its split-K argument) and each tile's last split sums the
+ *        others' fp32 partials, which pass through the workspace; larger M
+ *        needs none. Too small or NULL when needed: MXFP4_ERR_WORKSPACE; not
+ *        256-byte aligned: MXFP4_ERR_ALIGN.
  * ------------------------------------------------------------------------- */
 size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M,

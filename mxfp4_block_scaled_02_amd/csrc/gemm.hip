@@ -30,6 +30,7 @@
 //    leaves through a per-wave LDS staging block as 16-byte row stores.
 //    Workgroups are ordered so that the ones sharing an XCD (and its L2) share A
 //    rows and B columns.
+#include <algorithm>
 #include <type_traits>
 
 #include "host_common.hpp"
@@ -68,6 +69,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, 0x00020000);
 }
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+// Cache-policy operand of the buffer intrinsics: device scope (the access is
+// performed where every CU of the device observes it).
+constexpr int kCpolDevice = 16;
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
   const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
@@ -237,6 +241,184 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, D
 }
 
 // ---------------------------------------------------------------------------
+// Split-K kernel (M <= 16*MT, small)
+// ---------------------------------------------------------------------------
+// Grid: T tiles x S splits, workgroup id = tile * S + split. Tile t owns the
+// 16-column groups 4t .. 4t+3 (wave w computes group 4t+w) for all rows; split q
+// owns K steps [KT*q/S, KT*(q+1)/S). Each workgroup issues all of its loads at
+// once, quantises its A block once into LDS and runs the 16x16x128 instruction.
+// The splits of a tile are summed by its last split (the owner). Every other
+// split stores the bitwise complement of its fp32 partial with device scope and
+// exits; a workspace slot that still reads zero has not been written yet. The
+// owner polls its tile's slots (eight splits per round trip), adds the partials
+// in split order to its own, stores bf16 C and zeroes the slots again, so the
+// workspace is all zero between calls. No read-modify-write is shared between
+// workgroups (same-address atomics serialise at the memory side), and no
+// workgroup waits for one dispatched after it: the owner has the highest id of
+// its tile, so with in-order dispatch its producers have all started when it
+// starts, and they never wait. A partial whose bits are all ones (a NaN, from
+// non-finite input only) reads as unwritten; the poll bound then ends the wait.
+constexpr int kSpW = 4;           // waves per workgroup = column groups per tile
+constexpr int kSpT = kSpW * 64;
+constexpr int kSpMaxSteps = 8;    // K steps per split, at most (LDS size)
+constexpr int kSpMaxSplits = 64;
+constexpr int kSpBatch = 8;       // partial slots polled per round trip
+constexpr uint32_t kSpSpinCap = 1u << 22;  // owner's poll bound (never reached with finite input)
+
+struct SplitArgs {
+  uint32_t* part;  // [tile][split < S-1][wave][row tile][lane] x 4 words, complemented fp32; zero = empty
+  int S;
+};
+
+template <int MT>
+__global__ __launch_bounds__(kSpT) void gemm_splitk_kernel(Operand p, Dims d, SplitArgs sk) {
+  __shared__ __align__(16) uint32_t sAq[kSpMaxSteps][MT][64 * 4];  // A operand codes per step, row tile
+  __shared__ uint8_t sAs[kSpMaxSteps][MT][64];                    // A operand scales
+
+  const int tid = threadIdx.x, l = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int S = sk.S;
+  const int tile = blockIdx.x / S, q = blockIdx.x - tile * S;
+  const int jb = d.KT * q / S, ns = d.KT * (q + 1) / S - jb;
+  const int cg = tile * kSpW + wave;  // this wave's 16-column group
+  const int tail_k = d.K - 128 * (d.KT - 1);
+
+  // A: piece i = s*MT + rt is row 16rt + tid/16, elements 8*(tid%16) of step jb+s
+  // (a wave pass covers 4 whole rows; each lane quad holds one 32-element block).
+  const __amdgpu_buffer_rsrc_t ar = a_window(p, d.K, 0).at(0);
+  const uint32_t aoff = (uint32_t)(((tid >> 4) * p.lda + 8 * (tid & 15)) * 2);
+  const uint32_t arow16 = (uint32_t)(16 * p.lda * 2);
+  // Every load is issued unconditionally, before any of them is used: steps past
+  // this split's range repeat its last step (cache hits, never used). A guard
+  // per load would let the compiler pair each load with its use and wait for it.
+  uint32_t w[kSpMaxSteps * MT][4];
+#pragma unroll
+  for (int i = 0; i < kSpMaxSteps * MT; ++i) {
+    const int s = min(i / MT, ns - 1);
+    to_words(bload16(ar, aoff + (uint32_t)(i % MT) * arow16, (uint32_t)(jb + s) * 256), w[i]);
+  }
+
+  // B of column group cg (half of packed 32-column tile cg/2): as in the skinny
+  // kernel. Requested after A, so that the quantisation can start while B streams.
+  const int s16 = l >> 4;
+  const int t32 = cg >> 1;
+  const bool okB = t32 < d.NT32;
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(p.Bunit + (int64_t)t32 * d.KU * 1024, okB ? (int64_t)d.KU * 1024 : 0);
+  const __amdgpu_buffer_rsrc_t bss = make_rsrc(p.Bscale + (int64_t)t32 * d.KG * 64, okB ? (int64_t)d.KG * 256 : 0);
+  const uint32_t boff = (uint32_t)((s16 >> 1) * 1024 + (((s16 & 1) * 32 + (cg & 1) * 16 + (l & 15)) * 16));
+  const uint32_t soff = (uint32_t)(((s16 & 1) * 32 + (cg & 1) * 16 + (l & 15)) * 4);
+  const bool hi_unit = (s16 >> 1) != 0;
+  uint4 bq[kSpMaxSteps];
+  uint32_t bs[kSpMaxSteps];
+#pragma unroll
+  for (int s = 0; s < kSpMaxSteps; ++s) {
+    const int j = jb + min(s, ns - 1);
+    // Odd K/64: the last step has no second unit; its lanes read the first one
+    // (in range) and are zeroed below.
+    const bool no_unit = 2 * j + 1 >= d.KU && hi_unit;
+    bq[s] = bload16(brs, no_unit ? boff - 1024 : boff, (uint32_t)j * 2048);
+    bs[s] = bload4(bss, soff, (uint32_t)(j >> 1) * 256);
+    if (no_unit) bq[s] = make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  // Quantise A into the operand layout of the 16x16x128 instruction.
+  const int chunk = (tid & 15) >> 2, sub = tid & 3;
+  const int wslot = slot16(tid >> 4, chunk);
+#pragma unroll
+  for (int i = 0; i < kSpMaxSteps * MT; ++i) {
+    if (i < ns * MT) {
+      const int s = i / MT, rt = i % MT;
+      if (jb + s == d.KT - 1 && tail_k < 128 && 8 * (tid & 15) >= tail_k) w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
+      uint32_t sb;
+      const uint32_t code = mx::quant8_quad(w[i], sb);
+      sAq[s][rt][wslot * 4 + sub] = code;
+      sAs[s][rt][wslot] = (uint8_t)sb;  // the quad's four lanes store the same byte
+    }
+  }
+  __syncthreads();
+
+  mx::v4f acc[MT];
+#pragma unroll
+  for (int rt = 0; rt < MT; ++rt) acc[rt] = mx::v4f{0.f, 0.f, 0.f, 0.f};
+  const int aslot = slot16(l & 15, l >> 4);
+#pragma unroll
+  for (int s = 0; s < kSpMaxSteps; ++s) {
+    if (s < ns) {
+      const int bsh = 8 * ((2 * (jb + s) + (l >> 5)) & 3);
+#pragma unroll
+      for (int rt = 0; rt < MT; ++rt) {
+        const uint4 a = *reinterpret_cast<const uint4*>(&sAq[s][rt][aslot * 4]);
+        acc[rt] = mx::mfma_fp4(a, bq[s], acc[rt], sAs[s][rt][aslot], bs[s] >> bsh);
+      }
+    }
+  }
+
+  if (S > 1) {
+    const int64_t tile_part = (int64_t)tile * (S - 1) * kSpW * MT * 64 * 16;  // bytes
+    const __amdgpu_buffer_rsrc_t pr =
+        make_rsrc(reinterpret_cast<uint8_t*>(sk.part) + tile_part, (int64_t)(S - 1) * kSpW * MT * 64 * 16);
+    auto part_off = [&](int qq, int rt) { return (int)((((qq * kSpW + wave) * MT + rt) * 64 + l) * 16); };
+    // Whole-vector casts only: with this compiler a bit cast of one element of a
+    // vector value reads element 0 whatever the index.
+    if (q < S - 1) {
+#pragma unroll
+      for (int rt = 0; rt < MT; ++rt)
+        __builtin_amdgcn_raw_buffer_store_b128(~__builtin_bit_cast(u32x4, acc[rt]), pr, part_off(q, rt), 0,
+                                               kCpolDevice);
+      return;
+    }
+    // Owner: each wave collects its own column group's partials.
+    mx::v4f sum[MT];
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt) sum[rt] = mx::v4f{0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < S - 1; q0 += kSpBatch) {
+      const int nb = min(kSpBatch, S - 1 - q0);
+      u32x4 v[kSpBatch][MT];
+      for (uint32_t it = 0;; ++it) {
+        // All loads first (slots past the batch repeat its last one), then the test.
+#pragma unroll
+        for (int b = 0; b < kSpBatch; ++b)
+#pragma unroll
+          for (int rt = 0; rt < MT; ++rt)
+            v[b][rt] = __builtin_amdgcn_raw_buffer_load_b128(pr, part_off(q0 + min(b, nb - 1), rt), 0, kCpolDevice);
+        bool ready = true;
+#pragma unroll
+        for (int b = 0; b < kSpBatch; ++b)
+#pragma unroll
+          for (int rt = 0; rt < MT; ++rt) {
+            const u32x4 x = v[b][rt];
+            ready = ready && x.x != 0u && x.y != 0u && x.z != 0u && x.w != 0u;
+          }
+        if (__builtin_amdgcn_ballot_w64(!ready) == 0 || it >= kSpSpinCap) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+#pragma unroll
+      for (int b = 0; b < kSpBatch; ++b)
+        if (b < nb)
+#pragma unroll
+          for (int rt = 0; rt < MT; ++rt) {
+            sum[rt] += __builtin_bit_cast(mx::v4f, ~v[b][rt]);
+            __builtin_amdgcn_raw_buffer_store_b128(u32x4{0u, 0u, 0u, 0u}, pr, part_off(q0 + b, rt), 0, kCpolDevice);
+          }
+    }
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt) acc[rt] = sum[rt] + acc[rt];
+  }
+
+  // acc[rt] register e of lane l: row 16rt + 4(l/16) + e, column 16cg + l%16.
+  const int col = cg * 16 + (l & 15);
+  if (col < d.N) {
+#pragma unroll
+    for (int rt = 0; rt < MT; ++rt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = 16 * rt + 4 * (l >> 4) + e;
+        if (row < p.M) p.C[(int64_t)row * p.ldc + col] = mx::f32_to_bf16(acc[rt][e]);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Tiled kernel
 // ---------------------------------------------------------------------------
 // 512 threads (8 waves, two per SIMD so one wave's quantisation overlaps the
@@ -292,10 +474,12 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   // step: row 32h + tid/16, elements 8*(tid%16) .. +7. Piece h lies in 32-row
   // tile h; a wave's pass covers 4 whole rows (coalesced) and each lane quad
   // holds one 32-element block.
-  const AWindow aw = a_window(p, d.K, m0);
-  const __amdgpu_buffer_rsrc_t ar = aw.at(0);
+  // One resource per piece h, over the window of rows m0 + 32h onwards, so the
+  // four loads share one per-lane offset and each stays range-checked by it.
+  __amdgpu_buffer_rsrc_t ar[4];
+#pragma unroll
+  for (int h = 0; h < 4; ++h) ar[h] = a_window(p, d.K, m0 + 32 * h).at(0);
   const uint32_t aoff0 = (uint32_t)(((tid >> 4) * p.lda + 8 * (tid & 15)) * 2);
-  const uint32_t arow32 = (uint32_t)(32 * p.lda * 2);
   const int chunk = (tid & 15) >> 2, sub = tid & 3, qks = chunk >> 1;
   // LDS dword written for piece h: block (buf, ks, i = h), slot of unit lane
   // (chunk%2)*32 + tid/16 (its XOR term is chunk << 2).
@@ -306,7 +490,7 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   uint32_t raw[4][4];
   auto load_a = [&](int j) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) to_words(bload16(ar, aoff0 + (uint32_t)h * arow32, (uint32_t)j * 256), raw[h]);
+    for (int h = 0; h < 4; ++h) to_words(bload16(ar[h], aoff0, (uint32_t)j * 256), raw[h]);
   };
   auto quant_store = [&](int j, int buf) {
     if (j == d.KT - 1 && tail_k < 128 && 8 * (tid & 15) >= tail_k) {  // K tail: not A
@@ -349,28 +533,40 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
       for (int t = 0; t < 2; ++t) b[1][t] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
+  // Step j's 16 matrix instructions. The four A operands of the first 64-k half
+  // (and its scale dword) are read from LDS up front; the second half's reads
+  // are issued behind the first half's matrix instructions.
   auto compute = [&](int j, const uint4 (&b)[2][2], const uint32_t (&sc)[2]) {
     const int buf = j & 1;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int bsh = 8 * ((2 * j + ks) & 3);
-      const uint32_t sa = sm.as[buf][ks][l];
+    uint4 a[2][4];
+    uint32_t sa[2];
+    auto read_half = [&](int ks) {
+      sa[ks] = sm.as[buf][ks][l];
       const int sl = slot32(l, ks) * 4;
 #pragma unroll
+      for (int i = 0; i < 4; ++i) a[ks][i] = *reinterpret_cast<const uint4*>(&sm.a[buf][ks][i][sl]);
+    };
+    auto mfma_half = [&](int ks) {
+      const int bsh = 8 * ((2 * j + ks) & 3);
+#pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&sm.a[buf][ks][i][sl]);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const uint32_t sb = sc[t] >> bsh;
           switch (i) {  // A scale byte = 32-row tile; folds once unrolled
-            case 0: acc[i][t] = mx::mfma32_fp4<0, 0>(a, b[ks][t], acc[i][t], sa, sb); break;
-            case 1: acc[i][t] = mx::mfma32_fp4<1, 0>(a, b[ks][t], acc[i][t], sa, sb); break;
-            case 2: acc[i][t] = mx::mfma32_fp4<2, 0>(a, b[ks][t], acc[i][t], sa, sb); break;
-            default: acc[i][t] = mx::mfma32_fp4<3, 0>(a, b[ks][t], acc[i][t], sa, sb); break;
+            case 0: acc[i][t] = mx::mfma32_fp4<0, 0>(a[ks][i], b[ks][t], acc[i][t], sa[ks], sb); break;
+            case 1: acc[i][t] = mx::mfma32_fp4<1, 0>(a[ks][i], b[ks][t], acc[i][t], sa[ks], sb); break;
+            case 2: acc[i][t] = mx::mfma32_fp4<2, 0>(a[ks][i], b[ks][t], acc[i][t], sa[ks], sb); break;
+            default: acc[i][t] = mx::mfma32_fp4<3, 0>(a[ks][i], b[ks][t], acc[i][t], sa[ks], sb); break;
           }
         }
       }
-    }
+    };
+    read_half(0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_half(1);
+    mfma_half(0);
+    mfma_half(1);
   };
   // Quantise the raw bf16 A(j+1) into LDS buffer (j+1)&1 (steady state: no K tail).
   auto quant_next = [&](int j) {
@@ -576,6 +772,56 @@ SkinnyShape choose_skinny(int64_t M, int64_t N, int64_t K) {
   return best;
 }
 
+// Split-K geometry for M <= 16: 64-column tiles, and as many K splits as make
+// about one workgroup per CU (tiles x splits ~ 256), with at most kSpMaxSteps K
+// steps per split. The workspace holds the complemented fp32 partials of all
+// splits but the owner; it is all zero between calls.
+struct SplitGeom {
+  int MT = 0, T = 0, S = 0;
+  size_t part_bytes = 0;
+  bool ok = false;
+  size_t total() const { return part_bytes; }
+};
+SplitGeom split_geom(int64_t M, int64_t N, int64_t K) {
+  SplitGeom g;
+  if (M < 1 || M > 16 || N < 1 || K < 32) return g;
+  const int64_t KT = mxh::cdiv(K, 128);
+  const int64_t T = mxh::cdiv(mxh::cdiv(N, 16), kSpW);
+  const int64_t smin = mxh::cdiv(KT, kSpMaxSteps);
+  if (smin > kSpMaxSplits || T * kSpMaxSplits > INT32_MAX) return g;
+  // Pick S by a simple time model: a workgroup's loads take a latency plus its
+  // bytes at one CU's streaming rate, rounds of more workgroups than CUs add up,
+  // and splitting adds one device-scope hand-off to the owners.
+  int64_t S = smin;
+  double best = -1.0;
+  for (int64_t s = smin; s <= std::min<int64_t>(KT, kSpMaxSplits); ++s) {
+    const double steps = (double)mxh::cdiv(KT, s);
+    const double bytes = steps * (16.0 * 128 * 2 + kSpW * 1024.0 + kSpW * 256.0);  // A, B codes, B scales
+    const double rounds = (double)mxh::cdiv(T * s, 256);
+    const double t = rounds * (1.0 + bytes / 25e3) + (s > 1 ? 1.5 : 0.0);  // microseconds
+    if (best < 0 || t < best - 1e-9) {
+      best = t;
+      S = s;
+    }
+  }
+  g.MT = 1;
+  g.T = (int)T;
+  g.S = (int)S;
+  g.part_bytes = (size_t)T * (size_t)(S - 1) * kSpW * g.MT * 64 * 16;
+  g.ok = true;
+  return g;
+}
+
+hipError_t launch_splitk(const Operand& o, const Dims& d, const SplitGeom& g, void* ws, hipStream_t st) {
+  Operand op = o;
+  Dims dd = d;
+  SplitArgs sa{};
+  sa.part = (uint32_t*)ws;
+  sa.S = g.S;
+  void* args[] = {&op, &dd, &sa};
+  return hipLaunchKernel((const void*)gemm_splitk_kernel<1>, dim3((unsigned)(g.T * g.S)), dim3(kSpT), args, 0, st);
+}
+
 hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, int64_t K, hipStream_t st) {
   if (M <= 64) {
     const SkinnyShape sh = choose_skinny(M, N, K);
@@ -602,21 +848,27 @@ hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, in
 }  // namespace
 
 extern "C" size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
-  (void)M;
-  (void)N;
-  (void)K;
-  return 0;  // every output tile is reduced inside one workgroup
+  if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || M > mxh::kMaxDim || N > mxh::kMaxDim || K > mxh::kMaxDim) return 0;
+  const SplitGeom g = split_geom(M, N, K);
+  return g.ok ? g.total() : 0;  // larger M: every output tile is reduced inside one workgroup
 }
 
 extern "C" int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M, int64_t N,
                                int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   const int st = check_problem(A, lda, Bp, C, ldc, M, N, K);
   if (st != MXFP4_OK) return st;
   if (mxh::cdiv(M, kTBM) * mxh::cdiv(N, kTBN) > INT32_MAX) return MXFP4_ERR_SHAPE;
   const Operand o = make_operand(A, lda, Bp, C, ldc, M, N, K);
-  return mxh::launch_status(launch_gemm(o, make_dims(N, K), M, N, K, (hipStream_t)stream));
+  const Dims d = make_dims(N, K);
+  const SplitGeom g = split_geom(M, N, K);
+  if (g.ok) {
+    if (g.total() > 0) {
+      if (!workspace || workspace_bytes < g.total()) return MXFP4_ERR_WORKSPACE;
+      if (!mxh::aligned(workspace, 256)) return MXFP4_ERR_ALIGN;
+    }
+    return mxh::launch_status(launch_splitk(o, d, g, workspace, (hipStream_t)stream));
+  }
+  return mxh::launch_status(launch_gemm(o, d, M, N, K, (hipStream_t)stream));
 }
 
 extern "C" size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K) {

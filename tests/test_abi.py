@@ -53,11 +53,31 @@ def test_pack_B_bytes_invalid_is_zero(N, K):
     assert ops.lib().mxfp4_pack_B_bytes(N, K) == 0
 
 
+def _splitk_range(M, N, K):
+    """Split-K workspace (M <= 16), from the header's geometry: T = ceil(ceil(N/16)/4)
+    tiles of 64 columns and S splits with ceil(KT/8) <= S <= min(KT, 64), KT =
+    ceil(K/128); the fp32 partials (16 x 64 per tile) of S-1 splits, i.e.
+    T*(S-1)*4096 bytes. Returns (T, smin, smax), or None when split-K is not used."""
+    KT = -(-K // 128)
+    T = -(-(-(-N // 16)) // 4)
+    smin = -(-KT // 8)
+    if smin > 64:
+        return None
+    return T, smin, min(KT, 64)
+
+
 def test_workspace_sizes_are_consistent():
-    # every output tile is reduced inside one workgroup: no workspace is needed
     L = ops.lib()
     assert L.gemm_a4w4_workspace_bytes(0, 16, 32) == 0
-    for M, N, K in [(4, 256, 512), (16, 2112, 7168), (64, 7168, 2048), (4096, 4096, 7168)]:
+    assert L.gemm_a4w4_workspace_bytes(4, 16, 48) == 0  # invalid K
+    for M, N, K in [(4, 256, 512), (16, 2112, 7168), (1, 4096, 7168), (16, 64, 65536), (1, 1, 32), (16, 130, 7232)]:
+        T, smin, smax = _splitk_range(M, N, K)
+        w = L.gemm_a4w4_workspace_bytes(M, N, K)
+        assert w % (T * 4096) == 0 and smin <= w // (T * 4096) + 1 <= smax, (M, N, K, w)
+    assert L.gemm_a4w4_workspace_bytes(16, 2112, 7168) > 0  # K = 7168 needs at least 7 splits
+    assert L.gemm_a4w4_workspace_bytes(16, 64, 65536) == 63 * 4096  # 512 K steps: 64 splits
+    assert L.gemm_a4w4_workspace_bytes(16, 48, 66560) == 0  # more than 64 splits: no split-K
+    for M, N, K in [(17, 2112, 7168), (64, 7168, 2048), (4096, 4096, 7168)]:
         assert L.gemm_a4w4_workspace_bytes(M, N, K) == 0
 
 
@@ -94,6 +114,7 @@ OK_G = dict(A=P, lda=7168, Bp=P, C=P, ldc=2112, M=16, N=2112, K=7168, ws=P, wsb=
     (dict(M=0), 2), (dict(N=0), 2), (dict(K=7000), 2), (dict(lda=7000), 2), (dict(ldc=2000), 2),
     (dict(M=1 << 31), 2),
     (dict(A=P + 2), 3), (dict(lda=7172), 3), (dict(Bp=P + 8), 3), (dict(C=P + 1), 3),
+    (dict(ws=None), 4), (dict(wsb=1024), 4), (dict(ws=P + 16), 3),
 ])
 def test_gemm_validation(change, status):
     a = dict(OK_G, **change)
