@@ -62,6 +62,8 @@ def parse():
     p.add_argument("--summarize-stats", metavar="DIR", help="print a summary of rocprofv3 --stats CSV output")
     p.add_argument("--summarize-pmc", nargs=3, metavar=("WORKLOAD_DIR", "COPY_DIR", "KERNEL"),
                    help="turn FETCH_SIZE/WRITE_SIZE runs into the traffic record for KERNEL")
+    p.add_argument("--summarize-counters", nargs=2, metavar=("DIR", "KERNEL"),
+                   help="per-dispatch averages of every counter collected for KERNEL, and the MFMA busy fraction")
     return p.parse_args()
 
 
@@ -128,6 +130,23 @@ def summarize_pmc(workload_dir, copy_dir, kernel):
     print(json.dumps(out, indent=1))
 
 
+def summarize_counters(directory, kernel):
+    """Per-dispatch averages of the counters of one rocprofv3 --pmc run. The MFMA busy
+    fraction is SQ_VALU_MFMA_BUSY_CYCLES (summed over the 1024 SIMDs) over the kernel's
+    cycles, GRBM_GUI_ACTIVE (summed over the 8 XCDs) / 8, times 1024."""
+    vals = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if kernel in r["Kernel_Name"]:
+            vals.setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    out = {k: {"per_dispatch": sum(v) / len(v), "dispatches": len(v)} for k, v in sorted(vals.items())}
+    busy, active = vals.get("SQ_VALU_MFMA_BUSY_CYCLES"), vals.get("GRBM_GUI_ACTIVE")
+    if busy and active:
+        cycles = (sum(active) / len(active)) / 8
+        out["mfma_busy_fraction"] = (sum(busy) / len(busy)) / (1024 * cycles)
+        out["kernel_cycles"] = cycles
+    print(json.dumps(out, indent=1))
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -183,6 +202,9 @@ def main():
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
     if args.copy_calibration:
         copy_calibration()

@@ -484,7 +484,9 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   // LDS dword written for piece h: block (buf, ks, i = h), slot of unit lane
   // (chunk%2)*32 + tid/16 (its XOR term is chunk << 2).
   const int wbase = (qks * 4) * 256 + ((chunk & 1) * 32 + ((tid >> 4) ^ (chunk << 2))) * 4 + sub;
-  const int sbase = (qks * 64 + (chunk & 1) * 32 + (tid >> 4)) * 4;
+  // Scale dword of this lane's 4 pieces: byte h is the scale of piece h (32-row
+  // tile h), so one lane per quad stores all four as one dword.
+  const int sdw = qks * 64 + (chunk & 1) * 32 + (tid >> 4);
   const int tail_k = d.K - 128 * (d.KT - 1);
 
   uint32_t raw[4][4];
@@ -498,14 +500,15 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
       for (int h = 0; h < 4; ++h) raw[h][0] = raw[h][1] = raw[h][2] = raw[h][3] = 0u;
     }
     uint32_t* const sa_base = &sm.a[buf][0][0][0];
-    uint8_t* const ss_base = reinterpret_cast<uint8_t*>(&sm.as[buf][0][0]);
+    uint32_t sw = 0;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       uint32_t sb;
       const uint32_t code = mx::quant8_quad(raw[h], sb);
       sa_base[wbase + h * 256] = code;
-      ss_base[sbase + h] = (uint8_t)sb;  // the quad stores the same byte
+      sw |= sb << (8 * h);
     }
+    if (sub == 0) (&sm.as[buf][0][0])[sdw] = sw;  // the quad's lanes hold the same scales
   };
   __amdgpu_buffer_rsrc_t brs[2], bss[2];  // per packed tile: code units, scale dwords
 #pragma unroll
@@ -571,14 +574,15 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   // Quantise the raw bf16 A(j+1) into LDS buffer (j+1)&1 (steady state: no K tail).
   auto quant_next = [&](int j) {
     uint32_t* const sa_base = &sm.a[(j + 1) & 1][0][0][0];
-    uint8_t* const ss_base = reinterpret_cast<uint8_t*>(&sm.as[(j + 1) & 1][0][0]);
+    uint32_t sw = 0;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       uint32_t sb;
       const uint32_t code = mx::quant8_quad(raw[h], sb);
       sa_base[wbase + h * 256] = code;
-      ss_base[sbase + h] = (uint8_t)sb;  // the quad stores the same byte
+      sw |= sb << (8 * h);
     }
+    if (sub == 0) (&sm.as[(j + 1) & 1][0][0])[sdw] = sw;  // the quad's lanes hold the same scales
   };
   // Steady-state K step j (j + 2 < KT). B(j+1) is loaded into the other register
   // set while step j computes; A(j+1) is quantised into the other LDS buffer and

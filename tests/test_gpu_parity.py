@@ -152,6 +152,31 @@ def test_gemm_square_sampled_rows():
     assert_in_tolerance(c[rows], oracle.gemm_ref(w["A"][rows], bq, bs), "square")
 
 
+# Robustness runs: the same workloads from a second seed (100 + the workload's index).
+@pytest.mark.parametrize("name", ["tiny", "skinny", "stress"])
+def test_workload_second_seed(name):
+    seed = 100 + synth.default_seed(name)
+    say(f"workload {name} seed {seed}: quant bytes and full C")
+    w = synth.workload(name, seed)
+    q, s = gpu_quant(w["A"])
+    rq, rs = oracle.quant_mx(w["A"])
+    assert np.array_equal(q, rq) and np.array_equal(s, rs)
+    bq, bs = oracle.quant_mx(w["B"])
+    c = run_gemm(w["A"], bq, bs, w["N"])
+    assert_in_tolerance(bits_of(c), oracle.gemm_ref(w["A"], bq, bs), f"{name} seed {seed}")
+
+
+def test_square_second_seed_sampled_rows():
+    seed = 100 + synth.default_seed("square")
+    say(f"gemm workload square seed {seed} (sampled rows)")
+    w = synth.workload("square", seed)
+    bq, bs = oracle.quant_mx(w["B"])
+    c = bits_of(run_gemm(w["A"], bq, bs, w["N"]))
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(4096 - 8, 4096),
+                                     np.random.default_rng(seed).choice(4096, 32, replace=False)]))
+    assert_in_tolerance(c[rows], oracle.gemm_ref(w["A"][rows], bq, bs), f"square seed {seed}")
+
+
 @pytest.mark.timeout(600)
 def test_grouped_workload_sampled_rows():
     say("grouped workload (sampled rows)")
