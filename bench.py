@@ -57,6 +57,8 @@ def parse():
     p.add_argument("--warm-cache", action="store_true", help="reuse one operand set (Infinity Cache resident)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="time an eager launch loop instead of a graph replay")
+    p.add_argument("--unfused", action="store_true",
+                   help="time the two-launch comparator instead: mxfp4_quant(A), then gemm_a4w4 on A_q")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain device copies of a known size (counter calibration)")
     p.add_argument("--summarize-stats", metavar="DIR", help="print a summary of rocprofv3 --stats CSV output")
@@ -256,11 +258,19 @@ def main():
             b = b0.clone() if r else b0
             c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         sets.append((a, b, c))
+    if args.unfused:
+        if name == "grouped":
+            raise SystemExit("--unfused covers the single-GEMM workloads")
+        aq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
+        asc = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
 
     def step(i):
         a, b, c = sets[i % R]
         if name == "grouped":
             ops.grouped_gemm(a, b, N, out_list=c)
+        elif args.unfused:
+            ops.quant(a, out=(aq, asc))
+            ops.gemm_a4w4(aq, asc, b, N, out=c)
         else:
             ops.gemm(a, b, N, out=c)
 
@@ -304,7 +314,8 @@ def main():
         bound, achieved, peak, unit = "hbm", gbs, HBM_PEAK_GBS, "GB/s"
     value = achieved
     cfg = dict(workload=name, seed=seed, cache="warm (1 set)" if R == 1 else f"cold ({R} rotated operand sets)",
-               timing="hip graph replay" if not args.no_graph else "eager launch loop")
+               timing="hip graph replay" if not args.no_graph else "eager launch loop",
+               path="unfused: mxfp4_quant + gemm_a4w4 (two launches)" if args.unfused else "fused: gemm_a4w4_fused")
     if name == "grouped":
         cfg.update(G=len(Ms), Ms=Ms, N=N, K=K)
     else:

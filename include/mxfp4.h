@@ -118,6 +118,21 @@ int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t
                     int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * gemm_a4w4 -- C[M, N] = A_q . B^T with A ALREADY quantised (for example by
+ * mxfp4_quant): the unfused pipeline of page 683203's anatomy (quantise A in
+ * one launch, then run the block-scaled GEMM on A_q and its scales), kept as
+ * a comparator for the fused call. Same arithmetic as gemm_a4w4_fused: on the
+ * bytes mxfp4_quant(A) produces it gives the fused call's C.
+ *   Aq : fp4x2 [M, K/2], row stride ldaq bytes (ldaq >= K/2, ldaq <= 2^24);
+ *        Aq and ldaq must be multiples of 16 bytes.
+ *   As : E8M0 [M, K/32], row stride ldas bytes (K/32 <= ldas <= 2^24).
+ *   Bp, C, ldc, M, N, K, workspace : as for gemm_a4w4_fused, including the
+ *        workspace size (gemm_a4w4_workspace_bytes(M, N, K)).
+ * ------------------------------------------------------------------------- */
+int gemm_a4w4(const void* Aq, int64_t ldaq, const void* As, int64_t ldas, const void* Bp, void* C, int64_t ldc,
+              int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * grouped_gemm_a4w4 -- G independent fused problems C_g = Q(A_g) . B_g^T that
  * share N and K, in ONE launch (page 496271, ``custom_kernel``: a list of
  * per-group problems; there one launch per group, here a single launch whose

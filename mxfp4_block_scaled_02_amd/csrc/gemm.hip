@@ -39,8 +39,12 @@
 namespace {
 
 struct Operand {
-  const uint16_t* A;
+  const uint16_t* A;       // bf16 A (fused path)
   int64_t lda;
+  const uint8_t* Aq;       // pre-quantised A (gemm_a4w4): fp4x2 [M, K/2], row stride ldaq bytes
+  int64_t ldaq;
+  const uint8_t* As;       // and its E8M0 scales [M, K/32], row stride ldas bytes
+  int64_t ldas;
   const uint8_t* Bunit;    // packed codes: unit (t, u) at (t*KU + u)*1024
   const uint32_t* Bscale;  // packed scale dwords: (t, g, lane) at (t*KG + g)*64 + lane
   uint16_t* C;
@@ -79,6 +83,9 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 __device__ __forceinline__ uint32_t bload4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
+__device__ __forceinline__ uint32_t bload1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff = 0) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
 __device__ __forceinline__ void to_words(const uint4& v, uint32_t (&w)[4]) {
   w[0] = v.x;
   w[1] = v.y;
@@ -97,6 +104,12 @@ struct AWindow {
     return make_rsrc(base + (int64_t)j * 256, bytes - (int64_t)j * 256);
   }
 };
+// Rows m0.. of a byte matrix with row stride ld and rowlen meaningful bytes
+// (pre-quantised A codes or scales): in range up to the end of row M-1.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_window(const uint8_t* base, int64_t ld, int64_t rowlen, int M,
+                                                             int m0) {
+  return make_rsrc(base + (int64_t)m0 * ld, m0 < M ? (int64_t)(M - 1 - m0) * ld + rowlen : 0);
+}
 __device__ __forceinline__ AWindow a_window(const Operand& p, int K, int m0) {
   AWindow w;
   w.base = reinterpret_cast<const uint8_t*>(p.A) + (int64_t)m0 * p.lda * 2;
@@ -270,10 +283,12 @@ struct SplitArgs {
   int S;
 };
 
-template <int MT>
+// PREQ: A arrives pre-quantised (gemm_a4w4); each lane then loads its operand and
+// scale byte directly, and the quantisation and LDS stages are skipped.
+template <int MT, bool PREQ>
 __global__ __launch_bounds__(kSpT) void gemm_splitk_kernel(Operand p, Dims d, SplitArgs sk) {
-  __shared__ __align__(16) uint32_t sAq[kSpMaxSteps][MT][64 * 4];  // A operand codes per step, row tile
-  __shared__ uint8_t sAs[kSpMaxSteps][MT][64];                    // A operand scales
+  __shared__ __align__(16) uint32_t sAq[PREQ ? 1 : kSpMaxSteps][MT][64 * 4];  // A operand codes per step, row tile
+  __shared__ uint8_t sAs[PREQ ? 1 : kSpMaxSteps][MT][64];                    // A operand scales
 
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -283,19 +298,40 @@ __global__ __launch_bounds__(kSpT) void gemm_splitk_kernel(Operand p, Dims d, Sp
   const int cg = tile * kSpW + wave;  // this wave's 16-column group
   const int tail_k = d.K - 128 * (d.KT - 1);
 
-  // A: piece i = s*MT + rt is row 16rt + tid/16, elements 8*(tid%16) of step jb+s
-  // (a wave pass covers 4 whole rows; each lane quad holds one 32-element block).
-  const __amdgpu_buffer_rsrc_t ar = a_window(p, d.K, 0).at(0);
-  const uint32_t aoff = (uint32_t)(((tid >> 4) * p.lda + 8 * (tid & 15)) * 2);
-  const uint32_t arow16 = (uint32_t)(16 * p.lda * 2);
   // Every load is issued unconditionally, before any of them is used: steps past
   // this split's range repeat its last step (cache hits, never used). A guard
   // per load would let the compiler pair each load with its use and wait for it.
-  uint32_t w[kSpMaxSteps * MT][4];
+  // Fused: piece i = s*MT + rt is row 16rt + tid/16, elements 8*(tid%16) of step
+  // jb+s (a wave pass covers 4 whole rows; each lane quad holds one 32-element
+  // block). Pre-quantised: lane l's operand of row tile rt at step jb+s is row
+  // 16rt + l%16, 32-element chunk l/16: 16 code bytes and one scale byte.
+  uint32_t w[PREQ ? 1 : kSpMaxSteps * MT][4];
+  uint4 aop[PREQ ? kSpMaxSteps * MT : 1];
+  uint32_t asb[PREQ ? kSpMaxSteps * MT : 1];
+  if constexpr (!PREQ) {
+    const __amdgpu_buffer_rsrc_t ar = a_window(p, d.K, 0).at(0);
+    const uint32_t aoff = (uint32_t)(((tid >> 4) * p.lda + 8 * (tid & 15)) * 2);
+    const uint32_t arow16 = (uint32_t)(16 * p.lda * 2);
 #pragma unroll
-  for (int i = 0; i < kSpMaxSteps * MT; ++i) {
-    const int s = min(i / MT, ns - 1);
-    to_words(bload16(ar, aoff + (uint32_t)(i % MT) * arow16, (uint32_t)(jb + s) * 256), w[i]);
+    for (int i = 0; i < kSpMaxSteps * MT; ++i) {
+      const int s = min(i / MT, ns - 1);
+      to_words(bload16(ar, aoff + (uint32_t)(i % MT) * arow16, (uint32_t)(jb + s) * 256), w[i]);
+    }
+  } else {
+    const __amdgpu_buffer_rsrc_t qr = row_window(p.Aq, p.ldaq, d.K / 2, p.M, 0);
+    const __amdgpu_buffer_rsrc_t sr = row_window(p.As, p.ldas, d.K / 32, p.M, 0);
+    const int row = l & 15, ch = l >> 4;
+#pragma unroll
+    for (int i = 0; i < kSpMaxSteps * MT; ++i) {
+      const int s = min(i / MT, ns - 1), rt = i % MT, j = jb + s;
+      const int r = 16 * rt + row;
+      aop[i] = bload16(qr, (uint32_t)(r * p.ldaq + 16 * ch), (uint32_t)j * 64);
+      asb[i] = bload1(sr, (uint32_t)(r * p.ldas + ch), (uint32_t)j * 4);
+      if (j == d.KT - 1 && 32 * ch >= tail_k) {  // K tail: not A (and not a scale that could be NaN)
+        aop[i] = make_uint4(0u, 0u, 0u, 0u);
+        asb[i] = mx::kScaleOne;
+      }
+    }
   }
 
   // B of column group cg (half of packed 32-column tile cg/2): as in the skinny
@@ -322,20 +358,22 @@ __global__ __launch_bounds__(kSpT) void gemm_splitk_kernel(Operand p, Dims d, Sp
   }
 
   // Quantise A into the operand layout of the 16x16x128 instruction.
-  const int chunk = (tid & 15) >> 2, sub = tid & 3;
-  const int wslot = slot16(tid >> 4, chunk);
+  if constexpr (!PREQ) {
+    const int chunk = (tid & 15) >> 2, sub = tid & 3;
+    const int wslot = slot16(tid >> 4, chunk);
 #pragma unroll
-  for (int i = 0; i < kSpMaxSteps * MT; ++i) {
-    if (i < ns * MT) {
-      const int s = i / MT, rt = i % MT;
-      if (jb + s == d.KT - 1 && tail_k < 128 && 8 * (tid & 15) >= tail_k) w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
-      uint32_t sb;
-      const uint32_t code = mx::quant8_quad(w[i], sb);
-      sAq[s][rt][wslot * 4 + sub] = code;
-      sAs[s][rt][wslot] = (uint8_t)sb;  // the quad's four lanes store the same byte
+    for (int i = 0; i < kSpMaxSteps * MT; ++i) {
+      if (i < ns * MT) {
+        const int s = i / MT, rt = i % MT;
+        if (jb + s == d.KT - 1 && tail_k < 128 && 8 * (tid & 15) >= tail_k) w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
+        uint32_t sb;
+        const uint32_t code = mx::quant8_quad(w[i], sb);
+        sAq[s][rt][wslot * 4 + sub] = code;
+        sAs[s][rt][wslot] = (uint8_t)sb;  // the quad's four lanes store the same byte
+      }
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   mx::v4f acc[MT];
 #pragma unroll
@@ -347,8 +385,12 @@ __global__ __launch_bounds__(kSpT) void gemm_splitk_kernel(Operand p, Dims d, Sp
       const int bsh = 8 * ((2 * (jb + s) + (l >> 5)) & 3);
 #pragma unroll
       for (int rt = 0; rt < MT; ++rt) {
-        const uint4 a = *reinterpret_cast<const uint4*>(&sAq[s][rt][aslot * 4]);
-        acc[rt] = mx::mfma_fp4(a, bq[s], acc[rt], sAs[s][rt][aslot], bs[s] >> bsh);
+        if constexpr (PREQ) {
+          acc[rt] = mx::mfma_fp4(aop[s * MT + rt], bq[s], acc[rt], asb[s * MT + rt], bs[s] >> bsh);
+        } else {
+          const uint4 a = *reinterpret_cast<const uint4*>(&sAq[s][rt][aslot * 4]);
+          acc[rt] = mx::mfma_fp4(a, bq[s], acc[rt], sAs[s][rt][aslot], bs[s] >> bsh);
+        }
       }
     }
   }
@@ -456,6 +498,11 @@ struct TiledSmem {
   uint32_t cst[kTWaves][32 * kCPitch];  // per-wave C staging, 32 rows x 64 bf16
 };
 
+// PREQ: A arrives pre-quantised (gemm_a4w4). Thread tid then loads the 16 code
+// bytes of row tid/4, 32-element chunk tid%4 of each K step (and the first 128
+// threads their row's 4 scale bytes) and stores them into the same LDS operand
+// layout; everything else is shared with the fused path.
+template <bool PREQ>
 __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int mt, int nt, TiledSmem& sm) {
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
@@ -489,12 +536,48 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   const int sdw = qks * 64 + (chunk & 1) * 32 + (tid >> 4);
   const int tail_k = d.K - 128 * (d.KT - 1);
 
-  uint32_t raw[4][4];
+  uint32_t raw[PREQ ? 1 : 4][4];
+  // Pre-quantised A: row qr = tid/4, chunk qc = tid%4 of the step; in the operand
+  // layout that is 64-k half qc/2, 32-row tile qr/32, unit lane (qc%2)*32 + qr%32.
+  const int qr = tid >> 2, qc = tid & 3;
+  const __amdgpu_buffer_rsrc_t aqr = row_window(p.Aq, p.ldaq, d.K / 2, p.M, m0);
+  const __amdgpu_buffer_rsrc_t asr = row_window(p.As, p.ldas, d.K / 32, p.M, m0);
+  const int qslot = slot32((qc & 1) * 32 + (qr & 31), qc >> 1) * 4;
+  uint4 qraw = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t qsc = 0;  // row tid's 4 scale bytes of the step (threads < 128)
   auto load_a = [&](int j) {
+    if constexpr (!PREQ) {
 #pragma unroll
-    for (int h = 0; h < 4; ++h) to_words(bload16(ar[h], aoff0, (uint32_t)j * 256), raw[h]);
+      for (int h = 0; h < 4; ++h) to_words(bload16(ar[h], aoff0, (uint32_t)j * 256), raw[h]);
+    } else {
+      qraw = bload16(aqr, (uint32_t)(qr * p.ldaq + 16 * qc), (uint32_t)j * 64);
+      if (wave < 2) {  // rows 0..127: one per thread of waves 0 and 1
+        const uint32_t so = (uint32_t)(tid * p.ldas);
+        qsc = bload1(asr, so, (uint32_t)j * 4) | bload1(asr, so + 1, (uint32_t)j * 4) << 8 |
+              bload1(asr, so + 2, (uint32_t)j * 4) << 16 | bload1(asr, so + 3, (uint32_t)j * 4) << 24;
+      }
+    }
+  };
+  // Pre-quantised: store the step's codes and scale bytes into LDS buffer `buf`
+  // (K tail chunks zeroed).
+  auto store_preq = [&](int j, int buf) {
+    if (j == d.KT - 1 && 32 * qc >= tail_k) qraw = make_uint4(0u, 0u, 0u, 0u);  // K tail: not A
+    *reinterpret_cast<uint4*>(&sm.a[buf][qc >> 1][qr >> 5][qslot]) = qraw;
+    if (wave < 2) {
+      uint8_t* const sc = reinterpret_cast<uint8_t*>(&sm.as[buf][0][0]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {  // chunk c: half c/2, unit lane (c%2)*32 + row%32, byte = 32-row tile
+        const bool tail = j == d.KT - 1 && 32 * c >= tail_k;  // not A: neutral scale, never a NaN byte
+        sc[(((c >> 1) * 64 + (c & 1) * 32 + (tid & 31)) << 2) + (tid >> 5)] =
+            tail ? (uint8_t)mx::kScaleOne : (uint8_t)(qsc >> (8 * c));
+      }
+    }
   };
   auto quant_store = [&](int j, int buf) {
+    if constexpr (PREQ) {
+      store_preq(j, buf);
+      return;
+    }
     if (j == d.KT - 1 && tail_k < 128 && 8 * (tid & 15) >= tail_k) {  // K tail: not A
 #pragma unroll
       for (int h = 0; h < 4; ++h) raw[h][0] = raw[h][1] = raw[h][2] = raw[h][3] = 0u;
@@ -573,6 +656,10 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   };
   // Quantise the raw bf16 A(j+1) into LDS buffer (j+1)&1 (steady state: no K tail).
   auto quant_next = [&](int j) {
+    if constexpr (PREQ) {
+      store_preq(j + 1, (j + 1) & 1);
+      return;
+    }
     uint32_t* const sa_base = &sm.a[(j + 1) & 1][0][0][0];
     uint32_t sw = 0;
 #pragma unroll
@@ -688,10 +775,11 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   }
 }
 
+template <bool PREQ>
 __global__ __launch_bounds__(kTThreads) void gemm_tiled_kernel(Operand p, Dims d, int ntiles_n) {
   __shared__ __align__(16) TiledSmem sm;
   const int v = xcd_remap(blockIdx.x, gridDim.x);
-  tiled_tile(p, d, v / ntiles_n, v % ntiles_n, sm);
+  tiled_tile<PREQ>(p, d, v / ntiles_n, v % ntiles_n, sm);
 }
 
 struct GroupedArgs {
@@ -707,7 +795,7 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, 
   while (g + 1 < a.G && a.tile_start[g + 1] <= v) ++g;
   const int local = v - a.tile_start[g];
   __shared__ __align__(16) TiledSmem sm;
-  tiled_tile(a.g[g], d, local / a.ntiles_n, local % a.ntiles_n, sm);
+  tiled_tile<false>(a.g[g], d, local / a.ntiles_n, local % a.ntiles_n, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -729,6 +817,16 @@ Operand make_operand(const void* A, int64_t lda, const void* Bp, void* C, int64_
   o.C = (uint16_t*)C;
   o.ldc = ldc;
   o.M = (int)M;
+  return o;
+}
+
+Operand make_operand_q(const void* Aq, int64_t ldaq, const void* As, int64_t ldas, const void* Bp, void* C, int64_t ldc,
+                       int64_t M, int64_t N, int64_t K) {
+  Operand o = make_operand(nullptr, 0, Bp, C, ldc, M, N, K);
+  o.Aq = (const uint8_t*)Aq;
+  o.ldaq = ldaq;
+  o.As = (const uint8_t*)As;
+  o.ldas = ldas;
   return o;
 }
 
@@ -816,14 +914,25 @@ SplitGeom split_geom(int64_t M, int64_t N, int64_t K) {
   return g;
 }
 
-hipError_t launch_splitk(const Operand& o, const Dims& d, const SplitGeom& g, void* ws, hipStream_t st) {
+hipError_t launch_splitk(const Operand& o, const Dims& d, const SplitGeom& g, void* ws, bool preq, hipStream_t st) {
   Operand op = o;
   Dims dd = d;
   SplitArgs sa{};
   sa.part = (uint32_t*)ws;
   sa.S = g.S;
   void* args[] = {&op, &dd, &sa};
-  return hipLaunchKernel((const void*)gemm_splitk_kernel<1>, dim3((unsigned)(g.T * g.S)), dim3(kSpT), args, 0, st);
+  return hipLaunchKernel(preq ? (const void*)gemm_splitk_kernel<1, true> : (const void*)gemm_splitk_kernel<1, false>,
+                         dim3((unsigned)(g.T * g.S)), dim3(kSpT), args, 0, st);
+}
+
+hipError_t launch_tiled(const Operand& o, const Dims& d, int64_t M, int64_t N, bool preq, hipStream_t st) {
+  Operand op = o;
+  Dims dd = d;
+  int ntn = (int)mxh::cdiv(N, kTBN);
+  void* args[] = {&op, &dd, &ntn};
+  const int64_t tiles = mxh::cdiv(M, kTBM) * ntn;
+  return hipLaunchKernel(preq ? (const void*)gemm_tiled_kernel<true> : (const void*)gemm_tiled_kernel<false>,
+                         dim3((unsigned)tiles), dim3(kTThreads), args, 0, st);
 }
 
 hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, int64_t K, hipStream_t st) {
@@ -841,12 +950,7 @@ hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, in
       default: return launch_skinny<16, 4, 2>(o, d, M, st);
     }
   }
-  Operand op = o;
-  Dims dd = d;
-  int ntn = (int)mxh::cdiv(N, kTBN);
-  void* args[] = {&op, &dd, &ntn};
-  const int64_t tiles = mxh::cdiv(M, kTBM) * ntn;
-  return hipLaunchKernel((const void*)gemm_tiled_kernel, dim3((unsigned)tiles), dim3(kTThreads), args, 0, st);
+  return launch_tiled(o, d, M, N, false, st);
 }
 
 }  // namespace
@@ -870,9 +974,32 @@ extern "C" int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void*
       if (!workspace || workspace_bytes < g.total()) return MXFP4_ERR_WORKSPACE;
       if (!mxh::aligned(workspace, 256)) return MXFP4_ERR_ALIGN;
     }
-    return mxh::launch_status(launch_splitk(o, d, g, workspace, (hipStream_t)stream));
+    return mxh::launch_status(launch_splitk(o, d, g, workspace, false, (hipStream_t)stream));
   }
   return mxh::launch_status(launch_gemm(o, d, M, N, K, (hipStream_t)stream));
+}
+
+extern "C" int gemm_a4w4(const void* Aq, int64_t ldaq, const void* As, int64_t ldas, const void* Bp, void* C,
+                         int64_t ldc, int64_t M, int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  if (!Aq || !As || !Bp || !C) return MXFP4_ERR_NULL;
+  if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || M > mxh::kMaxDim || N > mxh::kMaxDim || K > mxh::kMaxDim)
+    return MXFP4_ERR_SHAPE;
+  if (ldaq < K / 2 || ldas < K / 32 || ldc < N) return MXFP4_ERR_SHAPE;
+  if (ldaq > (int64_t)1 << 24 || ldas > (int64_t)1 << 24) return MXFP4_ERR_SHAPE;  // 32-bit buffer offsets over 128 rows
+  if (!mxh::aligned(Aq, 16) || ldaq % 16 != 0 || !mxh::aligned(Bp, 16) || !mxh::aligned(C, 2)) return MXFP4_ERR_ALIGN;
+  if (mxh::cdiv(M, kTBM) * mxh::cdiv(N, kTBN) > INT32_MAX) return MXFP4_ERR_SHAPE;
+  const Operand o = make_operand_q(Aq, ldaq, As, ldas, Bp, C, ldc, M, N, K);
+  const Dims d = make_dims(N, K);
+  const SplitGeom g = split_geom(M, N, K);
+  if (g.ok) {
+    if (g.total() > 0) {
+      if (!workspace || workspace_bytes < g.total()) return MXFP4_ERR_WORKSPACE;
+      if (!mxh::aligned(workspace, 256)) return MXFP4_ERR_ALIGN;
+    }
+    return mxh::launch_status(launch_splitk(o, d, g, workspace, true, (hipStream_t)stream));
+  }
+  return mxh::launch_status(launch_tiled(o, d, M, N, true, (hipStream_t)stream));
 }
 
 extern "C" size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K) {

@@ -21,7 +21,7 @@ MXFP4_MAX_GROUPS = 32
 STATUS = {0: "MXFP4_OK", 1: "MXFP4_ERR_NULL", 2: "MXFP4_ERR_SHAPE", 3: "MXFP4_ERR_ALIGN", 4: "MXFP4_ERR_WORKSPACE",
           5: "MXFP4_ERR_TOO_MANY_GROUPS", 6: "MXFP4_ERR_HIP", 7: "MXFP4_ERR_BUFFER"}
 EXPORTED = ["mxfp4_status_str", "mxfp4_quant", "mxfp4_pack_B_bytes", "mxfp4_pack_B", "gemm_a4w4_workspace_bytes",
-            "gemm_a4w4_fused", "grouped_gemm_a4w4_workspace_bytes", "grouped_gemm_a4w4"]
+            "gemm_a4w4_fused", "gemm_a4w4", "grouped_gemm_a4w4_workspace_bytes", "grouped_gemm_a4w4"]
 
 
 class Mxfp4Error(RuntimeError):
@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_a4w4_workspace_bytes.argtypes, L.gemm_a4w4_workspace_bytes.restype = [i64, i64, i64], sz
         L.gemm_a4w4_fused.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp]
         L.gemm_a4w4_fused.restype = i32
+        L.gemm_a4w4.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp]
+        L.gemm_a4w4.restype = i32
         L.grouped_gemm_a4w4_workspace_bytes.argtypes = [ctypes.POINTER(Group), i32, i64, i64]
         L.grouped_gemm_a4w4_workspace_bytes.restype = sz
         L.grouped_gemm_a4w4.argtypes = [ctypes.POINTER(Group), i32, i64, i64, vp, sz, vp]
@@ -95,12 +97,19 @@ def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
     return buf
 
 
-def quant(x: torch.Tensor):
-    """bf16 [M, K] -> (q uint8 [M, K/2], s uint8 [M, K/32])."""
+def quant(x: torch.Tensor, out=None):
+    """bf16 [M, K] -> (q uint8 [M, K/2], s uint8 [M, K/32]); `out` = (q, s) reuses given buffers."""
     _require(x, torch.bfloat16, "x")
     M, K = x.shape
-    q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
-    s = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    if out is None:
+        q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        s = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    else:
+        q, s = out
+        _require(q, torch.uint8, "q")
+        _require(s, torch.uint8, "s")
+        if q.shape != (M, K // 2) or s.shape != (M, K // 32):
+            raise ValueError("out buffers must be [M, K/2] and [M, K/32]")
     _check(lib().mxfp4_quant(x.data_ptr(), x.stride(0), q.data_ptr(), q.stride(0), s.data_ptr(), s.stride(0), M, K,
                              _stream(x)), "mxfp4_quant")
     return q, s
@@ -138,6 +147,29 @@ def gemm(a: torch.Tensor, bp: torch.Tensor, N: int, out: torch.Tensor | None = N
     _check(lib().gemm_a4w4_fused(a.data_ptr(), a.stride(0), bp.data_ptr(), out.data_ptr(), out.stride(0), M, N, K,
                                  ws.data_ptr() if wsz else None, ws.numel() if wsz else 0, _stream(a)),
            "gemm_a4w4_fused")
+    return out
+
+
+def gemm_a4w4(aq: torch.Tensor, a_scale: torch.Tensor, bp: torch.Tensor, N: int,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """C[M, N] = A_q . B^T with A already quantised: aq fp4x2 [M, K/2], a_scale E8M0 [M, K/32] (uint8,
+    for example from quant()); bp from pack_B. The unfused comparator of gemm()."""
+    _require(aq, torch.uint8, "aq")
+    _require(a_scale, torch.uint8, "a_scale")
+    M, KH = aq.shape
+    K = 2 * KH
+    if a_scale.shape[0] != M or a_scale.shape[1] < K // 32:
+        raise ValueError("a_scale must be [M, >= K/32]")
+    if bp.numel() < pack_B_bytes(N, K):
+        raise ValueError("packed B is smaller than pack_B_bytes(N, K)")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=aq.device)
+    _require(out, torch.bfloat16, "out")
+    wsz = int(lib().gemm_a4w4_workspace_bytes(M, N, K))
+    ws = workspace(aq.device, wsz)
+    _check(lib().gemm_a4w4(aq.data_ptr(), aq.stride(0), a_scale.data_ptr(), a_scale.stride(0), bp.data_ptr(),
+                           out.data_ptr(), out.stride(0), M, N, K, ws.data_ptr() if wsz else None,
+                           ws.numel() if wsz else 0, _stream(aq)), "gemm_a4w4")
     return out
 
 

@@ -123,6 +123,23 @@ def test_gemm_validation(change, status):
     assert got == status
 
 
+OK_Q4 = dict(Aq=P, ldaq=3584, As=P, ldas=224, Bp=P, C=P, ldc=2112, M=16, N=2112, K=7168, ws=P, wsb=1 << 30)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(Aq=None), 1), (dict(As=None), 1), (dict(Bp=None), 1), (dict(C=None), 1),
+    (dict(M=0), 2), (dict(K=7000), 2), (dict(ldaq=3000), 2), (dict(ldas=200), 2), (dict(ldc=2000), 2),
+    (dict(ldaq=1 << 25), 2),
+    (dict(Aq=P + 8), 3), (dict(ldaq=3592), 3), (dict(Bp=P + 8), 3), (dict(C=P + 1), 3),
+    (dict(ws=None), 4), (dict(wsb=1024), 4), (dict(ws=P + 16), 3),
+])
+def test_gemm_a4w4_validation(change, status):
+    a = dict(OK_Q4, **change)
+    got = ops.lib().gemm_a4w4(a["Aq"], a["ldaq"], a["As"], a["ldas"], a["Bp"], a["C"], a["ldc"], a["M"], a["N"],
+                              a["K"], a["ws"], a["wsb"], None)
+    assert got == status
+
+
 def test_grouped_validation():
     L = ops.lib()
     g = (ops.Group * 2)()

@@ -257,6 +257,61 @@ def test_gemm_repeat_identical_and_workspace_left_zero(M, N, K):
         assert (used == 0).all()
 
 
+# gemm_a4w4: the unfused comparator (A quantised by mxfp4_quant, then the GEMM on A_q).
+# Where it runs the same kernel and tiling as the fused call (M <= 16: split-K;
+# M > 64: tiled) its C must be bit-identical; elsewhere within the oracle's tolerance.
+A4W4_SHAPES = [(1, 16, 128), (4, 256, 512), (16, 2112, 7168), (3, 70, 352), (16, 130, 7232), (33, 64, 352),
+               (64, 130, 2048), (65, 130, 288), (127, 257, 1056), (300, 33, 32), (256, 512, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", A4W4_SHAPES)
+def test_gemm_a4w4_matches_fused_and_oracle(M, N, K):
+    say(f"gemm_a4w4 M={M} N={N} K={K}")
+    g = np.random.default_rng(M * 5 + N * 3 + K)
+    a = synth.f32_to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    b = synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    bq, bs = oracle.quant_mx(b)
+    at, bp = to_dev_bf16(a), packed_b(bq, bs)
+    aq, asc = ops.quant(at)
+    c4 = bits_of(ops.gemm_a4w4(aq, asc, bp, N))
+    cf = bits_of(ops.gemm(at, bp, N))
+    if M <= 16 or M > 64:
+        assert np.array_equal(c4, cf)
+    assert_in_tolerance(c4, oracle.gemm_ref(a, bq, bs), f"a4w4 M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 2112, 7168), (5, 100, 352), (130, 200, 416)])
+def test_gemm_a4w4_strides_and_padding(M, N, K):
+    """Row strides with padding that holds garbage (codes 0x77, scale bytes 0xFF = E8M0 NaN) must be
+    ignored, including in a K tail; C's guard band stays untouched."""
+    say(f"gemm_a4w4 strided M={M} N={N} K={K}")
+    g = np.random.default_rng(13)
+    a = synth.f32_to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    b = synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    bq, bs = oracle.quant_mx(b)
+    rq, rs = oracle.quant_mx(a)
+    ldaq, ldas, ldc = K // 2 + 48, K // 32 + 5, N + 8
+    qbuf = np.full((M, ldaq), 0x77, np.uint8)
+    qbuf[:, :K // 2] = rq
+    sbuf = np.full((M, ldas), 0xFF, np.uint8)
+    sbuf[:, :K // 32] = rs
+    qd, sd = to_dev_u8(qbuf), to_dev_u8(sbuf)
+    cbuf = torch.full((M + 2, ldc), 1234.0, dtype=torch.bfloat16, device="cuda")
+    cview = cbuf[1:M + 1]
+    bp = packed_b(bq, bs)
+    wsz = ops.lib().gemm_a4w4_workspace_bytes(M, N, K)
+    ws = ops.workspace(qd.device, wsz)
+    rc = ops.lib().gemm_a4w4(qd.data_ptr(), ldaq, sd.data_ptr(), ldas, bp.data_ptr(), cview.data_ptr(), ldc, M, N, K,
+                             ws.data_ptr() if wsz else None, ws.numel() if wsz else 0,
+                             torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    cb = bits_of(cbuf)
+    assert_in_tolerance(cb[1:M + 1, :N], oracle.gemm_ref(a, bq, bs), "a4w4 strided")
+    guard = bits_of(torch.tensor([1234.0], dtype=torch.bfloat16))[0]
+    assert (cb[0] == guard).all() and (cb[M + 1] == guard).all() and (cb[:, N:] == guard).all()
+
+
 def test_grouped_ragged_small():
     say("grouped ragged small")
     g = np.random.default_rng(9)
