@@ -498,12 +498,80 @@ struct TiledSmem {
   uint32_t cst[kTWaves][32 * kCPitch];  // per-wave C staging, 32 rows x 64 bf16
 };
 
+// One stage of the per-wave B ring: the wave's 2 packed tiles x 2 units of a K
+// step (4 KB, unit (t, ks) at (2t + ks) * 1024, lane l's 16 bytes at l * 16) and
+// the tiles' scale dwords (t * 256 + l * 4). Three stages, filled by
+// buffer-to-LDS loads two steps ahead; each wave reads only its own part, so no
+// barrier guards it. The ring is read with ds instructions written as inline
+// assembly and explicit waits: the buffer loads into a stage are waited for by
+// count (vmcnt) and the reads by an lgkmcnt wait bound to their results. The
+// compiler sees neither, so it adds no wait of its own for the ring (which
+// would drain every outstanding ring load, the next step's included).
+constexpr int kRingWave = 4096 + 512;
+constexpr int kRingStage = kTWaves * kRingWave;
+constexpr int kRingBytes = 3 * kRingStage;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t lds_addr(const void* ptr) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)ptr;
+}
+template <int OFF>
+__device__ __forceinline__ u32x4v ring_read16(uint32_t addr) {
+  u32x4v r;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t ring_read4(uint32_t addr) {
+  uint32_t r;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(addr), "i"(OFF) : "memory");
+  return r;
+}
+// Wait until at most N vector-memory operations of this wave are outstanding.
+// The builtin (rather than assembly) lets the compiler's own wait analysis
+// account for it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");
+  // s_waitcnt fields: vmcnt[3:0] and [15:14], expcnt[6:4], lgkmcnt[11:8]; the
+  // latter two at their maximum (no wait).
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Workgroup barrier for the LDS written with ds instructions (the A tiles): wait
+// for this wave's LDS operations, then meet. Unlike __syncthreads() it does not
+// wait for outstanding buffer loads, which would drain the B ring.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// The A tiles' LDS stores, also written as inline assembly: the compiler waits
+// for every outstanding buffer-to-LDS load before an LDS store it emits itself.
+// The lds_barrier that follows them waits for their completion.
+template <int OFF>
+__device__ __forceinline__ void lds_st8(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b8 %0, %1 offset:%2" ::"v"(addr), "v"(v), "i"(OFF) : "memory");
+}
+__device__ __forceinline__ void lds_st32(uint32_t addr, uint32_t v) {
+  asm volatile("ds_write_b32 %0, %1" ::"v"(addr), "v"(v) : "memory");
+}
+// Two dwords at addr + 256 * O0 and addr + 256 * O1.
+template <int O0, int O1>
+__device__ __forceinline__ void lds_st2x32_st64(uint32_t addr, uint32_t v0, uint32_t v1) {
+  asm volatile("ds_write2st64_b32 %0, %1, %2 offset0:%3 offset1:%4" ::"v"(addr), "v"(v0), "v"(v1), "i"(O0),
+               "i"(O1)
+               : "memory");
+}
+__device__ __forceinline__ void lds_st128(uint32_t addr, const uint4& v) {
+  asm volatile("ds_write_b128 %0, %1" ::"v"(addr), "v"(__builtin_bit_cast(u32x4v, v)) : "memory");
+}
+
 // PREQ: A arrives pre-quantised (gemm_a4w4). Thread tid then loads the 16 code
-// bytes of row tid/4, 32-element chunk tid%4 of each K step (and the first 128
-// threads their row's 4 scale bytes) and stores them into the same LDS operand
-// layout; everything else is shared with the fused path.
+// bytes of row tid/4, 32-element chunk tid%4 of each K step (and row tid%128's
+// 4 scale bytes) and stores them into the same LDS operand layout; everything
+// else is shared with the fused path.
 template <bool PREQ>
-__device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int mt, int nt, TiledSmem& sm) {
+__device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int mt, int nt, TiledSmem& sm,
+                                           uint8_t* ring) {
   const int tid = threadIdx.x, l = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar addressing
   const int m0 = mt * kTBM;
@@ -536,62 +604,104 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   const int sdw = qks * 64 + (chunk & 1) * 32 + (tid >> 4);
   const int tail_k = d.K - 128 * (d.KT - 1);
 
-  uint32_t raw[PREQ ? 1 : 4][4];
+  // A registers of one K step in flight: the bf16 pieces, or the pre-quantised
+  // codes and (waves 0 and 1) the row's scale bytes. Two sets alternate: the A of
+  // step j+1 is quantised at step j while the A of step j+2 is arriving.
+  struct AStage {
+    uint32_t raw[PREQ ? 1 : 4][4];
+    uint4 q;
+    uint32_t qb[4];
+  };
+  AStage s0, s1;
   // Pre-quantised A: row qr = tid/4, chunk qc = tid%4 of the step; in the operand
   // layout that is 64-k half qc/2, 32-row tile qr/32, unit lane (qc%2)*32 + qr%32.
   const int qr = tid >> 2, qc = tid & 3;
   const __amdgpu_buffer_rsrc_t aqr = row_window(p.Aq, p.ldaq, d.K / 2, p.M, m0);
   const __amdgpu_buffer_rsrc_t asr = row_window(p.As, p.ldas, d.K / 32, p.M, m0);
   const int qslot = slot32((qc & 1) * 32 + (qr & 31), qc >> 1) * 4;
-  uint4 qraw = make_uint4(0u, 0u, 0u, 0u);
-  uint32_t qsc = 0;  // row tid's 4 scale bytes of the step (threads < 128)
-  auto load_a = [&](int j) {
+  // Step j's A (clamped to the last step: the loads run ahead of K and must stay
+  // inside A, whose K offset is not range-checked; the extra copies go unused).
+  auto load_a_piece = [&](int j, AStage& S, int h) {
+    const uint32_t jo = (uint32_t)(j < d.KT ? j : d.KT - 1);
+    to_words(bload16(ar[h], aoff0, jo * 256), S.raw[h]);
+  };
+  auto load_a = [&](int j, AStage& S) {
+    const uint32_t jo = (uint32_t)(j < d.KT ? j : d.KT - 1);
     if constexpr (!PREQ) {
 #pragma unroll
-      for (int h = 0; h < 4; ++h) to_words(bload16(ar[h], aoff0, (uint32_t)j * 256), raw[h]);
+      for (int h = 0; h < 4; ++h) load_a_piece(j, S, h);
     } else {
-      qraw = bload16(aqr, (uint32_t)(qr * p.ldaq + 16 * qc), (uint32_t)j * 64);
-      if (wave < 2) {  // rows 0..127: one per thread of waves 0 and 1
-        const uint32_t so = (uint32_t)(tid * p.ldas);
-        qsc = bload1(asr, so, (uint32_t)j * 4) | bload1(asr, so + 1, (uint32_t)j * 4) << 8 |
-              bload1(asr, so + 2, (uint32_t)j * 4) << 16 | bload1(asr, so + 3, (uint32_t)j * 4) << 24;
-      }
+      S.q = bload16(aqr, (uint32_t)(qr * p.ldaq + 16 * qc), jo * 64);
+      // Row tid%128's 4 scale bytes: every wave loads (and later stores) them,
+      // waves 2..7 repeating 0 and 1, so that no branch splits the step.
+      const uint32_t so = (uint32_t)((tid & 127) * p.ldas);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) S.qb[c] = bload1(asr, so + c, jo * 4);
     }
   };
+  // LDS byte addresses of this thread's A stores in buffer 0 (buffer 1 follows).
+  constexpr uint32_t kABuf = sizeof(sm.a[0]), kSBuf = sizeof(sm.as[0]);
+  const uint32_t qa = lds_addr(&sm.a[0][0][0][0]) + (uint32_t)wbase * 4;
+  const uint32_t qs = lds_addr(&sm.as[0][0][0]) + (uint32_t)sdw * 4;
+  const uint32_t pa = lds_addr(&sm.a[0][qc >> 1][qr >> 5][qslot]);
+  const uint32_t ps = lds_addr(&sm.as[0][0][0]) + (uint32_t)((tid & 31) * 4 + ((tid >> 5) & 3));
   // Pre-quantised: store the step's codes and scale bytes into LDS buffer `buf`
-  // (K tail chunks zeroed).
-  auto store_preq = [&](int j, int buf) {
-    if (j == d.KT - 1 && 32 * qc >= tail_k) qraw = make_uint4(0u, 0u, 0u, 0u);  // K tail: not A
-    *reinterpret_cast<uint4*>(&sm.a[buf][qc >> 1][qr >> 5][qslot]) = qraw;
-    if (wave < 2) {
-      uint8_t* const sc = reinterpret_cast<uint8_t*>(&sm.as[buf][0][0]);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {  // chunk c: half c/2, unit lane (c%2)*32 + row%32, byte = 32-row tile
-        const bool tail = j == d.KT - 1 && 32 * c >= tail_k;  // not A: neutral scale, never a NaN byte
-        sc[(((c >> 1) * 64 + (c & 1) * 32 + (tid & 31)) << 2) + (tid >> 5)] =
-            tail ? (uint8_t)mx::kScaleOne : (uint8_t)(qsc >> (8 * c));
-      }
-    }
+  // (K tail chunks zeroed). Scale byte of chunk c: half c/2, unit lane
+  // (c%2)*32 + row%32, byte = 32-row tile, i.e. 128c bytes past chunk 0's.
+  auto store_preq = [&](int j, int buf, AStage& S) {
+    const bool tl = j == d.KT - 1 && 32 * qc >= tail_k;  // K tail: not A
+    lds_st128(pa + buf * kABuf, tl ? make_uint4(0u, 0u, 0u, 0u) : S.q);
+    const bool last = j == d.KT - 1;  // K tail chunks: neutral scale, never a NaN byte
+    const uint32_t sb = ps + buf * kSBuf;
+    lds_st8<0>(sb, S.qb[0]);
+    lds_st8<128>(sb, last && 32 >= tail_k ? mx::kScaleOne : S.qb[1]);
+    lds_st8<256>(sb, last && 64 >= tail_k ? mx::kScaleOne : S.qb[2]);
+    lds_st8<384>(sb, last && 96 >= tail_k ? mx::kScaleOne : S.qb[3]);
   };
-  auto quant_store = [&](int j, int buf) {
-    if constexpr (PREQ) {
-      store_preq(j, buf);
-      return;
-    }
-    if (j == d.KT - 1 && tail_k < 128 && 8 * (tid & 15) >= tail_k) {  // K tail: not A
-#pragma unroll
-      for (int h = 0; h < 4; ++h) raw[h][0] = raw[h][1] = raw[h][2] = raw[h][3] = 0u;
-    }
-    uint32_t* const sa_base = &sm.a[buf][0][0][0];
-    uint32_t sw = 0;
+  // Quantise the bf16 A of step j held in S into LDS buffer j&1. The lanes of a
+  // quad hold the same four scales and all store that dword. A 32-element block
+  // past K (last step only) is stored as zero codes with the neutral scale,
+  // whatever the registers held. after_piece(h) runs once piece h's registers
+  // are consumed (the caller refills them there).
+  const bool ktail_lane = 8 * (tid & 15) >= tail_k;
+  auto quant_write = [&](int j, AStage& S, auto&& after_piece) {
+    uint32_t c[4], sw = 0;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
       uint32_t sb;
-      const uint32_t code = mx::quant8_quad(raw[h], sb);
-      sa_base[wbase + h * 256] = code;
+      c[h] = mx::quant8_quad(S.raw[h], sb);
       sw |= sb << (8 * h);
+      __builtin_amdgcn_sched_barrier(0);
+      after_piece(h);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (sub == 0) (&sm.as[buf][0][0])[sdw] = sw;  // the quad's lanes hold the same scales
+    if (j == d.KT - 1 && ktail_lane) {  // selects, not a branch
+#pragma unroll
+      for (int h = 0; h < 4; ++h) c[h] = 0u;
+      sw = mx::kScaleOne * 0x01010101u;
+    }
+    const int buf = j & 1;
+    const uint32_t aa = qa + buf * kABuf;  // piece h at + 1024h bytes
+    lds_st2x32_st64<0, 4>(aa, c[0], c[1]);
+    lds_st2x32_st64<8, 12>(aa, c[2], c[3]);
+    lds_st32(qs + buf * kSBuf, sw);
+  };
+  // Step j's A into LDS buffer j&1 (K tail included).
+  auto quant_store = [&](int j, AStage& S) {
+    if constexpr (PREQ)
+      store_preq(j, j & 1, S);
+    else
+      quant_write(j, S, [](int) {});
+  };
+  // Step jq's A from S into LDS buffer jq&1, and the A of step jl requested into
+  // S: piece by piece for bf16 A, so that the loads spread over the VALU work.
+  auto quant_then_load = [&](int jq, int jl, AStage& S) {
+    if constexpr (PREQ) {
+      store_preq(jq, jq & 1, S);
+      load_a(jl, S);
+    } else {
+      quant_write(jq, S, [&](int h) { load_a_piece(jl, S, h); });
+    }
   };
   __amdgpu_buffer_rsrc_t brs[2], bss[2];  // per packed tile: code units, scale dwords
 #pragma unroll
@@ -601,137 +711,160 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
     brs[t] = make_rsrc(p.Bunit + (int64_t)t32 * d.KU * 1024, ok ? (int64_t)d.KU * 1024 : 0);
     bss[t] = make_rsrc(p.Bscale + (int64_t)t32 * d.KG * 64, ok ? (int64_t)d.KG * 256 : 0);
   }
-  // B of step j: units 2j (ks 0) and 2j+1 (ks 1) of this wave's 2 packed tiles,
-  // lane l's 16 bytes of each, and the tiles' scale dwords.
-  // `full`: both units exist (every step but the last), so no branch splits the
-  // load sequence.
-  auto load_b = [&](auto full, int j, uint4 (&b)[2][2], uint32_t (&sc)[2]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      b[0][t] = bload16(brs[t], (uint32_t)l * 16, (uint32_t)j * 2048);
-      sc[t] = bload4(bss[t], (uint32_t)l * 4, (uint32_t)(j >> 1) * 256);
-    }
-    if (decltype(full)::value || 2 * j + 1 < d.KU) {  // the last step of an odd K/64 has one unit: never read past it
-#pragma unroll
-      for (int t = 0; t < 2; ++t) b[1][t] = bload16(brs[t], (uint32_t)l * 16 + 1024, (uint32_t)j * 2048);
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t) b[1][t] = make_uint4(0u, 0u, 0u, 0u);
+  // B of step jj into ring stage st: units 2jj (ks 0) and 2jj+1 (ks 1) of this
+  // wave's 2 packed tiles, and the tiles' scale dwords. The unit sits in the
+  // per-lane offset, so a unit past K (odd K/64) or a tile past N reads as zeros
+  // by the range check alone. Six buffer loads.
+  // Load p (< 6) of those: code unit (t, ks) = (p/2, p%2) for p < 4, else the
+  // scale dwords of tile p-4.
+  auto dma_part = [&](int jj, int st, int p) {
+    uint8_t* const base = ring + st * kRingStage + wave * kRingWave;
+    if (p < 4) {
+      const int t = p >> 1, ks = p & 1;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(brs[t], (lds_void*)(base + (2 * t + ks) * 1024), 16,
+                                               (int)((uint32_t)l * 16 + (uint32_t)(2 * jj + ks) * 1024), 0, 0, 0);
+    } else if (p < 6) {
+      const int t = p - 4;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(bss[t], (lds_void*)(base + 4096 + t * 256), 4,
+                                               (int)((uint32_t)l * 4 + (uint32_t)(jj >> 1) * 256), 0, 0, 0);
     }
   };
-  // Step j's 16 matrix instructions. The four A operands of the first 64-k half
-  // (and its scale dword) are read from LDS up front; the second half's reads
-  // are issued behind the first half's matrix instructions.
-  auto compute = [&](int j, const uint4 (&b)[2][2], const uint32_t (&sc)[2]) {
-    const int buf = j & 1;
-    uint4 a[2][4];
-    uint32_t sa[2];
-    auto read_half = [&](int ks) {
-      sa[ks] = sm.as[buf][ks][l];
-      const int sl = slot32(l, ks) * 4;
+  auto dma_b = [&](int jj, int st) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[ks][i] = *reinterpret_cast<const uint4*>(&sm.a[buf][ks][i][sl]);
-    };
-    auto mfma_half = [&](int ks) {
+    for (int p = 0; p < 6; ++p) dma_part(jj, st, p);
+  };
+  const uint32_t rlane = lds_addr(ring + wave * kRingWave) + (uint32_t)l * 16;
+  const uint32_t rlane_sc = lds_addr(ring + wave * kRingWave + 4096) + (uint32_t)l * 4;
+  // Step j's 16 matrix instructions on B from ring stage st (whose buffer loads
+  // the caller has waited for). B and the first 64-k half of A are read and
+  // waited for; the second half's A reads are issued before the first matrix
+  // instruction and land behind the first half's.
+  auto compute = [&](int j, int st, auto&& after_pair) {
+    const int buf = j & 1;
+    uint4 a0[4], a1[4];
+    const uint32_t so = (uint32_t)(st * kRingStage);
+    u32x4v b00 = ring_read16<0>(rlane + so), b01 = ring_read16<2048>(rlane + so);
+    u32x4v b10 = ring_read16<1024>(rlane + so), b11 = ring_read16<3072>(rlane + so);
+    uint32_t sc0 = ring_read4<0>(rlane_sc + so), sc1 = ring_read4<256>(rlane_sc + so);
+    const uint32_t sa0 = sm.as[buf][0][l];
+    const int sl0 = slot32(l, 0) * 4, sl1 = slot32(l, 1) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a0[i] = *reinterpret_cast<const uint4*>(&sm.a[buf][0][i][sl0]);
+    // Every LDS read so far has landed; binding the ring registers to this wait
+    // keeps each of their uses below it.
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(b00), "+v"(b01), "+v"(b10), "+v"(b11), "+v"(sc0), "+v"(sc1)
+                 :
+                 : "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t sa1 = sm.as[buf][1][l];
+    const uint4 b[2][2] = {{__builtin_bit_cast(uint4, b00), __builtin_bit_cast(uint4, b01)},
+                           {__builtin_bit_cast(uint4, b10), __builtin_bit_cast(uint4, b11)}};
+    const uint32_t sc[2] = {sc0, sc1};
+    auto mfma_pair = [&](int ks, int i, const uint4& av, uint32_t sa) {
       const int bsh = 8 * ((2 * j + ks) & 3);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const uint32_t sb = sc[t] >> bsh;
-          switch (i) {  // A scale byte = 32-row tile; folds once unrolled
-            case 0: acc[i][t] = mx::mfma32_fp4<0, 0>(a[ks][i], b[ks][t], acc[i][t], sa[ks], sb); break;
-            case 1: acc[i][t] = mx::mfma32_fp4<1, 0>(a[ks][i], b[ks][t], acc[i][t], sa[ks], sb); break;
-            case 2: acc[i][t] = mx::mfma32_fp4<2, 0>(a[ks][i], b[ks][t], acc[i][t], sa[ks], sb); break;
-            default: acc[i][t] = mx::mfma32_fp4<3, 0>(a[ks][i], b[ks][t], acc[i][t], sa[ks], sb); break;
-          }
+      for (int t = 0; t < 2; ++t) {
+        const uint32_t sb = sc[t] >> bsh;
+        switch (i) {  // A scale byte = 32-row tile; folds once unrolled
+          case 0: acc[i][t] = mx::mfma32_fp4<0, 0>(av, b[ks][t], acc[i][t], sa, sb); break;
+          case 1: acc[i][t] = mx::mfma32_fp4<1, 0>(av, b[ks][t], acc[i][t], sa, sb); break;
+          case 2: acc[i][t] = mx::mfma32_fp4<2, 0>(av, b[ks][t], acc[i][t], sa, sb); break;
+          default: acc[i][t] = mx::mfma32_fp4<3, 0>(av, b[ks][t], acc[i][t], sa, sb); break;
         }
       }
     };
-    read_half(0);
-    __builtin_amdgcn_sched_barrier(0);
-    read_half(1);
-    mfma_half(0);
-    mfma_half(1);
-  };
-  // Quantise the raw bf16 A(j+1) into LDS buffer (j+1)&1 (steady state: no K tail).
-  auto quant_next = [&](int j) {
-    if constexpr (PREQ) {
-      store_preq(j + 1, (j + 1) & 1);
-      return;
-    }
-    uint32_t* const sa_base = &sm.a[(j + 1) & 1][0][0][0];
-    uint32_t sw = 0;
+    // First 64-k half; the second half's A operand i is requested behind the
+    // first half's pair i, four pairs ahead of its use, in the registers that
+    // pair has finished with. after_pair(p) runs behind matrix pair p (< 8).
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      uint32_t sb;
-      const uint32_t code = mx::quant8_quad(raw[h], sb);
-      sa_base[wbase + h * 256] = code;
-      sw |= sb << (8 * h);
+    for (int i = 0; i < 4; ++i) {
+      mfma_pair(0, i, a0[i], sa0);
+      __builtin_amdgcn_sched_barrier(0);
+      a1[i] = *reinterpret_cast<const uint4*>(&sm.a[buf][1][i][sl1]);
+      after_pair(i);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (sub == 0) (&sm.as[(j + 1) & 1][0][0])[sdw] = sw;  // the quad's lanes hold the same scales
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      mfma_pair(1, i, a1[i], sa1);
+      __builtin_amdgcn_sched_barrier(0);
+      after_pair(4 + i);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
-  // Steady-state K step j (j + 2 < KT). B(j+1) is loaded into the other register
-  // set while step j computes; A(j+1) is quantised into the other LDS buffer and
-  // the bf16 A of step j+2 is requested. The two waves that share a SIMD (w and
-  // w+4) take the matrix and the quantisation phases in opposite orders, so that
-  // one wave's MFMAs run while the other wave's VALU quantisation runs.
-  uint4 bcur[2][2], bnxt[2][2];
-  uint32_t scur[2], snxt[2];
-  auto full_step = [&](auto mfma_first, int j) {
+  // Buffer loads a wave issues per A step: 4 (bf16 A), or 5 for pre-quantised A
+  // (codes and 4 scale bytes), and per B step 6. The waits below count the
+  // loads issued after a ring stage's.
+  constexpr int kLa = PREQ ? 5 : 4, kDb = 6;
+  // K step j. Every step requests B(j+2) into the ring stage read at step j-1,
+  // one load behind each of its first six matrix pairs, and the A of step j+3
+  // into the registers S, piece by piece as the quantisation of A(j+1) from S
+  // (into the other LDS buffer) empties them: spread over the step, the loads
+  // keep the address unit busy without stalling a wave on a full queue. Past
+  // the end of K the loads are clamped (A) or read zeros (B) and the quantised
+  // A lands in a buffer no step reads, so every step is the same code and the
+  // waits are fixed counts. The two waves that share a SIMD (w and w+4) take
+  // the matrix and the quantisation phases in opposite orders, so that one
+  // wave's MFMAs run while the other wave's VALU quantisation runs. Loads
+  // issued after B(j)'s, at B(j)'s use: matrix-first A(j+1), B(j+1), A(j+2);
+  // quantisation-first A(j+2), B(j+1), A(j+3).
+  auto step = [&](auto mfma_first, int j, int st, AStage& S) {
+    const int st2 = st == 0 ? 2 : st - 1;
+    const int jb = j + 2 < d.KT ? j + 2 : d.KT - 1;
+    auto dma_hook = [&](int p) { dma_part(jb, st2, p); };
     __builtin_amdgcn_sched_barrier(0);
-    load_b(std::true_type{}, j + 1, bnxt, snxt);
-    __syncthreads();  // A(j) is complete; every wave is past its reads of the other buffer
+    lds_barrier();  // A(j) is complete; every wave is past its reads of the other buffer
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(mfma_first)::value) {
-      compute(j, bcur, scur);
+      wait_vm<2 * kLa + kDb>();
+      compute(j, st, dma_hook);
       __builtin_amdgcn_sched_barrier(0);
-      quant_next(j);
-      __builtin_amdgcn_sched_barrier(0);
-      load_a(j + 2);
+      quant_then_load(j + 1, j + 3, S);
     } else {
-      quant_next(j);
+      quant_then_load(j + 1, j + 3, S);
       __builtin_amdgcn_sched_barrier(0);
-      load_a(j + 2);
-      __builtin_amdgcn_sched_barrier(0);
-      compute(j, bcur, scur);
+      wait_vm<2 * kLa + kDb>();
+      compute(j, st, dma_hook);
     }
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      bcur[0][t] = bnxt[0][t];
-      bcur[1][t] = bnxt[1][t];
-      scur[t] = snxt[t];
-    }
   };
-  // Generic step for the last two K steps (bounds tests, K tail).
-  auto tail_step = [&](int j) {
-    if (j + 1 < d.KT) load_b(std::false_type{}, j + 1, bnxt, snxt);
-    __syncthreads();
-    compute(j, bcur, scur);
-    if (j + 1 < d.KT) {
-      quant_store(j + 1, (j + 1) & 1);
-      if (j + 2 < d.KT) load_a(j + 2);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        bcur[0][t] = bnxt[0][t];
-        bcur[1][t] = bnxt[1][t];
-        scur[t] = snxt[t];
-      }
+  // Steps two at a time (the register sets alternate: even steps quantise from
+  // s1), then an odd last step. Step j reads ring stage j % 3.
+  auto run = [&](auto mfma_first) {
+    int j = 0, st = 0;
+    for (; j + 1 < d.KT; j += 2) {
+      step(mfma_first, j, st, s1);
+      st = st == 2 ? 0 : st + 1;
+      step(mfma_first, j + 1, st, s0);
+      st = st == 2 ? 0 : st + 1;
     }
+    if (j < d.KT) step(mfma_first, j, st, s1);
+    // No buffer-to-LDS load may still be in flight when the workgroup's LDS is
+    // released. Draining inside each branch also keeps the compiler's wait
+    // analysis from carrying one order's loads into the other order's loop (its
+    // structurised control flow links the two); the two waits differ in their
+    // LDS field so that they are not merged behind the join.
+    if constexpr (decltype(mfma_first)::value)
+      __builtin_amdgcn_s_waitcnt((7 << 4) | (0 << 8));  // vmcnt(0) lgkmcnt(0)
+    else
+      wait_vm<0>();
   };
 
-  load_a(0);
-  load_b(std::false_type{}, 0, bcur, scur);
-  quant_store(0, 0);
-  if (d.KT > 1) load_a(1);
-  int j = 0;
-  if (wave < kTWaves / 2) {  // uniform; each order is its own straight-line loop
-    for (; j + 2 < d.KT; ++j) full_step(std::true_type{}, j);
-  } else {
-    for (; j + 2 < d.KT; ++j) full_step(std::false_type{}, j);
-  }
-  for (; j < d.KT; ++j) tail_step(j);
+  // Prologue: B(0), B(1) and A(0..2) requested, A(0) quantised into buffer 0.
+  dma_b(0, 0);
+  dma_b(d.KT > 1 ? 1 : 0, 1);
+  load_a(0, s0);
+  quant_store(0, s0);
+  load_a(1, s1);
+  load_a(2, s0);
+  // Enter the loops with nothing in flight: the compiler's wait analysis would
+  // otherwise carry the prologue's loads into the loop and wait on them there.
+  wait_vm<0>();
+  if (wave < kTWaves / 2)  // uniform; each order is its own loop
+    run(std::true_type{});
+  else
+    run(std::false_type{});
 
   // Epilogue. acc[i][t] register r of lane l holds row 32i + 8(r/4) + 4(l/32) + r%4,
   // column 32t + l%32 of this wave's 128 x 64 block. Per 32-row tile i: lane pairs
@@ -778,8 +911,9 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
 template <bool PREQ>
 __global__ __launch_bounds__(kTThreads) void gemm_tiled_kernel(Operand p, Dims d, int ntiles_n) {
   __shared__ __align__(16) TiledSmem sm;
+  __shared__ __align__(16) uint8_t ring[kRingBytes];
   const int v = xcd_remap(blockIdx.x, gridDim.x);
-  tiled_tile<PREQ>(p, d, v / ntiles_n, v % ntiles_n, sm);
+  tiled_tile<PREQ>(p, d, v / ntiles_n, v % ntiles_n, sm, ring);
 }
 
 struct GroupedArgs {
@@ -795,7 +929,8 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, 
   while (g + 1 < a.G && a.tile_start[g + 1] <= v) ++g;
   const int local = v - a.tile_start[g];
   __shared__ __align__(16) TiledSmem sm;
-  tiled_tile<false>(a.g[g], d, local / a.ntiles_n, local % a.ntiles_n, sm);
+  __shared__ __align__(16) uint8_t ring[kRingBytes];
+  tiled_tile<false>(a.g[g], d, local / a.ntiles_n, local % a.ntiles_n, sm, ring);
 }
 
 // ---------------------------------------------------------------------------
