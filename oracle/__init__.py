@@ -24,3 +24,4 @@ from .mx import (  # noqa: F401
     quant_block_exact,
     gemm_exact_fraction,
 )
+from . import rmsnorm  # noqa: F401,E402  (RMSNorm followed by MXFP4 quantisation)
