@@ -47,7 +47,8 @@ typedef enum {
   MXFP4_ERR_WORKSPACE = 4,       /* workspace NULL or smaller than *_workspace_bytes()   */
   MXFP4_ERR_TOO_MANY_GROUPS = 5, /* G < 1 or G > MXFP4_MAX_GROUPS                        */
   MXFP4_ERR_HIP = 6,             /* the HIP runtime rejected a launch                    */
-  MXFP4_ERR_BUFFER = 7           /* an output buffer is smaller than the size required   */
+  MXFP4_ERR_BUFFER = 7,          /* an output buffer is smaller than the size required   */
+  MXFP4_ERR_ARG = 8              /* a scalar argument is out of range (e.g. eps <= 0)    */
 } mxfp4_status;
 
 /* Static, human-readable name of a status code (never NULL). */
@@ -67,6 +68,31 @@ const char* mxfp4_status_str(int status);
  * ------------------------------------------------------------------------- */
 int mxfp4_quant(const void* x, int64_t ldx, void* q, int64_t ldq, void* s, int64_t lds,
                 int64_t M, int64_t K, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mxfp4_rmsnorm_quant -- RMSNorm of each row of a bf16 matrix X[M, K] followed
+ * by MXFP4 quantisation along K, in one launch: the fused RMSNorm + MXFP4
+ * quantisation that page 683203 names (docstring trick 1, and the comment above
+ * ``_quant_shuffled``) as the step before the GEMM in a transformer layer; the
+ * pages print none of its arithmetic, so the norm is the standard one:
+ *   ss  = sum_k x[k]^2 in float64, in a fixed order (64 lane sums, lane t
+ *         adding k = 512c + 8t + e for c = 0, 1, ... and e = 0..7 in that
+ *         order, then a halving tree over the lanes), so results are
+ *         reproducible bit for bit;
+ *   inv = fp32(1 / sqrt(ss / K + eps)), float64 steps;
+ *   y   = bf16(fp32(fp32(x * inv) * w)), rounding to nearest even;
+ *   (q, s) = the MXFP4 quantisation of y, exactly as mxfp4_quant.
+ *   x   : bf16 [M, K], row stride ldx elements (ldx >= K); x and ldx*2 must be
+ *         multiples of 16 bytes.
+ *   w   : bf16 [K], 16-byte aligned.
+ *   eps : finite, > 0; otherwise MXFP4_ERR_ARG.
+ *   q   : out, fp4x2 [M, K/2], row stride ldq bytes (ldq >= K/2); q and ldq
+ *         multiples of 4 bytes.
+ *   s   : out, E8M0 [M, K/32], row stride lds bytes (lds >= K/32).
+ *   K % 32 == 0, M >= 1, K >= 32.
+ * ------------------------------------------------------------------------- */
+int mxfp4_rmsnorm_quant(const void* x, int64_t ldx, const void* w, float eps, void* q, int64_t ldq,
+                        void* s, int64_t lds, int64_t M, int64_t K, void* stream);
 
 /* ---------------------------------------------------------------------------
  * mxfp4_pack_B -- one-time, offline repacking of a quantised weight B[N, K]

@@ -88,6 +88,9 @@ __device__ __forceinline__ void quant32(const uint32_t (&w)[16], uint32_t (&q)[4
 // the matrix instruction's product: an all-zero block gets byte 0 instead of
 // e8m0_from_amax_bits' 127 (its codes are zero, so the product is zero under
 // any finite scale), which leaves a saturating subtract as the whole rule.
+// EXACT_ZERO: give an all-zero block the E8M0 byte 127 of the full rule
+// (e8m0_from_amax_bits), for callers that store the scale bytes.
+template <bool EXACT_ZERO = false>
 __device__ __forceinline__ uint32_t quant8_quad(const uint32_t (&w)[4], uint32_t& sbyte) {
   const v2u16 m2 = __builtin_elementwise_max(__builtin_elementwise_max(abs_pair(w[0]), abs_pair(w[1])),
                                              __builtin_elementwise_max(abs_pair(w[2]), abs_pair(w[3])));
@@ -96,7 +99,7 @@ __device__ __forceinline__ uint32_t quant8_quad(const uint32_t (&w)[4], uint32_t
   a = a > o ? a : o;
   o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)a, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
   a = a > o ? a : o;
-  sbyte = __builtin_elementwise_sub_sat(a >> 7, 2u);  // max(e - 2, 0)
+  sbyte = EXACT_ZERO ? e8m0_from_amax_bits(a) : __builtin_elementwise_sub_sat(a >> 7, 2u);  // max(e - 2, 0)
   const float scale = __builtin_bit_cast(float, sbyte << 23);
   uint32_t r = 0;
   r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(v2bf, w[0]), scale, 0);

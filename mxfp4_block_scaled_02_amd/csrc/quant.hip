@@ -51,6 +51,7 @@ extern "C" const char* mxfp4_status_str(int status) {
     case MXFP4_ERR_TOO_MANY_GROUPS: return "MXFP4_ERR_TOO_MANY_GROUPS: G outside [1, MXFP4_MAX_GROUPS]";
     case MXFP4_ERR_HIP: return "MXFP4_ERR_HIP: the HIP runtime rejected a launch";
     case MXFP4_ERR_BUFFER: return "MXFP4_ERR_BUFFER: output buffer too small";
+    case MXFP4_ERR_ARG: return "MXFP4_ERR_ARG: a scalar argument is out of range";
     default: return "unknown mxfp4 status";
   }
 }

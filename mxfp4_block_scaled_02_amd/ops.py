@@ -19,8 +19,8 @@ _lock = threading.Lock()
 
 MXFP4_MAX_GROUPS = 32
 STATUS = {0: "MXFP4_OK", 1: "MXFP4_ERR_NULL", 2: "MXFP4_ERR_SHAPE", 3: "MXFP4_ERR_ALIGN", 4: "MXFP4_ERR_WORKSPACE",
-          5: "MXFP4_ERR_TOO_MANY_GROUPS", 6: "MXFP4_ERR_HIP", 7: "MXFP4_ERR_BUFFER"}
-EXPORTED = ["mxfp4_status_str", "mxfp4_quant", "mxfp4_pack_B_bytes", "mxfp4_pack_B", "gemm_a4w4_workspace_bytes",
+          5: "MXFP4_ERR_TOO_MANY_GROUPS", 6: "MXFP4_ERR_HIP", 7: "MXFP4_ERR_BUFFER", 8: "MXFP4_ERR_ARG"}
+EXPORTED = ["mxfp4_status_str", "mxfp4_quant", "mxfp4_rmsnorm_quant", "mxfp4_pack_B_bytes", "mxfp4_pack_B", "gemm_a4w4_workspace_bytes",
             "gemm_a4w4_fused", "gemm_a4w4", "grouped_gemm_a4w4_workspace_bytes", "grouped_gemm_a4w4"]
 
 
@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
         vp, i64, sz, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
         L.mxfp4_status_str.argtypes, L.mxfp4_status_str.restype = [i32], ctypes.c_char_p
         L.mxfp4_quant.argtypes, L.mxfp4_quant.restype = [vp, i64, vp, i64, vp, i64, i64, i64, vp], i32
+        L.mxfp4_rmsnorm_quant.argtypes = [vp, i64, vp, ctypes.c_float, vp, i64, vp, i64, i64, i64, vp]
+        L.mxfp4_rmsnorm_quant.restype = i32
         L.mxfp4_pack_B_bytes.argtypes, L.mxfp4_pack_B_bytes.restype = [i64, i64], sz
         L.mxfp4_pack_B.argtypes, L.mxfp4_pack_B.restype = [vp, vp, i64, i64, vp, sz, vp], i32
         L.gemm_a4w4_workspace_bytes.argtypes, L.gemm_a4w4_workspace_bytes.restype = [i64, i64, i64], sz
@@ -112,6 +114,27 @@ def quant(x: torch.Tensor, out=None):
             raise ValueError("out buffers must be [M, K/2] and [M, K/32]")
     _check(lib().mxfp4_quant(x.data_ptr(), x.stride(0), q.data_ptr(), q.stride(0), s.data_ptr(), s.stride(0), M, K,
                              _stream(x)), "mxfp4_quant")
+    return q, s
+
+
+def rmsnorm_quant(x: torch.Tensor, w: torch.Tensor, eps: float, out=None):
+    """RMSNorm of each row of bf16 x [M, K] with bf16 weight w [K], then MXFP4:
+    (q uint8 [M, K/2], s uint8 [M, K/32]); `out` = (q, s) reuses given buffers."""
+    _require(x, torch.bfloat16, "x")
+    M, K = x.shape
+    if not w.is_cuda or w.dtype != torch.bfloat16 or w.dim() != 1 or w.shape[0] != K or w.stride(0) != 1:
+        raise ValueError("w must be a contiguous bf16 CUDA vector of length K")
+    if out is None:
+        q = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+        s = torch.empty((M, K // 32), dtype=torch.uint8, device=x.device)
+    else:
+        q, s = out
+        _require(q, torch.uint8, "q")
+        _require(s, torch.uint8, "s")
+        if q.shape != (M, K // 2) or s.shape != (M, K // 32):
+            raise ValueError("out buffers must be [M, K/2] and [M, K/32]")
+    _check(lib().mxfp4_rmsnorm_quant(x.data_ptr(), x.stride(0), w.data_ptr(), float(eps), q.data_ptr(), q.stride(0),
+                                     s.data_ptr(), s.stride(0), M, K, _stream(x)), "mxfp4_rmsnorm_quant")
     return q, s
 
 

@@ -37,7 +37,7 @@ WORKLOADS = {
 }
 WORKLOAD_ORDER = ["tiny", "skinny", "stress", "square", "grouped"]
 
-STREAM_A, STREAM_B, STREAM_MASK, STREAM_ROWEXP, STREAM_GROUPS = 0, 1, 2, 3, 4
+STREAM_A, STREAM_B, STREAM_MASK, STREAM_ROWEXP, STREAM_GROUPS, STREAM_NORM_W = 0, 1, 2, 3, 4, 5
 
 
 def rng(seed: int, stream: int, *sub: int) -> np.random.Generator:
@@ -64,6 +64,12 @@ def make_a(M: int, K: int, seed: int, stream_sub=()) -> np.ndarray:
 
 def make_b(N: int, K: int, seed: int, stream_sub=()) -> np.ndarray:
     return normal_bf16((N, K), 0.02, rng(seed, STREAM_B, *stream_sub))
+
+
+def make_norm_weight(K: int, seed: int) -> np.ndarray:
+    """RMSNorm weight [K] as bf16 bits: 1 + N(0, 0.1), the usual shape of a trained norm gain."""
+    w = np.float32(1.0) + np.float32(0.1) * rng(seed, STREAM_NORM_W).standard_normal(size=K, dtype=np.float32)
+    return f32_to_bf16_bits(w)
 
 
 def make_stress_a(M: int, K: int, seed: int) -> np.ndarray:

@@ -96,6 +96,22 @@ def test_quant_validation(change, status):
     assert got == status
 
 
+OK_R = dict(x=P, ldx=64, w=P, eps=1e-6, q=P, ldq=32, s=P, lds=2, M=4, K=64)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(x=None), 1), (dict(w=None), 1), (dict(q=None), 1), (dict(s=None), 1),
+    (dict(M=0), 2), (dict(K=0), 2), (dict(K=48), 2), (dict(ldx=32), 2), (dict(ldq=16), 2), (dict(lds=1), 2),
+    (dict(eps=0.0), 8), (dict(eps=-1e-6), 8), (dict(eps=float("nan")), 8), (dict(eps=float("inf")), 8),
+    (dict(x=P + 2), 3), (dict(w=P + 8), 3), (dict(q=P + 2), 3), (dict(ldx=68), 3), (dict(ldq=34), 3),
+])
+def test_rmsnorm_quant_validation(change, status):
+    a = dict(OK_R, **change)
+    got = ops.lib().mxfp4_rmsnorm_quant(a["x"], a["ldx"], a["w"], a["eps"], a["q"], a["ldq"], a["s"], a["lds"],
+                                        a["M"], a["K"], None)
+    assert got == status
+
+
 @pytest.mark.parametrize("change,status", [
     (dict(bq=None), 1), (dict(out=None), 1), (dict(N=0), 2), (dict(K=40), 2),
     (dict(bq=P + 4), 3), (dict(out=P + 1), 3), (dict(out_bytes=1000), 7),
