@@ -52,7 +52,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="skinny", choices=["tiny", "skinny", "stress", "square", "grouped"])
+    p.add_argument("--workload", default="skinny", choices=["tiny", "skinny", "stress", "square", "grouped", "rmsnorm"],
+                   help="rmsnorm times mxfp4_rmsnorm_quant (RMSNorm fused with MXFP4 quantisation) at M4096 K7168")
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--warm-cache", action="store_true", help="reuse one operand set (Infinity Cache resident)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -187,6 +188,95 @@ def cpu_baseline(w, unit, budget_s=12.0):
                 sample=f"{sample_desc}; median of {len(times)} runs, {t * 1e3:.1f} ms each")
 
 
+RMS_METRIC = "µs/call and HBM GB/s (% of peak) for RMSNorm fused with MXFP4 quantisation, M=4096 K=7168"
+RMS_M, RMS_K, RMS_EPS = 4096, 7168, 1e-6
+
+
+def rms_bytes(M, K):
+    """x read once (2MK), the gain w (2K), codes (MK/2) and scale bytes (MK/32) written once."""
+    return 2 * M * K + 2 * K + M * K // 2 + M * K // 32
+
+
+def bench_rmsnorm(args):
+    """One call of mxfp4_rmsnorm_quant per step, over rotated (cold) input sets."""
+    import torch
+    from mxfp4_block_scaled_02_amd import ops, synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    seed = 101 if args.seed is None else args.seed
+    M, K = RMS_M, RMS_K
+    log(f"[bench] workload=rmsnorm seed={seed}: generating inputs")
+    xb, wb = synth.make_a(M, K, seed), synth.make_norm_weight(K, seed)
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x0, w = bf16(xb), bf16(wb)
+    set_bytes = rms_bytes(M, K)
+    R = 1 if args.warm_cache else max(1, math.ceil(ROTATE_BYTES / set_bytes))
+    R = min(R, args.steps)
+    sets = [(x0.clone() if r else x0, torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
+             torch.empty((M, K // 32), dtype=torch.uint8, device=dev)) for r in range(R)]
+
+    def step(i):
+        x, q, sc = sets[i % R]
+        ops.rmsnorm_quant(x, w, RMS_EPS, out=(q, sc))
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if args.no_graph:
+        runner = lambda: [step(i) for i in range(args.steps)]  # noqa: E731
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.steps):
+                step(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        runner = g.replay
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    runner()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    gbs = set_bytes / (ms_step * 1e-3) / 1e9
+    out = dict(metric=RMS_METRIC, value=round(gbs, 3), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+               ms_per_step=round(ms_step, 6), higher_is_better=True, scaling="weak", vs_baseline=None,
+               dtype="bf16 in, f64 sum of squares, f32 scale, mxfp4 out", data="synthetic",
+               config=dict(workload="rmsnorm", seed=seed, M=M, K=K, eps=RMS_EPS,
+                           cache="warm (1 set)" if R == 1 else f"cold ({R} rotated input sets)",
+                           timing="hip graph replay" if not args.no_graph else "eager launch loop",
+                           path="mxfp4_rmsnorm_quant"),
+               us_per_call=round(ms_step * 1e3, 3), hbm_gbs=round(gbs, 2),
+               roofline=dict(bound="hbm", achieved=round(gbs, 3), peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, algorithmic_bytes=set_bytes))
+    if not args.no_cpu_baseline:
+        import oracle.rmsnorm as orn
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            threads = 1
+        rows = 64
+        times, t_end = [], time.perf_counter() + 12.0
+        while True:
+            t0 = time.perf_counter()
+            orn.rmsnorm_quant(xb[:rows], wb, RMS_EPS)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() > t_end or len(times) >= 200:
+                break
+        t = float(np.median(times))
+        out["cpu_baseline"] = dict(value=round(rms_bytes(rows, K) / t / 1e9, 6), unit="GB/s", cores=int(threads),
+                                   kind="oracle", sample=f"oracle rmsnorm_quant on rows 0..{rows - 1} (K={K}); "
+                                   f"median of {len(times)} runs, {t * 1e3:.1f} ms each")
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration():
     import torch
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -215,6 +305,9 @@ def main():
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build measures the single-GPU "
               "kernel and has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "rmsnorm":
+        bench_rmsnorm(args)
+        return
     import torch
     from mxfp4_block_scaled_02_amd import ops, synth
 

@@ -89,7 +89,7 @@ int mxfp4_quant(const void* x, int64_t ldx, void* q, int64_t ldq, void* s, int64
  *   q   : out, fp4x2 [M, K/2], row stride ldq bytes (ldq >= K/2); q and ldq
  *         multiples of 4 bytes.
  *   s   : out, E8M0 [M, K/32], row stride lds bytes (lds >= K/32).
- *   K % 32 == 0, M >= 1, K >= 32.
+ *   K % 32 == 0, M >= 1, 32 <= K <= 2^29.
  * ------------------------------------------------------------------------- */
 int mxfp4_rmsnorm_quant(const void* x, int64_t ldx, const void* w, float eps, void* q, int64_t ldq,
                         void* s, int64_t lds, int64_t M, int64_t K, void* stream);

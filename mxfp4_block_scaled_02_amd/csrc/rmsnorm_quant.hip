@@ -34,93 +34,128 @@ struct RmsArgs {
 constexpr int kRowsPerBlock = 4;  // waves per 256-thread workgroup, one row each
 constexpr int kBatch = 8;         // passes whose loads are in flight together
 
+// Row loads go through a buffer resource over the row's 2K bytes: a lane whose
+// 16 bytes lie past the row reads zeros by the range check on its own offset,
+// which leaves the sums unchanged and needs no clamp or select.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t row_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 row_load16(__amdgpu_buffer_rsrc_t r, int k) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, 2 * k, 0, 0));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
-__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
-  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + wave;
-  if (r >= a.M) return;  // whole waves only; the kernel has no barrier
-  const uint16_t* const xr = a.x + r * a.ldx;
-  const int passes = (a.K + 511) / 512;
-
-  // Pass one: lane sum of squares, pass by pass and element by element. K is a
-  // multiple of 32, so a lane's 8 elements lie wholly inside or outside the row.
-  // Loads past the row read its last 16 bytes (they stay in bounds and are
-  // issued unconditionally, kBatch at a time) and count as zeros, which leaves
-  // every sum unchanged.
-  double acc = 0.0;
-  for (int c0 = 0; c0 < passes; c0 += kBatch) {
-    uint4 v[kBatch];
+// Lane quad quantisation of y = bf16((x * inv) * w) for one pass: 8 elements
+// of x and w per lane (zeros past the row); only lanes inside the row store.
+__device__ __forceinline__ void norm_quant_pass(const RmsArgs& a, int64_t r, int k0, const uint4& xv, const uint4& wv,
+                                                float inv, int l) {
+  const uint32_t xw[4] = {xv.x, xv.y, xv.z, xv.w}, ww[4] = {wv.x, wv.y, wv.z, wv.w};
+  uint32_t y[4];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int k0 = 512 * (c0 + b) + 8 * l;
-      v[b] = mx::ldg16(xr + (k0 < a.K ? k0 : a.K - 8));
-    }
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const bool in = 512 * (c0 + b) + 8 * l < a.K;
-      const uint32_t wd[4] = {in ? v[b].x : 0u, in ? v[b].y : 0u, in ? v[b].z : 0u, in ? v[b].w : 0u};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const double f = (double)((e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]));
-        acc = __builtin_fma(f, f, acc);  // f*f is exact in float64: this is acc + f^2, rounded once
-      }
-    }
+  for (int i = 0; i < 4; ++i) {
+    const float t0 = bf16_lo(xw[i]) * inv, t1 = bf16_hi(xw[i]) * inv;
+    const float y0 = t0 * bf16_lo(ww[i]), y1 = t1 * bf16_hi(ww[i]);
+    y[i] = mx::pack_bf16x2(y0, y1);  // one packed convert, round to nearest even
   }
+  uint32_t sb;
+  const uint32_t codes = mx::quant8_quad<true>(y, sb);  // all four lanes of a quad agree on k0 < K
+  if (k0 < a.K) {
+    *reinterpret_cast<uint32_t*>(a.q + r * a.ldq + k0 / 2) = codes;
+    if ((l & 3) == 0) a.s[r * a.lds + k0 / 32] = (uint8_t)sb;
+  }
+}
+
+// Adds the squares of one pass's 8 elements to acc in element order.
+__device__ __forceinline__ double add_squares(double acc, const uint4& v) {
+  const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const double f = (double)((e & 1) ? bf16_hi(wd[e >> 1]) : bf16_lo(wd[e >> 1]));
+    acc = __builtin_fma(f, f, acc);  // f*f is exact in float64: this is acc + f^2, rounded once
+  }
+  return acc;
+}
+
+// The 64 lane sums in the halving tree, then inv = fp32(1 / sqrt(ss/K + eps)).
+__device__ __forceinline__ float row_inv(double acc, int l, int K, float eps) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) {
     const double o = __shfl_down(acc, (unsigned)s, 64);
     if (l < s) acc = acc + o;
   }
   const double ss = __shfl(acc, 0, 64);
-  const double ms = ss / (double)a.K + (double)a.eps;
-  const float inv = (float)(1.0 / __builtin_sqrt(ms));
+  const double ms = ss / (double)K + (double)eps;
+  return (float)(1.0 / __builtin_sqrt(ms));
+}
 
-  // Pass two: y = bf16((x * inv) * w), then MXFP4 per lane quad. Every lane
-  // computes (clamped loads as above); only lanes inside the row store.
-  for (int c0 = 0; c0 < passes; c0 += kBatch) {
-    uint4 xv[kBatch], wv[kBatch];
+// KEEP > 0: rows of at most KEEP passes keep x (and w) in registers between
+// the two passes (one read of x). KEEP == 0: any K, x read again in pass two,
+// kBatch passes at a time.
+template <int KEEP>
+__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
+  const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + wave;
+  if (r >= a.M) return;  // whole waves only; the kernel has no barrier
+  const __amdgpu_buffer_rsrc_t xr = row_rsrc(a.x + r * a.ldx, 2 * a.K), wr = row_rsrc(a.w, 2 * a.K);
+  const int passes = (a.K + 511) / 512;
+
+  if constexpr (KEEP > 0) {
+    uint4 v[KEEP], wv[KEEP];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int k0 = 512 * (c0 + b) + 8 * l, kc = k0 < a.K ? k0 : a.K - 8;
-      xv[b] = mx::ldg16(xr + kc);
-      wv[b] = mx::ldg16(a.w + kc);
+    for (int c = 0; c < KEEP; ++c) v[c] = row_load16(xr, c < passes ? 512 * c + 8 * l : a.K);
+#pragma unroll
+    for (int c = 0; c < KEEP; ++c) wv[c] = row_load16(wr, c < passes ? 512 * c + 8 * l : a.K);
+    double acc = 0.0;
+#pragma unroll
+    for (int c = 0; c < KEEP; ++c) acc = add_squares(acc, v[c]);
+    const float inv = row_inv(acc, l, a.K, a.eps);
+#pragma unroll
+    for (int c = 0; c < KEEP; ++c)
+      if (c < passes) norm_quant_pass(a, r, 512 * c + 8 * l, v[c], wv[c], inv, l);
+  } else {
+    double acc = 0.0;
+    for (int c0 = 0; c0 < passes; c0 += kBatch) {
+      uint4 v[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) v[b] = row_load16(xr, 512 * (c0 + b) + 8 * l);
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) acc = add_squares(acc, v[b]);
     }
+    const float inv = row_inv(acc, l, a.K, a.eps);
+    for (int c0 = 0; c0 < passes; c0 += kBatch) {
+      uint4 xv[kBatch], wv[kBatch];
 #pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int k0 = 512 * (c0 + b) + 8 * l;
-      const uint32_t xw[4] = {xv[b].x, xv[b].y, xv[b].z, xv[b].w}, ww[4] = {wv[b].x, wv[b].y, wv[b].z, wv[b].w};
-      uint32_t y[4];
+      for (int b = 0; b < kBatch; ++b) {
+        xv[b] = row_load16(xr, 512 * (c0 + b) + 8 * l);
+        wv[b] = row_load16(wr, 512 * (c0 + b) + 8 * l);
+      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float t0 = bf16_lo(xw[i]) * inv, t1 = bf16_hi(xw[i]) * inv;
-        const float y0 = t0 * bf16_lo(ww[i]), y1 = t1 * bf16_hi(ww[i]);
-        y[i] = (uint32_t)mx::f32_to_bf16(y0) | ((uint32_t)mx::f32_to_bf16(y1) << 16);
-      }
-      uint32_t sb;
-      const uint32_t codes = mx::quant8_quad<true>(y, sb);  // all four lanes of a quad agree on `in`
-      if (k0 < a.K) {
-        *reinterpret_cast<uint32_t*>(a.q + r * a.ldq + k0 / 2) = codes;
-        if ((l & 3) == 0) a.s[r * a.lds + k0 / 32] = (uint8_t)sb;
-      }
+      for (int b = 0; b < kBatch; ++b) norm_quant_pass(a, r, 512 * (c0 + b) + 8 * l, xv[b], wv[b], inv, l);
     }
   }
 }
+
+// Rows of up to 16 passes (K <= 8192) take the register-resident kernel.
+constexpr int kKeepPasses = 16;
 
 }  // namespace
 
 extern "C" int mxfp4_rmsnorm_quant(const void* x, int64_t ldx, const void* w, float eps, void* q, int64_t ldq,
                                    void* s, int64_t lds, int64_t M, int64_t K, void* stream) {
   if (!x || !w || !q || !s) return MXFP4_ERR_NULL;
-  if (M < 1 || K < 32 || K % 32 != 0 || M > mxh::kMaxDim || K > mxh::kMaxDim) return MXFP4_ERR_SHAPE;
+  // K <= 2^29: a row's byte offsets (2k) then stay inside a buffer resource's 31-bit range.
+  if (M < 1 || K < 32 || K % 32 != 0 || M > mxh::kMaxDim || K > ((int64_t)1 << 29)) return MXFP4_ERR_SHAPE;
   if (ldx < K || ldq < K / 2 || lds < K / 32) return MXFP4_ERR_SHAPE;
   if (!(eps > 0.0f) || !(eps <= 3.4028235e38f)) return MXFP4_ERR_ARG;  // also rejects NaN
   if (!mxh::aligned(x, 16) || (ldx * 2) % 16 != 0 || !mxh::aligned(w, 16) || !mxh::aligned(q, 4) || ldq % 4 != 0)
     return MXFP4_ERR_ALIGN;
   RmsArgs a{(const uint16_t*)x, ldx, (const uint16_t*)w, (uint8_t*)q, ldq, (uint8_t*)s, lds, M, (int)K, eps};
   void* args[] = {&a};
-  return mxh::launch_status(hipLaunchKernel((const void*)rmsnorm_quant_kernel,
-                                            dim3((unsigned)mxh::cdiv(M, kRowsPerBlock)), dim3(256), args, 0,
+  const void* kern = (K + 511) / 512 <= kKeepPasses ? (const void*)rmsnorm_quant_kernel<kKeepPasses>
+                                                     : (const void*)rmsnorm_quant_kernel<0>;
+  return mxh::launch_status(hipLaunchKernel(kern, dim3((unsigned)mxh::cdiv(M, kRowsPerBlock)), dim3(256), args, 0,
                                             (hipStream_t)stream));
 }

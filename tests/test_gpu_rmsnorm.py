@@ -45,7 +45,8 @@ def check(xb, wb, eps, rows=None, **kw):
     assert np.array_equal(q[rows], qr), "codes differ"
 
 
-@pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (4, 512), (5, 544), (16, 7168), (17, 1056), (64, 2048)])
+@pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (4, 512), (5, 544), (16, 7168), (17, 1056), (64, 2048),
+                                 (2, 8192), (3, 8224), (2, 16384)])
 def test_parity_small(M, K):
     say(f"[rmsnorm] M{M} K{K}")
     check(synth.make_a(M, K, 21), synth.make_norm_weight(K, 21), 1e-6)
