@@ -35,6 +35,8 @@ ROTATE_BYTES = 512 << 20
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["mxfp4_block_scaled_02_amd/csrc/gemm.hip", "mxfp4_block_scaled_02_amd/csrc/mx_device.hpp",
                   "mxfp4_block_scaled_02_amd/csrc/host_common.hpp"]
+RMS_SOURCES = ["mxfp4_block_scaled_02_amd/csrc/rmsnorm_quant.hip", "mxfp4_block_scaled_02_amd/csrc/mx_device.hpp",
+               "mxfp4_block_scaled_02_amd/csrc/host_common.hpp"]
 COPY_BYTES = 256 << 20  # plain device copy used to calibrate the FETCH_SIZE / WRITE_SIZE counters
 
 
@@ -70,10 +72,10 @@ def parse():
     return p.parse_args()
 
 
-def kernel_source_hash():
+def kernel_source_hash(sources=KERNEL_SOURCES):
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in sources:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -86,7 +88,7 @@ def recorded_traffic(name):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(RMS_SOURCES if name == "rmsnorm" else KERNEL_SOURCES):
         return None
     return rec.get("bytes_per_launch")
 
@@ -121,7 +123,8 @@ def summarize_pmc(workload_dir, copy_dir, kernel):
     kv, kn = per_dispatch(workload_dir, kernel)
     cv, cn = per_dispatch(copy_dir, "copy")  # torch's device copy kernel
     expected_kib = COPY_BYTES / 1024
-    out = {"kernel": kernel, "kernel_source_hash": kernel_source_hash(), "copy_bytes": COPY_BYTES}
+    out = {"kernel": kernel, "kernel_source_hash": kernel_source_hash(RMS_SOURCES if "rmsnorm" in kernel else KERNEL_SOURCES),
+           "copy_bytes": COPY_BYTES}
     total = 0.0
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
         factor = expected_kib / cv[c] if cv.get(c) else None
@@ -254,7 +257,8 @@ def bench_rmsnorm(args):
                            path="mxfp4_rmsnorm_quant"),
                us_per_call=round(ms_step * 1e3, 3), hbm_gbs=round(gbs, 2),
                roofline=dict(bound="hbm", achieved=round(gbs, 3), peak=HBM_PEAK_GBS, unit="GB/s",
-                             frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, algorithmic_bytes=set_bytes))
+                             frac=round(gbs / HBM_PEAK_GBS, 4), traffic=recorded_traffic("rmsnorm"),
+                             algorithmic_bytes=set_bytes))
     if not args.no_cpu_baseline:
         import oracle.rmsnorm as orn
         try:
