@@ -184,6 +184,39 @@ size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, int G, int64
 int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,
                       size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * grouped_gemm_a4w4_mnk -- G groups of fused problems with their OWN (M, N, K)
+ * and a batch count L each, in ONE launch: page 496271's problem form
+ * (``custom_kernel``: a list of groups, each with its problem size (m, n, k, l)
+ * and tensors carrying a batch index l; there one launch per group and per l,
+ * here one launch over every problem's output tiles). Batch l of group g is
+ *   C_l = Q(A_l) . B_l^T,  A_l = A + l*strideA (elements), B_l = Bp + l*strideB
+ *   (bytes, each an mxfp4_pack_B(N, K) image), C_l = C + l*strideC (elements).
+ *   Per batch the rules of gemm_a4w4_fused apply to A, lda, B, C, ldc, M, N, K
+ *   (each batch row-major with unit stride along K; page 496271's layout with
+ *   the batch index innermost is transposed by the caller).
+ *   L >= 1. For L > 1: strideA >= 0 with strideA*2 a multiple of 16; strideB >=
+ *   mxfp4_pack_B_bytes(N, K), a multiple of 16; strideC >= M*ldc (the C slices
+ *   do not overlap); otherwise MXFP4_ERR_SHAPE / MXFP4_ERR_ALIGN.
+ *   The sum of L over the groups is at most MXFP4_MAX_GROUPS
+ *   (else MXFP4_ERR_TOO_MANY_GROUPS). No workspace: every problem runs on the
+ *   128 x 512 tiled kernel, whatever its M.
+ *   groups : HOST array of G descriptors, read during the call only.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void* A;
+  int64_t lda;
+  int64_t strideA;
+  const void* Bp;
+  int64_t strideB;
+  void* C;
+  int64_t ldc;
+  int64_t strideC;
+  int64_t M, N, K, L;
+} mxfp4_group_mnk;
+
+int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

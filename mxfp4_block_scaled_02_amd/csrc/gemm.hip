@@ -936,6 +936,46 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
+// Per-problem list of grouped_gemm_a4w4_mnk: every group contributes L
+// problems with their own (M, N, K); tile_start holds the prefix sums of the
+// problems' output tiles (128 x 512 each).
+struct MnkProblem {
+  const uint16_t* A;
+  int64_t lda;
+  const uint8_t* Bunit;
+  const uint32_t* Bscale;
+  uint16_t* C;
+  int64_t ldc;
+  int M, N, K, pad_;
+};
+struct MnkArgs {
+  MnkProblem p[MXFP4_MAX_GROUPS];
+  int tile_start[MXFP4_MAX_GROUPS + 1];
+  int P;
+};
+
+__global__ __launch_bounds__(kTThreads) void gemm_grouped_mnk_kernel(MnkArgs a) {
+  const int v = xcd_remap(blockIdx.x, gridDim.x);
+  int g = 0;
+  while (g + 1 < a.P && a.tile_start[g + 1] <= v) ++g;
+  const int local = v - a.tile_start[g];
+  const MnkProblem& q = a.p[g];
+  Operand o{};
+  o.A = q.A;
+  o.lda = q.lda;
+  o.Bunit = q.Bunit;
+  o.Bscale = q.Bscale;
+  o.C = q.C;
+  o.ldc = q.ldc;
+  o.M = q.M;
+  const int ku = (q.K + 63) / 64;
+  const Dims d{q.N, q.K, (q.K + 127) / 128, ku, (q.N + 31) / 32, (ku + 3) / 4};
+  const int ntn = (q.N + kTBN - 1) / kTBN;
+  __shared__ __align__(16) TiledSmem sm;
+  __shared__ __align__(16) uint8_t ring[kRingBytes];
+  tiled_tile<false>(o, d, local / ntn, local % ntn, sm, ring);
+}
+
 Dims make_dims(int64_t N, int64_t K) {
   const mxh::PackedGeom g(N, K);
   return Dims{(int)N, (int)K, (int)mxh::cdiv(K, 128), (int)g.KU, (int)g.NT, (int)g.KG};
@@ -1169,5 +1209,47 @@ extern "C" int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, in
   Dims d = make_dims(N, K);
   void* args[] = {&a, &d};
   return mxh::launch_status(hipLaunchKernel((const void*)gemm_grouped_kernel, dim3((unsigned)total),
+                                            dim3(kTThreads), args, 0, (hipStream_t)stream));
+}
+
+extern "C" int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void* stream) {
+  if (!groups) return MXFP4_ERR_NULL;
+  if (G < 1) return MXFP4_ERR_TOO_MANY_GROUPS;
+  MnkArgs a{};
+  int P = 0;
+  int64_t total = 0;
+  for (int g = 0; g < G; ++g) {
+    const mxfp4_group_mnk& q = groups[g];
+    if (q.L < 1) return MXFP4_ERR_SHAPE;
+    if (q.L > MXFP4_MAX_GROUPS - P) return MXFP4_ERR_TOO_MANY_GROUPS;
+    const int st = check_problem(q.A, q.lda, q.Bp, q.C, q.ldc, q.M, q.N, q.K);
+    if (st != MXFP4_OK) return st;
+    const mxh::PackedGeom pg(q.N, q.K);
+    if (q.L > 1) {  // batches: C slices must not overlap; every slice keeps the alignment rules
+      if (q.strideA < 0 || q.strideB < (int64_t)pg.total() || q.strideC < q.M * q.ldc) return MXFP4_ERR_SHAPE;
+      if ((q.strideA * 2) % 16 != 0 || q.strideB % 16 != 0) return MXFP4_ERR_ALIGN;
+    }
+    const int64_t tiles = mxh::cdiv(q.M, kTBM) * mxh::cdiv(q.N, kTBN);
+    for (int64_t l = 0; l < q.L; ++l) {
+      MnkProblem& o = a.p[P];
+      o.A = (const uint16_t*)q.A + l * q.strideA;
+      o.lda = q.lda;
+      o.Bunit = (const uint8_t*)q.Bp + l * q.strideB;
+      o.Bscale = (const uint32_t*)(o.Bunit + pg.code_bytes);
+      o.C = (uint16_t*)q.C + l * q.strideC;
+      o.ldc = q.ldc;
+      o.M = (int)q.M;
+      o.N = (int)q.N;
+      o.K = (int)q.K;
+      a.tile_start[P] = (int)total;
+      total += tiles;
+      if (total > INT32_MAX) return MXFP4_ERR_SHAPE;
+      ++P;
+    }
+  }
+  a.tile_start[P] = (int)total;
+  a.P = P;
+  void* args[] = {&a};
+  return mxh::launch_status(hipLaunchKernel((const void*)gemm_grouped_mnk_kernel, dim3((unsigned)total),
                                             dim3(kTThreads), args, 0, (hipStream_t)stream));
 }

@@ -21,13 +21,22 @@ MXFP4_MAX_GROUPS = 32
 STATUS = {0: "MXFP4_OK", 1: "MXFP4_ERR_NULL", 2: "MXFP4_ERR_SHAPE", 3: "MXFP4_ERR_ALIGN", 4: "MXFP4_ERR_WORKSPACE",
           5: "MXFP4_ERR_TOO_MANY_GROUPS", 6: "MXFP4_ERR_HIP", 7: "MXFP4_ERR_BUFFER", 8: "MXFP4_ERR_ARG"}
 EXPORTED = ["mxfp4_status_str", "mxfp4_quant", "mxfp4_rmsnorm_quant", "mxfp4_pack_B_bytes", "mxfp4_pack_B", "gemm_a4w4_workspace_bytes",
-            "gemm_a4w4_fused", "gemm_a4w4", "grouped_gemm_a4w4_workspace_bytes", "grouped_gemm_a4w4"]
+            "gemm_a4w4_fused", "gemm_a4w4", "grouped_gemm_a4w4_workspace_bytes", "grouped_gemm_a4w4",
+            "grouped_gemm_a4w4_mnk"]
 
 
 class Mxfp4Error(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = status
         super().__init__(f"{where}: {lib().mxfp4_status_str(status).decode()} (status {status})")
+
+
+class GroupMnk(ctypes.Structure):
+    """mirror of mxfp4_group_mnk"""
+    _fields_ = [("A", ctypes.c_void_p), ("lda", ctypes.c_int64), ("strideA", ctypes.c_int64),
+                ("Bp", ctypes.c_void_p), ("strideB", ctypes.c_int64), ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64),
+                ("strideC", ctypes.c_int64), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
+                ("L", ctypes.c_int64)]
 
 
 class Group(ctypes.Structure):
@@ -63,6 +72,8 @@ def lib() -> ctypes.CDLL:
         L.grouped_gemm_a4w4_workspace_bytes.restype = sz
         L.grouped_gemm_a4w4.argtypes = [ctypes.POINTER(Group), i32, i64, i64, vp, sz, vp]
         L.grouped_gemm_a4w4.restype = i32
+        L.grouped_gemm_a4w4_mnk.argtypes = [ctypes.POINTER(GroupMnk), i32, vp]
+        L.grouped_gemm_a4w4_mnk.restype = i32
         _lib = L
         return L
 
@@ -218,3 +229,35 @@ def grouped_gemm(a_list, bp_list, N: int, out_list=None):
     _check(lib().grouped_gemm_a4w4(arr, G, N, K, ws.data_ptr() if wsz else None, ws.numel() if wsz else 0,
                                    _stream(a_list[0])), "grouped_gemm_a4w4")
     return out_list
+
+
+def grouped_gemm_mnk(problems, out_list=None):
+    """Groups with their own (M, N, K) and a batch count, in one launch.
+
+    problems: list of (A, Bp, N) with A bf16 [L, M, K] (or [M, K] for L = 1) and
+    Bp uint8 [L, pack_B_bytes(N, K)] (or 1-D for L = 1), each batch row-major.
+    Returns (or fills `out_list` with) bf16 C tensors [L, M, N] ([M, N] for L = 1).
+    """
+    descs, outs = [], []
+    for gi, (A, Bp, N) in enumerate(problems):
+        batched = A.dim() == 3
+        A3 = A if batched else A.unsqueeze(0)
+        B2 = Bp if Bp.dim() == 2 else Bp.unsqueeze(0)
+        L, M, K = A3.shape
+        if not A3.is_cuda or A3.dtype != torch.bfloat16 or A3.stride(2) != 1:
+            raise ValueError("A must be a bf16 CUDA tensor with unit stride along K")
+        if B2.dtype != torch.uint8 or B2.shape[0] != L or B2.shape[1] < pack_B_bytes(N, K) or B2.stride(1) != 1:
+            raise ValueError("Bp must be uint8 [L, pack_B_bytes(N, K)]")
+        if out_list is None:
+            C3 = torch.empty((L, M, N), dtype=torch.bfloat16, device=A.device)
+        else:
+            C = out_list[gi]
+            C3 = C if C.dim() == 3 else C.unsqueeze(0)
+            if C3.shape != (L, M, N) or C3.dtype != torch.bfloat16 or C3.stride(2) != 1:
+                raise ValueError("out_list[i] must be bf16 [L, M, N]")
+        descs.append(GroupMnk(A3.data_ptr(), A3.stride(1), A3.stride(0), B2.data_ptr(), B2.stride(0),
+                              C3.data_ptr(), C3.stride(1), C3.stride(0), M, N, K, L))
+        outs.append(C3 if batched else C3[0])
+    arr = (GroupMnk * len(descs))(*descs)
+    _check(lib().grouped_gemm_a4w4_mnk(arr, len(descs), _stream(problems[0][0])), "grouped_gemm_a4w4_mnk")
+    return outs if out_list is None else out_list

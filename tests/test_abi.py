@@ -169,3 +169,35 @@ def test_grouped_validation():
     assert L.grouped_gemm_a4w4(g, 2, 4096, 7168, None, 0, None) == 1
     g[1] = ops.Group(P + 2, 7168, P, P, 4096, 64)
     assert L.grouped_gemm_a4w4(g, 2, 4096, 7168, None, 0, None) == 3
+
+
+def _mnk(**kw):
+    d = dict(A=P, lda=512, strideA=0, Bp=P, strideB=0, C=P, ldc=64, strideC=0, M=16, N=64, K=512, L=1)
+    d.update(kw)
+    return ops.GroupMnk(d["A"], d["lda"], d["strideA"], d["Bp"], d["strideB"], d["C"], d["ldc"], d["strideC"],
+                        d["M"], d["N"], d["K"], d["L"])
+
+
+@pytest.mark.parametrize("groups,status", [
+    ([_mnk(A=None)], 1), ([_mnk(C=None)], 1),
+    ([_mnk(L=0)], 2), ([_mnk(K=48)], 2), ([_mnk(lda=256)], 2), ([_mnk(ldc=32)], 2), ([_mnk(M=0)], 2),
+    ([_mnk(A=P + 8)], 3), ([_mnk(Bp=P + 4)], 3), ([_mnk(lda=516)], 3),
+    # batches: C slices must not overlap, B slices must hold a packed image, strides keep alignment
+    ([_mnk(L=2, strideA=512 * 16, strideB=1 << 20, strideC=16 * 64 - 1)], 2),
+    ([_mnk(L=2, strideA=512 * 16, strideB=100, strideC=16 * 64)], 2),
+    ([_mnk(L=2, strideA=-8, strideB=1 << 20, strideC=16 * 64)], 2),
+    ([_mnk(L=2, strideA=4, strideB=1 << 20, strideC=16 * 64)], 3),
+    ([_mnk(L=2, strideA=512 * 16, strideB=(1 << 20) + 4, strideC=16 * 64)], 3),
+    # at most 32 problems in all
+    ([_mnk(L=20, strideA=8192, strideB=1 << 20, strideC=1024), _mnk(L=13, strideA=8192, strideB=1 << 20,
+                                                                      strideC=1024)], 5),
+])
+def test_grouped_mnk_validation(groups, status):
+    arr = (ops.GroupMnk * len(groups))(*groups)
+    assert ops.lib().grouped_gemm_a4w4_mnk(arr, len(groups), None) == status
+
+
+def test_grouped_mnk_rejects_empty_list():
+    assert ops.lib().grouped_gemm_a4w4_mnk(None, 1, None) == 1
+    arr = (ops.GroupMnk * 1)(_mnk())
+    assert ops.lib().grouped_gemm_a4w4_mnk(arr, 0, None) == 5
