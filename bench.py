@@ -54,8 +54,10 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="skinny", choices=["tiny", "skinny", "stress", "square", "grouped", "rmsnorm"],
-                   help="rmsnorm times mxfp4_rmsnorm_quant (RMSNorm fused with MXFP4 quantisation) at M4096 K7168")
+    p.add_argument("--workload", default="skinny",
+                   choices=["tiny", "skinny", "stress", "square", "grouped", "rmsnorm", "grouped_mnk"],
+                   help="rmsnorm times mxfp4_rmsnorm_quant (RMSNorm fused with MXFP4 quantisation) at M4096 K7168; "
+                        "grouped_mnk times grouped_gemm_a4w4_mnk on seeded groups with their own (M, N, K, L)")
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--warm-cache", action="store_true", help="reuse one operand set (Infinity Cache resident)")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -281,6 +283,115 @@ def bench_rmsnorm(args):
     print(json.dumps(out), flush=True)
 
 
+MNK_METRIC = "µs/call and TFLOP/s (% of peak) for grouped a4w4 GEMM with per-group (M, N, K) and batch L"
+
+
+def mnk_problems(seed):
+    """Seeded groups: M in {128..1024 step 64}, N in {1024, 2048, 4096}, K in {1024, 2048, 4096, 7168}, L in {1, 2, 3};
+    six groups (at most 18 problems)."""
+    g = np.random.default_rng([seed, 7])
+    return [(int(128 + 64 * g.integers(0, 15)), int(g.choice([1024, 2048, 4096])),
+             int(g.choice([1024, 2048, 4096, 7168])), int(g.integers(1, 4))) for _ in range(6)]
+
+
+def bench_grouped_mnk(args):
+    """One grouped_gemm_a4w4_mnk call per step over rotated (cold) operand sets."""
+    import torch
+    from mxfp4_block_scaled_02_amd import ops, synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    seed = 102 if args.seed is None else args.seed
+    shapes = mnk_problems(seed)
+    log(f"[bench] workload=grouped_mnk seed={seed}: {shapes}")
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    base = []
+    for gi, (M, N, K, L) in enumerate(shapes):
+        A = torch.stack([bf16(synth.make_a(M, K, seed, (gi, l))) for l in range(L)])
+        Bp = torch.stack([ops.pack_B(*ops.quant(bf16(synth.make_b(N, K, seed, (gi, l))))) for l in range(L)])
+        base.append((A, Bp, N))
+    flops = sum(L * alg_flops(M, N, K) for M, N, K, L in shapes)
+    nbytes = sum(L * alg_bytes(M, N, K) for M, N, K, L in shapes)
+    set_bytes = sum(A.numel() * 2 + Bp.numel() for A, Bp, _ in base) + sum(L * 2 * M * N for M, N, K, L in shapes)
+    R = 1 if args.warm_cache else max(1, math.ceil(ROTATE_BYTES / set_bytes))
+    R = min(R, args.steps)
+    sets = []
+    for r in range(R):
+        probs = [(A.clone() if r else A, Bp.clone() if r else Bp, N) for A, Bp, N in base]
+        outs = [torch.empty((A.shape[0], A.shape[1], N), dtype=torch.bfloat16, device=dev) for A, _, N in probs]
+        sets.append((probs, outs))
+
+    def step(i):
+        probs, outs = sets[i % R]
+        ops.grouped_gemm_mnk(probs, out_list=outs)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if args.no_graph:
+        runner = lambda: [step(i) for i in range(args.steps)]  # noqa: E731
+    else:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(args.steps):
+                step(i)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        runner = gr.replay
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    runner()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    if flops / (FP4_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
+        bound, achieved, peak, unit = "mfma", tflops, FP4_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", gbs, HBM_PEAK_GBS, "GB/s"
+    out = dict(metric=MNK_METRIC, value=round(achieved, 3), unit=unit, n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=round(ms_step, 6), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="mxfp4 (e2m1 x e8m0, fp32 accumulate, bf16 out)", data="synthetic",
+               config=dict(workload="grouped_mnk", seed=seed, groups=[dict(M=M, N=N, K=K, L=L) for M, N, K, L in shapes],
+                           cache="warm (1 set)" if R == 1 else f"cold ({R} rotated operand sets)",
+                           timing="hip graph replay" if not args.no_graph else "eager launch loop",
+                           path="grouped_gemm_a4w4_mnk"),
+               us_per_call=round(ms_step * 1e3, 3), tflops=round(tflops, 3), hbm_gbs=round(gbs, 2),
+               roofline=dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
+                             frac=round(achieved / peak, 4), traffic=None, algorithmic_bytes=nbytes,
+                             algorithmic_flops=flops))
+    if not args.no_cpu_baseline:
+        import oracle
+        M, N, K, L = shapes[0]
+        a = synth.make_a(M, K, seed, (0, 0))
+        bq, bs = oracle.quant_mx(synth.make_b(N, K, seed, (0, 0)))
+        rows = min(M, 64)
+        times, t_end = [], time.perf_counter() + 12.0
+        while True:
+            t0 = time.perf_counter()
+            oracle.gemm_ref(a[:rows], bq, bs)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() > t_end or len(times) >= 200:
+                break
+        t = float(np.median(times))
+        val = alg_flops(rows, N, K) / t / 1e12 if unit == "TFLOP/s" else alg_bytes(rows, N, K) / t / 1e9
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            threads = 1
+        out["cpu_baseline"] = dict(value=round(val, 6), unit=unit, cores=int(threads), kind="oracle",
+                                   sample=f"oracle gemm_ref on rows 0..{rows - 1} of the first problem (N={N}, K={K}); "
+                                          f"median of {len(times)} runs, {t * 1e3:.1f} ms each")
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration():
     import torch
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -311,6 +422,9 @@ def main():
         sys.exit(2)
     if args.workload == "rmsnorm":
         bench_rmsnorm(args)
+        return
+    if args.workload == "grouped_mnk":
+        bench_grouped_mnk(args)
         return
     import torch
     from mxfp4_block_scaled_02_amd import ops, synth
