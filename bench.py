@@ -55,7 +55,7 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="skinny",
-                   choices=["tiny", "skinny", "stress", "square", "grouped", "rmsnorm", "grouped_mnk"],
+                   choices=["tiny", "skinny", "stress", "square", "grouped", "rmsnorm", "grouped_mnk", "skinny_shard8"],
                    help="rmsnorm times mxfp4_rmsnorm_quant (RMSNorm fused with MXFP4 quantisation) at M4096 K7168; "
                         "grouped_mnk times grouped_gemm_a4w4_mnk on seeded groups with their own (M, N, K, L)")
     p.add_argument("--seed", type=int, default=None)

@@ -1068,14 +1068,17 @@ SplitGeom split_geom(int64_t M, int64_t N, int64_t K) {
   if (smin > kSpMaxSplits || T * kSpMaxSplits > INT32_MAX) return g;
   // Pick S by a simple time model: a workgroup's loads take a latency plus its
   // bytes at one CU's streaming rate, rounds of more workgroups than CUs add up,
-  // and splitting adds one device-scope hand-off to the owners.
+  // and splitting adds one device-scope hand-off to the owners, plus one more
+  // poll round trip for every further batch of kSpBatch partials. (Measured at
+  // M16 K7168, N 264..2112: 5.5-6.2 us with one batch, +0.6-1 us per batch.)
   int64_t S = smin;
   double best = -1.0;
   for (int64_t s = smin; s <= std::min<int64_t>(KT, kSpMaxSplits); ++s) {
     const double steps = (double)mxh::cdiv(KT, s);
     const double bytes = steps * (16.0 * 128 * 2 + kSpW * 1024.0 + kSpW * 256.0);  // A, B codes, B scales
     const double rounds = (double)mxh::cdiv(T * s, 256);
-    const double t = rounds * (1.0 + bytes / 25e3) + (s > 1 ? 1.5 : 0.0);  // microseconds
+    const double batches = (double)mxh::cdiv(s - 1, kSpBatch);
+    const double t = rounds * (1.0 + bytes / 25e3) + (s > 1 ? 1.5 * batches : 0.0);  // microseconds
     if (best < 0 || t < best - 1e-9) {
       best = t;
       S = s;

@@ -19,6 +19,8 @@ kernelbot nvfp4-group-gemm submission 496271):
   square   M=4096 N=4096  K=7168   A ~ N(0,1), B ~ N(0, 0.02)
   grouped  8 groups sharing N=4096, K=7168; M_g = 128 + 64*U{0..14};
            each group has its own A_g ~ N(0,1) and B_g ~ N(0,0.02)
+  skinny_shard8  M=16 N=264 K7168: one GPU's share of skinny when N is split
+           eight ways (skinny's A and the first 264 rows of its B, same seed)
 
 Every tensor draws from its own stream:
 numpy PCG64(SeedSequence([seed, stream, *sub])). Streams: 0 = A, 1 = B,
@@ -34,8 +36,10 @@ WORKLOADS = {
     "stress": dict(M=64, N=7168, K=2048),
     "square": dict(M=4096, N=4096, K=7168),
     "grouped": dict(G=8, N=4096, K=7168),
+    "skinny_shard8": dict(M=16, N=264, K=7168),
 }
 WORKLOAD_ORDER = ["tiny", "skinny", "stress", "square", "grouped"]
+SHARD_OF = {"skinny_shard8": "skinny"}  # a shard draws from its parent's seed
 
 STREAM_A, STREAM_B, STREAM_MASK, STREAM_ROWEXP, STREAM_GROUPS, STREAM_NORM_W = 0, 1, 2, 3, 4, 5
 
@@ -126,4 +130,4 @@ def workload(name: str, seed: int, rows=None):
 
 
 def default_seed(name: str) -> int:
-    return WORKLOAD_ORDER.index(name)
+    return WORKLOAD_ORDER.index(SHARD_OF.get(name, name))

@@ -133,7 +133,7 @@ def test_pack_B_layout(N, K):
 # ---------------------------------------------------------------------------
 # fused GEMM
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["tiny", "skinny", "stress"])
+@pytest.mark.parametrize("name", ["tiny", "skinny", "stress", "skinny_shard8"])
 def test_gemm_workload_full(name):
     say(f"gemm workload {name}")
     w = synth.workload(name, synth.default_seed(name))
@@ -195,9 +195,11 @@ def test_grouped_workload_sampled_rows():
 
 EDGE = [(1, 1, 32), (1, 16, 128), (2, 100, 96), (4, 256, 512), (16, 2112, 7168), (17, 50, 160), (33, 64, 352),
         (64, 130, 2048), (65, 130, 288), (127, 257, 1056), (255, 300, 4096), (1, 4096, 7168), (300, 33, 32),
-        # split-K path (M <= 16): K tail with M < 16; odd K/64 with one K step per split (57 splits);
-        # the 64-split maximum; more K than 64 splits can hold (falls back); a middle case
-        (3, 70, 352), (16, 130, 7232), (16, 64, 65536), (16, 48, 66560), (8, 1000, 6144)]
+        # split-K path (M <= 16): K tail with M < 16; odd K/64 with a K tail (9 splits of 6-7 steps);
+        # odd K/64 with one K step per split (9 splits); the 64-split maximum; more K than 64 splits
+        # can hold (falls back); a middle case; the 8-way N shard of skinny
+        (3, 70, 352), (16, 130, 7232), (16, 130, 1088), (16, 64, 65536), (16, 48, 66560), (8, 1000, 6144),
+        (16, 264, 7168)]
 
 
 @pytest.mark.parametrize("M,N,K", EDGE)

@@ -44,3 +44,9 @@ def test_group_sizes():
     for seed in range(5):
         ms = synth.group_sizes(seed)
         assert len(ms) == 8 and all(128 <= m <= 1024 and (m - 128) % 64 == 0 for m in ms)
+
+
+def test_shard_is_a_slice_of_its_parent():
+    a, b = synth.workload("skinny_shard8", synth.default_seed("skinny_shard8")), synth.workload("skinny", 1)
+    assert synth.default_seed("skinny_shard8") == synth.default_seed("skinny")
+    assert np.array_equal(a["A"], b["A"]) and np.array_equal(a["B"], b["B"][:264])
