@@ -42,6 +42,7 @@ WORKLOAD_ORDER = ["tiny", "skinny", "stress", "square", "grouped"]
 SHARD_OF = {"skinny_shard8": "skinny"}  # a shard draws from its parent's seed
 
 STREAM_A, STREAM_B, STREAM_MASK, STREAM_ROWEXP, STREAM_GROUPS, STREAM_NORM_W = 0, 1, 2, 3, 4, 5
+STREAM_NV_CODES, STREAM_NV_SCALES = 6, 7
 
 
 def rng(seed: int, stream: int, *sub: int) -> np.random.Generator:
@@ -131,3 +132,15 @@ def workload(name: str, seed: int, rows=None):
 
 def default_seed(name: str) -> int:
     return WORKLOAD_ORDER.index(SHARD_OF.get(name, name))
+
+
+def make_nvfp4(R: int, K: int, seed: int, stream_sub=()):
+    """Random NVFP4 operand [R, K]: packed E2M1 codes uint8 [R, K/2], every byte
+    uniform over 0..255 (all 16 codes equally likely, both signs), and E4M3
+    scale bytes uint8 [R, K/16], positive, exponent field uniform in 4..10
+    (2^-3 .. 2^3) and mantissa field uniform in 0..7. Raw bytes only."""
+    codes = rng(seed, STREAM_NV_CODES, *stream_sub).integers(0, 256, size=(R, K // 2), dtype=np.uint8)
+    g = rng(seed, STREAM_NV_SCALES, *stream_sub)
+    e = g.integers(4, 11, size=(R, K // 16), dtype=np.uint8)
+    m = g.integers(0, 8, size=(R, K // 16), dtype=np.uint8)
+    return codes, ((e << np.uint8(3)) | m).astype(np.uint8)

@@ -25,3 +25,4 @@ from .mx import (  # noqa: F401
     gemm_exact_fraction,
 )
 from . import rmsnorm  # noqa: F401,E402  (RMSNorm followed by MXFP4 quantisation)
+from . import nvfp4  # noqa: F401,E402  (NVFP4: E2M1 with one E4M3 scale per 16)
