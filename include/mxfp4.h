@@ -217,6 +217,57 @@ typedef struct {
 
 int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * grouped_gemm_nvfp4 -- the NVFP4 block-scaled GEMM of page 496271
+ * (kernelbot nvfp4-group-gemm: module docstring, constants block,
+ * ``nvfp4_gemm_kernel``, ``custom_kernel``) for G groups with their own
+ * (M, N, K) and batch count L, in ONE launch. Both operands arrive quantised:
+ *   C_l[m, n] = sum_k deq(A_l)[m, k] * deq(B_l)[n, k],   deq(X)[r, k] =
+ *     E2M1(code of element k of row r) * E4M3(Xs[r, k / 16]),
+ * accumulated in fp32 and stored as float16 (round to nearest even; overflow
+ * gives infinity). No per-tensor scale (the page applies none).
+ *   Aq : E2M1 codes [M, K/2], two per byte, element 2j in the low nibble of
+ *        byte j, sign in bit 3 (the MXFP4 nibble order); row stride lda bytes,
+ *        8-byte aligned, lda a multiple of 8, lda >= K/2.
+ *   As : E4M3 (OCP FP8 E4M3: bias 7, no infinities, 0x7F/0xFF NaN) scale bytes
+ *        [M, K/16] row-major (the page's reordered layout is not used), row
+ *        stride ldas >= K/16 bytes, any alignment.
+ *   Bq, ldb, Bs, ldbs : the same for B [N, K].
+ *   C  : float16 [M, N], row stride ldc >= N elements, 2-byte aligned.
+ *   M, N >= 1; K >= 16 with K % 16 == 0 (else MXFP4_ERR_SHAPE). Code bytes of
+ *   elements past K in a row are ignored (any value); scale bytes past K/16
+ *   are ignored. A NaN scale inside K makes the affected C entries NaN.
+ *   (M + 128) * lda, (M + 128) * ldas, (N + 128) * ldb and (N + 128) * ldbs
+ *   must stay below 2^31 (else MXFP4_ERR_SHAPE).
+ *   Batch l uses Aq + l*strideA, As + l*strideAs, Bq + l*strideB,
+ *   Bs + l*strideBs (bytes) and C + l*strideC (elements). L >= 1; for L > 1
+ *   the strides are >= 0, strideA and strideB multiples of 8
+ *   (MXFP4_ERR_ALIGN), strideC >= M*ldc (MXFP4_ERR_SHAPE).
+ *   The sum of L over the groups is at most MXFP4_MAX_GROUPS
+ *   (else MXFP4_ERR_TOO_MANY_GROUPS). No workspace.
+ *   groups : HOST array of G descriptors, read during the call only.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  const void* Aq;
+  int64_t lda;
+  int64_t strideA;
+  const void* As;
+  int64_t ldas;
+  int64_t strideAs;
+  const void* Bq;
+  int64_t ldb;
+  int64_t strideB;
+  const void* Bs;
+  int64_t ldbs;
+  int64_t strideBs;
+  void* C;
+  int64_t ldc;
+  int64_t strideC;
+  int64_t M, N, K, L;
+} nvfp4_group;
+
+int grouped_gemm_nvfp4(const nvfp4_group* groups, int G, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmxfp4.so")
-SOURCES = ["quant.hip", "rmsnorm_quant.hip", "pack_b.hip", "gemm.hip"]
+SOURCES = ["quant.hip", "rmsnorm_quant.hip", "pack_b.hip", "gemm.hip", "nvfp4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,0 +1,254 @@
+// grouped_gemm_nvfp4: the NVFP4 block-scaled GEMM of kernelbot nvfp4-group-gemm,
+// submission 496271 (module docstring, constants block, ``nvfp4_gemm_kernel``,
+// ``custom_kernel``): C = A B^T for a list of problems with their own (m, n, k, l),
+// E2M1 elements on both sides with one E4M3 scale per 16 along K, fp32
+// accumulation, float16 C. One launch covers every problem's output tiles.
+//
+// The gfx950 scaled matrix instructions take one power-of-two (E8M0) scale per
+// lane's 32-element chunk, and their fp4 conversions likewise use only the
+// exponent of the scale they are given; an E4M3 scale has three mantissa bits
+// and covers 16 elements. An E2M1 value (2 significant bits) times an E4M3 scale
+// (4 significant bits) has at most 6 significant bits and lies in [2^-10, 2688],
+// so it is exact in bf16. Each workgroup therefore expands its operand tiles to
+// bf16 in LDS, exactly, and runs the dense bf16 32x32x16 instruction: the sum
+// is then that of the exact products, in fp32.
+//
+// Workgroup: 256 threads own a 128 x 128 tile of C; a K step is 64. Thread t
+// expands 32 elements of row t/2 (K half t%2) of each operand per step: two
+// 8-byte code loads, two 1-byte scale loads, 16 unpack instructions (two fp4 to
+// two fp32 each), 32 multiplies, 16 byte permutes (the products are exact, so
+// their top halves are the bf16 values). Wave w computes rows 64(w/2).. and
+// columns 64(w%2).. as 2 x 2 32x32 accumulators. LDS holds two bf16 tiles per
+// operand (double buffer), rows padded to 144 bytes so that the 16-byte operand
+// reads of 8 consecutive rows cover all banks once.
+#include "host_common.hpp"
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kNvBM = 128, kNvBN = 128, kNvBK = 64, kNvThreads = 256;
+constexpr int kNvRow = kNvBK + 8;        // bf16 per LDS row: 64 + 8 padding (144 bytes)
+constexpr int kNvTile = kNvBM * kNvRow;  // bf16 per operand tile (kNvBM == kNvBN)
+
+struct NvProblem {
+  const uint8_t* Aq;  // codes [M, K/2], row stride lda bytes
+  const uint8_t* As;  // E4M3 [M, K/16], row stride ldas bytes
+  const uint8_t* Bq;
+  const uint8_t* Bs;
+  uint16_t* C;  // fp16 [M, N], row stride ldc elements
+  int64_t lda, ldas, ldb, ldbs, ldc;
+  int M, N, K, pad_;
+};
+struct NvArgs {
+  NvProblem p[MXFP4_MAX_GROUPS];
+  int tile_start[MXFP4_MAX_GROUPS + 1];
+  int P;
+};
+
+// Buffer resource over [base, base + bytes): loads past the end read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t nv_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// E4M3 byte -> fp32 (OCP 8-bit floating point, E4M3: bias 7, subnormals m/8 * 2^-6,
+// S.1111.111 is NaN).
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  float v = e ? __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+  if (e == 15u && m == 7u) v = __builtin_nanf("");
+  return (b & 0x80u) ? -v : v;
+}
+
+// One operand row piece of a K step: 32 elements (16 code bytes, loaded as two
+// 8-byte halves so that rows need only 8-byte alignment) and their two scale
+// bytes (loaded one by one: scale rows need no alignment).
+struct Piece {
+  u32x2 q0, q1;
+  uint32_t s0, s1;
+};
+
+__device__ __forceinline__ Piece load_piece(__amdgpu_buffer_rsrc_t qr, __amdgpu_buffer_rsrc_t sr, uint32_t row_q,
+                                            uint32_t row_s, int kk) {
+  Piece p;
+  p.q0 = __builtin_amdgcn_raw_buffer_load_b64(qr, row_q + (uint32_t)(kk / 2), 0, 0);
+  p.q1 = __builtin_amdgcn_raw_buffer_load_b64(qr, row_q + (uint32_t)(kk / 2) + 8u, 0, 0);
+  p.s0 = __builtin_amdgcn_raw_buffer_load_b8(sr, row_s + (uint32_t)(kk / 16), 0, 0);
+  p.s1 = __builtin_amdgcn_raw_buffer_load_b8(sr, row_s + (uint32_t)(kk / 16) + 1u, 0, 0);
+  return p;
+}
+
+// Expands one piece to 32 bf16 in LDS at dst (16-byte aligned). Blocks at or past
+// K get scale 0: their products are zero whatever bytes the loads returned.
+__device__ __forceinline__ void expand_piece(const Piece& p, int kk, int K, __bf16* dst) {
+  const float f0 = kk < K ? e4m3_to_f32(p.s0 & 0xffu) : 0.0f;
+  const float f1 = kk + 16 < K ? e4m3_to_f32(p.s1 & 0xffu) : 0.0f;
+  const uint32_t qw[4] = {p.q0.x, p.q0.y, p.q1.x, p.q1.y};
+  uint32_t out[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float sc = i < 2 ? f0 : f1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f32x2 v;
+      switch (j) {  // the byte select must be a constant
+        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw[i], 1.0f, 0); break;
+        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw[i], 1.0f, 1); break;
+        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw[i], 1.0f, 2); break;
+        default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw[i], 1.0f, 3); break;
+      }
+      const uint32_t lo = __builtin_bit_cast(uint32_t, v.x * sc), hi = __builtin_bit_cast(uint32_t, v.y * sc);
+      out[4 * i + j] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // top halves: exact bf16 pair, low first
+    }
+  }
+  u32x4* d = reinterpret_cast<u32x4*>(dst);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) d[c] = u32x4{out[4 * c], out[4 * c + 1], out[4 * c + 2], out[4 * c + 3]};
+}
+
+__global__ __launch_bounds__(kNvThreads) void gemm_nvfp4_kernel(NvArgs a) {
+  __shared__ __align__(16) __bf16 sA[2][kNvTile];
+  __shared__ __align__(16) __bf16 sB[2][kNvTile];
+
+  int g = 0;
+  while (g + 1 < a.P && a.tile_start[g + 1] <= (int)blockIdx.x) ++g;
+  const NvProblem& q = a.p[g];
+  const int local = (int)blockIdx.x - a.tile_start[g];
+  const int ntn = (q.N + kNvBN - 1) / kNvBN;
+  const int m0 = (local / ntn) * kNvBM, n0 = (local % ntn) * kNvBN;
+
+  const int tid = threadIdx.x, l = tid & 63, wave = tid >> 6;
+  const int prow = tid >> 1, ph = tid & 1;  // this thread's piece: row and K half
+  // Rows past M (N) start past the end of the resource and read zeros, and so
+  // do the last row's loads past K (K/2 is a whole number of 8-byte loads).
+  const __amdgpu_buffer_rsrc_t aq = nv_rsrc(q.Aq, (int64_t)(q.M - 1) * q.lda + q.K / 2);
+  const __amdgpu_buffer_rsrc_t as = nv_rsrc(q.As, (int64_t)(q.M - 1) * q.ldas + q.K / 16);
+  const __amdgpu_buffer_rsrc_t bq = nv_rsrc(q.Bq, (int64_t)(q.N - 1) * q.ldb + q.K / 2);
+  const __amdgpu_buffer_rsrc_t bs = nv_rsrc(q.Bs, (int64_t)(q.N - 1) * q.ldbs + q.K / 16);
+  const uint32_t arq = (uint32_t)((m0 + prow) * q.lda), ars = (uint32_t)((m0 + prow) * q.ldas);
+  const uint32_t brq = (uint32_t)((n0 + prow) * q.ldb), brs = (uint32_t)((n0 + prow) * q.ldbs);
+  const int KT = (q.K + kNvBK - 1) / kNvBK;
+  const int dst = prow * kNvRow + 32 * ph;
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  {
+    const int kk = 32 * ph;
+    const Piece pa = load_piece(aq, as, arq, ars, kk), pb = load_piece(bq, bs, brq, brs, kk);
+    expand_piece(pa, kk, q.K, &sA[0][dst]);
+    expand_piece(pb, kk, q.K, &sB[0][dst]);
+  }
+  __syncthreads();
+
+  const int wm = 64 * (wave >> 1), wn = 64 * (wave & 1);
+  const int orow = (l & 31) * kNvRow + 8 * (l >> 5);  // operand element of this lane within a 32-row block
+  for (int j = 0; j < KT; ++j) {
+    // Next step's pieces, issued before this step's matrix work (the last step
+    // reloads itself: every load is unconditional, so none waits at issue).
+    const int kn = kNvBK * min(j + 1, KT - 1) + 32 * ph;
+    const Piece pa = load_piece(aq, as, arq, ars, kn), pb = load_piece(bq, bs, brq, brs, kn);
+
+    const __bf16* A = sA[j & 1];
+    const __bf16* B = sB[j & 1];
+#pragma unroll
+    for (int ks = 0; ks < kNvBK / 16; ++ks) {
+      bf16x8 fa[2], fb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        fa[i] = *reinterpret_cast<const bf16x8*>(&A[(wm + 32 * i) * kNvRow + orow + 16 * ks]);
+        fb[i] = *reinterpret_cast<const bf16x8*>(&B[(wn + 32 * i) * kNvRow + orow + 16 * ks]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
+    }
+    // The other buffer was last read in step j-1, before the barrier that ended it.
+    expand_piece(pa, kn, q.K, &sA[(j + 1) & 1][dst]);
+    expand_piece(pb, kn, q.K, &sB[(j + 1) & 1][dst]);
+    __syncthreads();
+  }
+
+  // acc[i][jj] register r of lane l: row 8(r/4) + 4(l/32) + r%4, column l%32 of its 32x32 block.
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int col = n0 + wn + 32 * jj + (l & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm + 32 * i + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        if (row < q.M && col < q.N)
+          q.C[(int64_t)row * q.ldc + col] = __builtin_bit_cast(uint16_t, (_Float16)acc[i][jj][r]);
+      }
+    }
+}
+
+}  // namespace
+
+extern "C" int grouped_gemm_nvfp4(const nvfp4_group* groups, int G, void* stream) {
+  if (!groups) return MXFP4_ERR_NULL;
+  if (G < 1) return MXFP4_ERR_TOO_MANY_GROUPS;
+  NvArgs a{};
+  int P = 0;
+  int64_t total = 0;
+  const int64_t lim = (int64_t)1 << 31;  // 32-bit buffer offsets, with a tile of rows to spare
+  for (int g = 0; g < G; ++g) {
+    const nvfp4_group& q = groups[g];
+    if (!q.Aq || !q.As || !q.Bq || !q.Bs || !q.C) return MXFP4_ERR_NULL;
+    if (q.M < 1 || q.N < 1 || q.K < 16 || q.K % 16 != 0 || q.M > mxh::kMaxDim || q.N > mxh::kMaxDim ||
+        q.K > mxh::kMaxDim || q.L < 1)
+      return MXFP4_ERR_SHAPE;
+    if (q.lda < q.K / 2 || q.ldas < q.K / 16 || q.ldb < q.K / 2 || q.ldbs < q.K / 16 || q.ldc < q.N)
+      return MXFP4_ERR_SHAPE;
+    if ((q.M + kNvBM) * q.lda >= lim || (q.M + kNvBM) * q.ldas >= lim || (q.N + kNvBN) * q.ldb >= lim ||
+        (q.N + kNvBN) * q.ldbs >= lim)
+      return MXFP4_ERR_SHAPE;
+    if (!mxh::aligned(q.Aq, 8) || !mxh::aligned(q.Bq, 8) || q.lda % 8 != 0 || q.ldb % 8 != 0 ||
+        !mxh::aligned(q.C, 2))
+      return MXFP4_ERR_ALIGN;
+    if (q.L > MXFP4_MAX_GROUPS - P) return MXFP4_ERR_TOO_MANY_GROUPS;
+    if (q.L > 1) {  // batches: C slices must not overlap; every slice keeps the alignment rules
+      if (q.strideA < 0 || q.strideAs < 0 || q.strideB < 0 || q.strideBs < 0 || q.strideC < q.M * q.ldc)
+        return MXFP4_ERR_SHAPE;
+      if (q.strideA % 8 != 0 || q.strideB % 8 != 0) return MXFP4_ERR_ALIGN;
+    }
+    const int64_t tiles = mxh::cdiv(q.M, kNvBM) * mxh::cdiv(q.N, kNvBN);
+    for (int64_t l = 0; l < q.L; ++l) {
+      NvProblem& o = a.p[P];
+      o.Aq = (const uint8_t*)q.Aq + l * q.strideA;
+      o.As = (const uint8_t*)q.As + l * q.strideAs;
+      o.Bq = (const uint8_t*)q.Bq + l * q.strideB;
+      o.Bs = (const uint8_t*)q.Bs + l * q.strideBs;
+      o.C = (uint16_t*)q.C + l * q.strideC;
+      o.lda = q.lda;
+      o.ldas = q.ldas;
+      o.ldb = q.ldb;
+      o.ldbs = q.ldbs;
+      o.ldc = q.ldc;
+      o.M = (int)q.M;
+      o.N = (int)q.N;
+      o.K = (int)q.K;
+      a.tile_start[P] = (int)total;
+      total += tiles;
+      if (total > INT32_MAX) return MXFP4_ERR_SHAPE;
+      ++P;
+    }
+  }
+  a.tile_start[P] = (int)total;
+  a.P = P;
+  void* args[] = {&a};
+  return mxh::launch_status(hipLaunchKernel((const void*)gemm_nvfp4_kernel, dim3((unsigned)total),
+                                            dim3(kNvThreads), args, 0, (hipStream_t)stream));
+}

@@ -22,7 +22,7 @@ STATUS = {0: "MXFP4_OK", 1: "MXFP4_ERR_NULL", 2: "MXFP4_ERR_SHAPE", 3: "MXFP4_ER
           5: "MXFP4_ERR_TOO_MANY_GROUPS", 6: "MXFP4_ERR_HIP", 7: "MXFP4_ERR_BUFFER", 8: "MXFP4_ERR_ARG"}
 EXPORTED = ["mxfp4_status_str", "mxfp4_quant", "mxfp4_rmsnorm_quant", "mxfp4_pack_B_bytes", "mxfp4_pack_B", "gemm_a4w4_workspace_bytes",
             "gemm_a4w4_fused", "gemm_a4w4", "grouped_gemm_a4w4_workspace_bytes", "grouped_gemm_a4w4",
-            "grouped_gemm_a4w4_mnk"]
+            "grouped_gemm_a4w4_mnk", "grouped_gemm_nvfp4"]
 
 
 class Mxfp4Error(RuntimeError):
@@ -37,6 +37,16 @@ class GroupMnk(ctypes.Structure):
                 ("Bp", ctypes.c_void_p), ("strideB", ctypes.c_int64), ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64),
                 ("strideC", ctypes.c_int64), ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64),
                 ("L", ctypes.c_int64)]
+
+
+class GroupNv(ctypes.Structure):
+    """mirror of nvfp4_group"""
+    _fields_ = [("Aq", ctypes.c_void_p), ("lda", ctypes.c_int64), ("strideA", ctypes.c_int64),
+                ("As", ctypes.c_void_p), ("ldas", ctypes.c_int64), ("strideAs", ctypes.c_int64),
+                ("Bq", ctypes.c_void_p), ("ldb", ctypes.c_int64), ("strideB", ctypes.c_int64),
+                ("Bs", ctypes.c_void_p), ("ldbs", ctypes.c_int64), ("strideBs", ctypes.c_int64),
+                ("C", ctypes.c_void_p), ("ldc", ctypes.c_int64), ("strideC", ctypes.c_int64),
+                ("M", ctypes.c_int64), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("L", ctypes.c_int64)]
 
 
 class Group(ctypes.Structure):
@@ -74,6 +84,7 @@ def lib() -> ctypes.CDLL:
         L.grouped_gemm_a4w4.restype = i32
         L.grouped_gemm_a4w4_mnk.argtypes = [ctypes.POINTER(GroupMnk), i32, vp]
         L.grouped_gemm_a4w4_mnk.restype = i32
+        L.grouped_gemm_nvfp4.argtypes, L.grouped_gemm_nvfp4.restype = [ctypes.POINTER(GroupNv), i32, vp], i32
         _lib = L
         return L
 
@@ -260,4 +271,43 @@ def grouped_gemm_mnk(problems, out_list=None):
         outs.append(C3 if batched else C3[0])
     arr = (GroupMnk * len(descs))(*descs)
     _check(lib().grouped_gemm_a4w4_mnk(arr, len(descs), _stream(problems[0][0])), "grouped_gemm_a4w4_mnk")
+    return outs if out_list is None else out_list
+
+
+def grouped_gemm_nvfp4(problems, out_list=None):
+    """NVFP4 groups with their own (M, N, K) and a batch count, in one launch.
+
+    problems: list of (aq, a_scale, bq, b_scale): uint8 tensors aq [L, M, K/2]
+    (E2M1 codes, low nibble first), a_scale [L, M, K/16] (E4M3), bq [L, N, K/2],
+    b_scale [L, N, K/16]; 2-D for L = 1. Rows may be padded (unit stride along
+    K). Returns (or fills `out_list` with) float16 C tensors [L, M, N] ([M, N]
+    for L = 1).
+    """
+    def as3(t, name):
+        t3 = t if t.dim() == 3 else t.unsqueeze(0)
+        if not t3.is_cuda or t3.dtype != torch.uint8 or t3.stride(2) != 1:
+            raise ValueError(f"{name} must be a uint8 CUDA tensor with unit stride along K")
+        return t3
+
+    descs, outs = [], []
+    for gi, (aq, a_s, bq, b_s) in enumerate(problems):
+        batched = aq.dim() == 3
+        A, As, B, Bs = as3(aq, "aq"), as3(a_s, "a_scale"), as3(bq, "bq"), as3(b_s, "b_scale")
+        L, M, KH = A.shape
+        N, K = B.shape[1], 2 * KH
+        if B.shape != (L, N, KH) or As.shape != (L, M, K // 16) or Bs.shape != (L, N, K // 16):
+            raise ValueError("aq [L, M, K/2], a_scale [L, M, K/16], bq [L, N, K/2], b_scale [L, N, K/16] must agree")
+        if out_list is None:
+            C3 = torch.empty((L, M, N), dtype=torch.float16, device=aq.device)
+        else:
+            C = out_list[gi]
+            C3 = C if C.dim() == 3 else C.unsqueeze(0)
+            if C3.shape != (L, M, N) or C3.dtype != torch.float16 or C3.stride(2) != 1:
+                raise ValueError("out_list[i] must be float16 [L, M, N]")
+        descs.append(GroupNv(A.data_ptr(), A.stride(1), A.stride(0), As.data_ptr(), As.stride(1), As.stride(0),
+                             B.data_ptr(), B.stride(1), B.stride(0), Bs.data_ptr(), Bs.stride(1), Bs.stride(0),
+                             C3.data_ptr(), C3.stride(1), C3.stride(0), M, N, K, L))
+        outs.append(C3 if batched else C3[0])
+    arr = (GroupNv * len(descs))(*descs)
+    _check(lib().grouped_gemm_nvfp4(arr, len(descs), _stream(problems[0][0])), "grouped_gemm_nvfp4")
     return outs if out_list is None else out_list

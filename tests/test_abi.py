@@ -201,3 +201,36 @@ def test_grouped_mnk_rejects_empty_list():
     assert ops.lib().grouped_gemm_a4w4_mnk(None, 1, None) == 1
     arr = (ops.GroupMnk * 1)(_mnk())
     assert ops.lib().grouped_gemm_a4w4_mnk(arr, 0, None) == 5
+
+
+def _nv(**kw):
+    d = dict(Aq=P, lda=256, strideA=0, As=P, ldas=32, strideAs=0, Bq=P, ldb=256, strideB=0, Bs=P, ldbs=32,
+             strideBs=0, C=P, ldc=64, strideC=0, M=16, N=64, K=512, L=1)
+    d.update(kw)
+    return ops.GroupNv(*(d[f] for f, _ in ops.GroupNv._fields_))
+
+
+@pytest.mark.parametrize("groups,status", [
+    ([_nv(Aq=None)], 1), ([_nv(As=None)], 1), ([_nv(Bs=None)], 1), ([_nv(C=None)], 1),
+    ([_nv(L=0)], 2), ([_nv(K=40)], 2), ([_nv(K=0)], 2), ([_nv(M=0)], 2), ([_nv(N=0)], 2),
+    ([_nv(lda=240)], 2), ([_nv(ldas=30)], 2), ([_nv(ldb=128)], 2), ([_nv(ldbs=16)], 2), ([_nv(ldc=63)], 2),
+    ([_nv(M=1 << 24, lda=1 << 8)], 2),  # (M + 128) * lda reaches 2^31
+    ([_nv(Aq=P + 4)], 3), ([_nv(Bq=P + 12)], 3), ([_nv(lda=260)], 3), ([_nv(ldb=258)], 3), ([_nv(C=P + 1)], 3),
+    # batches: C slices must not overlap; strides keep alignment
+    ([_nv(L=2, strideA=4096, strideAs=512, strideB=16384, strideBs=2048, strideC=16 * 64 - 1)], 2),
+    ([_nv(L=2, strideA=-16, strideAs=512, strideB=16384, strideBs=2048, strideC=16 * 64)], 2),
+    ([_nv(L=2, strideA=4100, strideAs=512, strideB=16384, strideBs=2048, strideC=16 * 64)], 3),
+    ([_nv(L=2, strideA=4096, strideAs=512, strideB=16386, strideBs=2048, strideC=16 * 64)], 3),
+    # at most 32 problems in all
+    ([_nv(L=20, strideA=4096, strideAs=512, strideB=16384, strideBs=2048, strideC=1024),
+      _nv(L=13, strideA=4096, strideAs=512, strideB=16384, strideBs=2048, strideC=1024)], 5),
+])
+def test_grouped_nvfp4_validation(groups, status):
+    arr = (ops.GroupNv * len(groups))(*groups)
+    assert ops.lib().grouped_gemm_nvfp4(arr, len(groups), None) == status
+
+
+def test_grouped_nvfp4_rejects_empty_list():
+    assert ops.lib().grouped_gemm_nvfp4(None, 1, None) == 1
+    arr = (ops.GroupNv * 1)(_nv())
+    assert ops.lib().grouped_gemm_nvfp4(arr, 0, None) == 5

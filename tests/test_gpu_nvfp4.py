@@ -1,0 +1,135 @@
+"""Parity of grouped_gemm_nvfp4 (page 496271's NVFP4 block-scaled group GEMM:
+E2M1 with one E4M3 scale per 16 along K, float16 C) with the CPU oracle, on an MI355X.
+
+Each C must be within |C - C_ref| <= 2^-7 |C_ref| + 1e-3 max|C_ref| of the
+oracle's fp64 product of the dequantised operands rounded to float16, over the
+finite entries; infinities and NaNs must sit at the same places with the same
+sign. The kernel's products are exact (bf16 holds E2M1 x E4M3 exactly), so the
+only differences are fp32 accumulation and the one float16 rounding.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp4_block_scaled_02_amd import ops, synth
+from tests.helpers import to_dev_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def f16_of(t):
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def assert_nv_tolerance(c_bits, ref_bits, what):
+    c = oracle.nvfp4.f16_bits_to_f64(c_bits)
+    r = oracle.nvfp4.f16_bits_to_f64(ref_bits)
+    fin = np.isfinite(r)
+    assert np.array_equal(np.isnan(c), np.isnan(r)), f"{what}: NaN positions differ"
+    assert np.array_equal(c[np.isinf(r)], r[np.isinf(r)]), f"{what}: infinities differ"
+    assert np.isfinite(c[fin]).all(), f"{what}: non-finite where the oracle is finite"
+    if fin.any():
+        tol = 2.0 ** -7 * np.abs(r[fin]) + 1e-3 * np.abs(r[fin]).max()
+        bad = ~(np.abs(c[fin] - r[fin]) <= tol)
+        assert not bad.any(), f"{what}: {int(bad.sum())} of {bad.size} outside tolerance"
+
+
+def run_one(aq, as_, bq, bs):
+    (c,) = ops.grouped_gemm_nvfp4([(to_dev_u8(aq), to_dev_u8(as_), to_dev_u8(bq), to_dev_u8(bs))])
+    torch.cuda.synchronize()
+    return f16_of(c)
+
+
+SHAPES = [(1, 1, 16), (5, 37, 48), (128, 128, 64), (130, 257, 1040), (300, 200, 4096), (64, 2112, 7168),
+          (1024, 1024, 2048), (17, 129, 16)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_shapes_match_oracle(M, N, K):
+    say(f"[nvfp4] M={M} N={N} K={K}")
+    aq, as_ = synth.make_nvfp4(M, K, 41, (M, K))
+    bq, bs = synth.make_nvfp4(N, K, 42, (N, K))
+    assert_nv_tolerance(run_one(aq, as_, bq, bs), oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs), f"M={M} N={N} K={K}")
+
+
+def test_special_scales():
+    """Subnormal, negative and zero scales, the smallest and largest normal ones."""
+    say("[nvfp4] special scales")
+    M, N, K = 40, 72, 256
+    aq, as_ = synth.make_nvfp4(M, K, 43)
+    bq, bs = synth.make_nvfp4(N, K, 44)
+    g = np.random.default_rng(5)
+    special = np.array([0x01, 0x07, 0x08, 0x00, 0x80, 0xB8, 0xC3, 0x7E, 0x09], dtype=np.uint8)
+    as_.reshape(-1)[g.choice(as_.size, 200, replace=False)] = g.choice(special, 200)
+    bs.reshape(-1)[g.choice(bs.size, 300, replace=False)] = g.choice(special, 300)
+    assert_nv_tolerance(run_one(aq, as_, bq, bs), oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs), "special scales")
+
+
+def test_overflow_and_nan():
+    """Sums past the float16 range give infinities; a NaN scale makes its rows NaN."""
+    say("[nvfp4] overflow and NaN")
+    M, N, K = 8, 40, 64
+    aq = np.full((M, K // 2), 0x77, dtype=np.uint8)  # every element +6
+    bq = np.full((N, K // 2), 0x77, dtype=np.uint8)
+    bq[1::2] = 0xFF  # odd rows of B: every element -6
+    as_ = np.full((M, K // 16), 0x7E, dtype=np.uint8)  # 448
+    bs = np.full((N, K // 16), 0x7E, dtype=np.uint8)
+    as_[3, 2] = 0x7F  # NaN scale: row 3 of C is NaN
+    ref = oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs)
+    assert np.isinf(oracle.nvfp4.f16_bits_to_f64(ref)).sum() == (M - 1) * N
+    assert_nv_tolerance(run_one(aq, as_, bq, bs), ref, "overflow and NaN")
+
+
+def test_padded_rows_and_guard_band():
+    """Row strides past K/2, K/16 and N; bytes past K hold 0xFF codes and NaN scales,
+    which must be ignored, and C's padding must stay untouched."""
+    say("[nvfp4] padded rows")
+    M, N, K = 70, 150, 272  # K % 64 == 16: the last step holds one block
+    aq, as_ = synth.make_nvfp4(M, K, 45)
+    bq, bs = synth.make_nvfp4(N, K, 46)
+    lda, ldas, ldb, ldbs, ldc = K // 2 + 24, K // 16 + 5, K // 2 + 8, K // 16 + 2, N + 9
+
+    def pad(x, ld, fill):
+        out = np.full((x.shape[0], ld), fill, dtype=np.uint8)
+        out[:, :x.shape[1]] = x
+        return to_dev_u8(out)[:, :x.shape[1]]
+
+    A, As = pad(aq, lda, 0xFF), pad(as_, ldas, 0x7F)
+    B, Bs = pad(bq, ldb, 0xFF), pad(bs, ldbs, 0x7F)
+    C = torch.full((M, ldc), 12345, dtype=torch.int16, device="cuda").view(torch.float16)
+    ops.grouped_gemm_nvfp4([(A, As, B, Bs)], out_list=[C[:, :N]])
+    torch.cuda.synchronize()
+    got = f16_of(C)
+    assert (got[:, N:] == 12345).all(), "C padding written"
+    assert_nv_tolerance(got[:, :N], oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs), "padded rows")
+
+
+def test_groups_and_batches_one_launch():
+    say("[nvfp4] groups and batches")
+    shapes = [(100, 300, 512, 2), (257, 1024, 2048, 1), (48, 96, 1056, 3), (1, 32, 64, 2), (130, 520, 4096, 1)]
+    host, dev = [], []
+    for gi, (M, N, K, L) in enumerate(shapes):
+        ops_ = [synth.make_nvfp4(M, K, 47, (gi, l)) + synth.make_nvfp4(N, K, 48, (gi, l)) for l in range(L)]
+        host.append(ops_)
+        dev.append(tuple(torch.stack([to_dev_u8(o[i]) for o in ops_]) for i in range(4)))
+    outs = ops.grouped_gemm_nvfp4(dev)
+    torch.cuda.synchronize()
+    for gi, ((M, N, K, L), ops_, c) in enumerate(zip(shapes, host, outs)):
+        assert c.shape == (L, M, N)
+        for l in range(L):
+            aq, as_, bq, bs = ops_[l]
+            assert_nv_tolerance(f16_of(c[l]), oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs), f"group {gi} batch {l}")
+
+
+def test_repeat_identical():
+    say("[nvfp4] repeat")
+    aq, as_ = synth.make_nvfp4(300, 2048, 49)
+    bq, bs = synth.make_nvfp4(500, 2048, 50)
+    first = run_one(aq, as_, bq, bs)
+    for _ in range(3):
+        assert np.array_equal(run_one(aq, as_, bq, bs), first)
