@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 FP4_PEAK_TFLOPS = 10100.0   # MI355X dense MXFP4 matrix peak, TFLOP/s
+BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, TFLOP/s (the NVFP4 path's instruction)
 METRIC = "µs/call, TFLOP/s and HBM GB/s (% of peak) for quant+a4w4 GEMM, M=16..4096"
 ROTATE_BYTES = 512 << 20
 PROFILES = os.path.join(ROOT, "profiles")
@@ -55,7 +56,8 @@ def parse():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--workload", default="skinny",
-                   choices=["tiny", "skinny", "stress", "square", "grouped", "rmsnorm", "grouped_mnk", "skinny_shard8"],
+                   choices=["tiny", "skinny", "stress", "square", "grouped", "rmsnorm", "grouped_mnk", "skinny_shard8",
+                            "nvfp4_grouped"],
                    help="rmsnorm times mxfp4_rmsnorm_quant (RMSNorm fused with MXFP4 quantisation) at M4096 K7168; "
                         "grouped_mnk times grouped_gemm_a4w4_mnk on seeded groups with their own (M, N, K, L)")
     p.add_argument("--seed", type=int, default=None)
@@ -392,6 +394,110 @@ def bench_grouped_mnk(args):
     print(json.dumps(out), flush=True)
 
 
+NV_METRIC = "µs/call and TFLOP/s (% of peak) for the NVFP4 group GEMM (E2M1, E4M3 per 16), per-group (M, N, K, L)"
+
+
+def nv_bytes(M, N, K):
+    """Algorithmic bytes of one NVFP4 problem: codes and scales of A and B read once, fp16 C written once."""
+    return (M + N) * (K // 2 + K // 16) + 2 * M * N
+
+
+def bench_nvfp4(args):
+    """One grouped_gemm_nvfp4 call per step over rotated (cold) operand sets; the group
+    shapes are those of the grouped_mnk workload (same seed)."""
+    import torch
+    from mxfp4_block_scaled_02_amd import ops, synth
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    seed = 102 if args.seed is None else args.seed
+    shapes = mnk_problems(seed)
+    log(f"[bench] workload=nvfp4_grouped seed={seed}: {shapes}")
+    u8 = lambda x: torch.from_numpy(np.ascontiguousarray(x)).to(dev)  # noqa: E731
+    base = []
+    for gi, (M, N, K, L) in enumerate(shapes):
+        ops_ = [synth.make_nvfp4(M, K, seed, (gi, l)) + synth.make_nvfp4(N, K, seed, (gi, 100 + l)) for l in range(L)]
+        base.append(tuple(torch.stack([u8(o[i]) for o in ops_]) for i in range(4)))
+    flops = sum(L * alg_flops(M, N, K) for M, N, K, L in shapes)
+    nbytes = sum(L * nv_bytes(M, N, K) for M, N, K, L in shapes)
+    set_bytes = sum(sum(t.numel() for t in b) for b in base) + sum(L * 2 * M * N for M, N, K, L in shapes)
+    R = 1 if args.warm_cache else max(1, math.ceil(ROTATE_BYTES / set_bytes))
+    R = min(R, args.steps)
+    sets = []
+    for r in range(R):
+        probs = [tuple(t.clone() if r else t for t in b) for b in base]
+        outs = [torch.empty((L, M, N), dtype=torch.float16, device=dev) for M, N, K, L in shapes]
+        sets.append((probs, outs))
+
+    def step(i):
+        probs, outs = sets[i % R]
+        ops.grouped_gemm_nvfp4(probs, out_list=outs)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if args.no_graph:
+        runner = lambda: [step(i) for i in range(args.steps)]  # noqa: E731
+    else:
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for i in range(args.steps):
+                step(i)
+        torch.cuda.synchronize()
+        gr.replay()
+        torch.cuda.synchronize()
+        runner = gr.replay
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    runner()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    tflops = flops / (ms_step * 1e-3) / 1e12
+    gbs = nbytes / (ms_step * 1e-3) / 1e9
+    if flops / (BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
+        bound, achieved, peak, unit = "mfma", tflops, BF16_PEAK_TFLOPS, "TFLOP/s"
+    else:
+        bound, achieved, peak, unit = "hbm", gbs, HBM_PEAK_GBS, "GB/s"
+    out = dict(metric=NV_METRIC, value=round(achieved, 3), unit=unit, n_gpus=1, steps=args.steps,
+               warmup=args.warmup, ms_per_step=round(ms_step, 6), higher_is_better=True, scaling="weak",
+               vs_baseline=None, dtype="nvfp4 (e2m1 x e4m3 per 16; exact bf16 products, fp32 accumulate, fp16 out)",
+               data="synthetic",
+               config=dict(workload="nvfp4_grouped", seed=seed, groups=[dict(M=M, N=N, K=K, L=L) for M, N, K, L in shapes],
+                           cache="warm (1 set)" if R == 1 else f"cold ({R} rotated operand sets)",
+                           timing="hip graph replay" if not args.no_graph else "eager launch loop",
+                           path="grouped_gemm_nvfp4"),
+               us_per_call=round(ms_step * 1e3, 3), tflops=round(tflops, 3), hbm_gbs=round(gbs, 2),
+               roofline=dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
+                             frac=round(achieved / peak, 4), traffic=None, algorithmic_bytes=nbytes,
+                             algorithmic_flops=flops))
+    if not args.no_cpu_baseline:
+        import oracle
+        M, N, K, L = shapes[0]
+        aq, as_ = synth.make_nvfp4(M, K, seed, (0, 0))
+        bq, bs = synth.make_nvfp4(N, K, seed, (0, 100))
+        rows = min(M, 64)
+        times, t_end = [], time.perf_counter() + 12.0
+        while True:
+            t0 = time.perf_counter()
+            oracle.nvfp4.nvfp4_gemm_ref(aq[:rows], as_[:rows], bq, bs)
+            times.append(time.perf_counter() - t0)
+            if time.perf_counter() > t_end or len(times) >= 200:
+                break
+        t = float(np.median(times))
+        val = alg_flops(rows, N, K) / t / 1e12 if unit == "TFLOP/s" else nv_bytes(rows, N, K) / t / 1e9
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            threads = 1
+        out["cpu_baseline"] = dict(value=round(val, 6), unit=unit, cores=int(threads), kind="oracle",
+                                   sample=f"oracle nvfp4_gemm_ref on rows 0..{rows - 1} of the first problem "
+                                          f"(N={N}, K={K}); median of {len(times)} runs, {t * 1e3:.1f} ms each")
+    print(json.dumps(out), flush=True)
+
+
 def copy_calibration():
     import torch
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -425,6 +531,9 @@ def main():
         return
     if args.workload == "grouped_mnk":
         bench_grouped_mnk(args)
+        return
+    if args.workload == "nvfp4_grouped":
+        bench_nvfp4(args)
         return
     import torch
     from mxfp4_block_scaled_02_amd import ops, synth

@@ -8,32 +8,34 @@
 // lane's 32-element chunk, and their fp4 conversions likewise use only the
 // exponent of the scale they are given; an E4M3 scale has three mantissa bits
 // and covers 16 elements. An E2M1 value (2 significant bits) times an E4M3 scale
-// (4 significant bits) has at most 6 significant bits and lies in [2^-10, 2688],
-// so it is exact in bf16. Each workgroup therefore expands its operand tiles to
-// bf16 in LDS, exactly, and runs the dense bf16 32x32x16 instruction: the sum
-// is then that of the exact products, in fp32.
+// (4 significant bits) has at most 6 significant bits and lies in [2^-10, 2880]
+// in magnitude (or is zero), so it is exact in fp16, normal. Each workgroup
+// therefore expands its operand tiles to fp16 in LDS, exactly, and runs the
+// dense fp16 32x32x16 instruction: the sum is then that of the exact products,
+// in fp32.
 //
 // Workgroup: 256 threads own a 128 x 128 tile of C; a K step is 64. Thread t
 // expands 32 elements of row t/2 (K half t%2) of each operand per step: two
-// 8-byte code loads, two 1-byte scale loads, 16 unpack instructions (two fp4 to
-// two fp32 each), 32 multiplies, 16 byte permutes (the products are exact, so
-// their top halves are the bf16 values). Wave w computes rows 64(w/2).. and
-// columns 64(w%2).. as 2 x 2 32x32 accumulators. LDS holds two bf16 tiles per
-// operand (double buffer), rows padded to 144 bytes so that the 16-byte operand
-// reads of 8 consecutive rows cover all banks once.
+// 8-byte code loads, two 1-byte scale loads, then per pair of elements one
+// convert (two fp4 to two fp16, times the scale's power of two, exact) and one
+// packed fp16 multiply by the scale's significand (exact). Wave w computes rows
+// 64(w/2).. and columns 64(w%2).. as 2 x 2 32x32 accumulators. LDS holds two
+// fp16 tiles per operand (double buffer), rows padded to 144 bytes so that the
+// 16-byte operand reads of 8 consecutive rows cover all banks once.
 #include "host_common.hpp"
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kNvBM = 128, kNvBN = 128, kNvBK = 64, kNvThreads = 256;
-constexpr int kNvRow = kNvBK + 8;        // bf16 per LDS row: 64 + 8 padding (144 bytes)
-constexpr int kNvTile = kNvBM * kNvRow;  // bf16 per operand tile (kNvBM == kNvBN)
+constexpr int kNvRow = kNvBK + 8;        // fp16 per LDS row: 64 + 8 padding (144 bytes)
+constexpr int kNvTile = kNvBM * kNvRow;  // fp16 per operand tile (kNvBM == kNvBN)
+constexpr int kNvDepth = 4;              // K steps of loads in flight (even: the LDS buffer is j & 1)
 
 struct NvProblem {
   const uint8_t* Aq;  // codes [M, K/2], row stride lda bytes
@@ -55,13 +57,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t nv_rsrc(const void* base, int6
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// E4M3 byte -> fp32 (OCP 8-bit floating point, E4M3: bias 7, subnormals m/8 * 2^-6,
-// S.1111.111 is NaN).
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+// E4M3 byte (OCP 8-bit floating point, E4M3: bias 7, subnormals m/8 * 2^-6,
+// S.1111.111 is NaN) as p2 * sig: p2 = 2^(e-7) (2^-6 for e = 0) as an fp32
+// power of two, sig = +-(1 + m/8) (+-m/8 for e = 0) as an fp16 pair, exact.
+struct NvScale {
+  float p2;
+  f16x2 sig;
+};
+__device__ __forceinline__ NvScale e4m3_split(uint32_t b) {
   const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float v = e ? __builtin_bit_cast(float, ((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  if (e == 15u && m == 7u) v = __builtin_nanf("");
-  return (b & 0x80u) ? -v : v;
+  NvScale r;
+  r.p2 = __builtin_bit_cast(float, ((e ? e : 1u) + 120u) << 23);
+  _Float16 g = (_Float16)((float)(e ? 8u + m : m) * 0.125f);
+  if (e == 15u && m == 7u) g = (_Float16)__builtin_nanf("");
+  if (b & 0x80u) g = -g;
+  r.sig = f16x2{g, g};
+  return r;
 }
 
 // One operand row piece of a K step: 32 elements (16 code bytes, loaded as two
@@ -82,27 +93,27 @@ __device__ __forceinline__ Piece load_piece(__amdgpu_buffer_rsrc_t qr, __amdgpu_
   return p;
 }
 
-// Expands one piece to 32 bf16 in LDS at dst (16-byte aligned). Blocks at or past
-// K get scale 0: their products are zero whatever bytes the loads returned.
-__device__ __forceinline__ void expand_piece(const Piece& p, int kk, int K, __bf16* dst) {
-  const float f0 = kk < K ? e4m3_to_f32(p.s0 & 0xffu) : 0.0f;
-  const float f1 = kk + 16 < K ? e4m3_to_f32(p.s1 & 0xffu) : 0.0f;
+// Expands one piece to 32 fp16 in LDS at dst (16-byte aligned). Blocks at or past
+// K get significand 0: their products are zero whatever bytes the loads returned.
+__device__ __forceinline__ void expand_piece(const Piece& p, int kk, int K, _Float16* dst) {
+  NvScale s0 = e4m3_split(p.s0 & 0xffu), s1 = e4m3_split(p.s1 & 0xffu);
+  if (kk >= K) s0.sig = f16x2{(_Float16)0.0f, (_Float16)0.0f};
+  if (kk + 16 >= K) s1.sig = f16x2{(_Float16)0.0f, (_Float16)0.0f};
   const uint32_t qw[4] = {p.q0.x, p.q0.y, p.q1.x, p.q1.y};
   uint32_t out[16];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const float sc = i < 2 ? f0 : f1;
+    const NvScale& sc = i < 2 ? s0 : s1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      f32x2 v;
+      f16x2 v;
       switch (j) {  // the byte select must be a constant
-        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw[i], 1.0f, 0); break;
-        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw[i], 1.0f, 1); break;
-        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw[i], 1.0f, 2); break;
-        default: v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(qw[i], 1.0f, 3); break;
+        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw[i], sc.p2, 0); break;
+        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw[i], sc.p2, 1); break;
+        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw[i], sc.p2, 2); break;
+        default: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw[i], sc.p2, 3); break;
       }
-      const uint32_t lo = __builtin_bit_cast(uint32_t, v.x * sc), hi = __builtin_bit_cast(uint32_t, v.y * sc);
-      out[4 * i + j] = __builtin_amdgcn_perm(hi, lo, 0x07060302u);  // top halves: exact bf16 pair, low first
+      out[4 * i + j] = __builtin_bit_cast(uint32_t, v * sc.sig);  // element 2(4i+j) in the low half
     }
   }
   u32x4* d = reinterpret_cast<u32x4*>(dst);
@@ -111,8 +122,8 @@ __device__ __forceinline__ void expand_piece(const Piece& p, int kk, int K, __bf
 }
 
 __global__ __launch_bounds__(kNvThreads) void gemm_nvfp4_kernel(NvArgs a) {
-  __shared__ __align__(16) __bf16 sA[2][kNvTile];
-  __shared__ __align__(16) __bf16 sB[2][kNvTile];
+  __shared__ __align__(16) _Float16 sA[2][kNvTile];
+  __shared__ __align__(16) _Float16 sB[2][kNvTile];
 
   int g = 0;
   while (g + 1 < a.P && a.tile_start[g + 1] <= (int)blockIdx.x) ++g;
@@ -142,42 +153,57 @@ __global__ __launch_bounds__(kNvThreads) void gemm_nvfp4_kernel(NvArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  {
-    const int kk = 32 * ph;
-    const Piece pa = load_piece(aq, as, arq, ars, kk), pb = load_piece(bq, bs, brq, brs, kk);
-    expand_piece(pa, kk, q.K, &sA[0][dst]);
-    expand_piece(pb, kk, q.K, &sB[0][dst]);
+  // The pieces of the next kNvDepth steps are in flight in a register ring
+  // (slot = step mod kNvDepth): one K step's matrix work is far shorter than a
+  // load's latency. The step count is padded to a multiple of kNvDepth; the
+  // padding steps lie past K, so they expand to zeros (zero scales) and add
+  // nothing, and every load is unconditional (past the end, a load reads zeros).
+  const int KTp = (KT + kNvDepth - 1) / kNvDepth * kNvDepth;
+  Piece ra[kNvDepth], rb[kNvDepth];
+#pragma unroll
+  for (int u = 0; u < kNvDepth; ++u) {
+    const int kk = kNvBK * u + 32 * ph;
+    ra[u] = load_piece(aq, as, arq, ars, kk);
+    rb[u] = load_piece(bq, bs, brq, brs, kk);
   }
+  expand_piece(ra[0], 32 * ph, q.K, &sA[0][dst]);
+  expand_piece(rb[0], 32 * ph, q.K, &sB[0][dst]);
+  ra[0] = load_piece(aq, as, arq, ars, kNvBK * kNvDepth + 32 * ph);
+  rb[0] = load_piece(bq, bs, brq, brs, kNvBK * kNvDepth + 32 * ph);
   __syncthreads();
 
   const int wm = 64 * (wave >> 1), wn = 64 * (wave & 1);
   const int orow = (l & 31) * kNvRow + 8 * (l >> 5);  // operand element of this lane within a 32-row block
-  for (int j = 0; j < KT; ++j) {
-    // Next step's pieces, issued before this step's matrix work (the last step
-    // reloads itself: every load is unconditional, so none waits at issue).
-    const int kn = kNvBK * min(j + 1, KT - 1) + 32 * ph;
-    const Piece pa = load_piece(aq, as, arq, ars, kn), pb = load_piece(bq, bs, brq, brs, kn);
-
-    const __bf16* A = sA[j & 1];
-    const __bf16* B = sB[j & 1];
+  for (int j0 = 0; j0 < KTp; j0 += kNvDepth) {
 #pragma unroll
-    for (int ks = 0; ks < kNvBK / 16; ++ks) {
-      bf16x8 fa[2], fb[2];
+    for (int u = 0; u < kNvDepth; ++u) {
+      const int j = j0 + u;
+      const _Float16* A = sA[u & 1];  // j & 1: kNvDepth is even
+      const _Float16* B = sB[u & 1];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        fa[i] = *reinterpret_cast<const bf16x8*>(&A[(wm + 32 * i) * kNvRow + orow + 16 * ks]);
-        fb[i] = *reinterpret_cast<const bf16x8*>(&B[(wn + 32 * i) * kNvRow + orow + 16 * ks]);
+      for (int ks = 0; ks < kNvBK / 16; ++ks) {
+        f16x8 fa[2], fb[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          fa[i] = *reinterpret_cast<const f16x8*>(&A[(wm + 32 * i) * kNvRow + orow + 16 * ks]);
+          fb[i] = *reinterpret_cast<const f16x8*>(&B[(wn + 32 * i) * kNvRow + orow + 16 * ks]);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-          acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
+      // Step j+1 into the other buffer (last read in step j-1, before the barrier
+      // that ended it), then its ring slot takes step j+1+kNvDepth.
+      const int un = (u + 1) % kNvDepth;
+      const int kn = kNvBK * (j + 1) + 32 * ph;
+      expand_piece(ra[un], kn, q.K, &sA[(u + 1) & 1][dst]);
+      expand_piece(rb[un], kn, q.K, &sB[(u + 1) & 1][dst]);
+      ra[un] = load_piece(aq, as, arq, ars, kn + kNvBK * kNvDepth);
+      rb[un] = load_piece(bq, bs, brq, brs, kn + kNvBK * kNvDepth);
+      __syncthreads();
     }
-    // The other buffer was last read in step j-1, before the barrier that ended it.
-    expand_piece(pa, kn, q.K, &sA[(j + 1) & 1][dst]);
-    expand_piece(pb, kn, q.K, &sB[(j + 1) & 1][dst]);
-    __syncthreads();
   }
 
   // acc[i][jj] register r of lane l: row 8(r/4) + 4(l/32) + r%4, column l%32 of its 32x32 block.
