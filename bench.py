@@ -38,6 +38,7 @@ KERNEL_SOURCES = ["mxfp4_block_scaled_02_amd/csrc/gemm.hip", "mxfp4_block_scaled
                   "mxfp4_block_scaled_02_amd/csrc/host_common.hpp"]
 RMS_SOURCES = ["mxfp4_block_scaled_02_amd/csrc/rmsnorm_quant.hip", "mxfp4_block_scaled_02_amd/csrc/mx_device.hpp",
                "mxfp4_block_scaled_02_amd/csrc/host_common.hpp"]
+NV_SOURCES = ["mxfp4_block_scaled_02_amd/csrc/nvfp4.hip", "mxfp4_block_scaled_02_amd/csrc/host_common.hpp"]
 COPY_BYTES = 256 << 20  # plain device copy used to calibrate the FETCH_SIZE / WRITE_SIZE counters
 
 
@@ -85,6 +86,15 @@ def kernel_source_hash(sources=KERNEL_SOURCES):
     return h.hexdigest()[:16]
 
 
+def sources_for(name):
+    """Source files whose hash keys the counter record of a workload or kernel name."""
+    if "rmsnorm" in name:
+        return RMS_SOURCES
+    if "nvfp4" in name:
+        return NV_SOURCES
+    return KERNEL_SOURCES
+
+
 def recorded_traffic(name):
     """HBM bytes per launch from the committed counter record, or None if the kernel changed since."""
     path = os.path.join(PROFILES, f"traffic_{name}.json")
@@ -92,7 +102,7 @@ def recorded_traffic(name):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_hash") != kernel_source_hash(RMS_SOURCES if name == "rmsnorm" else KERNEL_SOURCES):
+    if rec.get("kernel_source_hash") != kernel_source_hash(sources_for(name)):
         return None
     return rec.get("bytes_per_launch")
 
@@ -127,7 +137,7 @@ def summarize_pmc(workload_dir, copy_dir, kernel):
     kv, kn = per_dispatch(workload_dir, kernel)
     cv, cn = per_dispatch(copy_dir, "copy")  # torch's device copy kernel
     expected_kib = COPY_BYTES / 1024
-    out = {"kernel": kernel, "kernel_source_hash": kernel_source_hash(RMS_SOURCES if "rmsnorm" in kernel else KERNEL_SOURCES),
+    out = {"kernel": kernel, "kernel_source_hash": kernel_source_hash(sources_for(kernel)),
            "copy_bytes": COPY_BYTES}
     total = 0.0
     for c in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -366,7 +376,8 @@ def bench_grouped_mnk(args):
                            path="grouped_gemm_a4w4_mnk"),
                us_per_call=round(ms_step * 1e3, 3), tflops=round(tflops, 3), hbm_gbs=round(gbs, 2),
                roofline=dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
-                             frac=round(achieved / peak, 4), traffic=None, algorithmic_bytes=nbytes,
+                             frac=round(achieved / peak, 4), traffic=recorded_traffic("grouped_mnk"),
+                             algorithmic_bytes=nbytes,
                              algorithmic_flops=flops))
     if not args.no_cpu_baseline:
         import oracle
@@ -470,7 +481,8 @@ def bench_nvfp4(args):
                            path="grouped_gemm_nvfp4"),
                us_per_call=round(ms_step * 1e3, 3), tflops=round(tflops, 3), hbm_gbs=round(gbs, 2),
                roofline=dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
-                             frac=round(achieved / peak, 4), traffic=None, algorithmic_bytes=nbytes,
+                             frac=round(achieved / peak, 4), traffic=recorded_traffic("nvfp4_grouped"),
+                             algorithmic_bytes=nbytes,
                              algorithmic_flops=flops))
     if not args.no_cpu_baseline:
         import oracle
