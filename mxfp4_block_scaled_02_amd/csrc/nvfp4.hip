@@ -16,12 +16,18 @@
 //
 // Workgroup: 256 threads own a 128 x 128 tile of C; a K step is 64. Thread t
 // expands 32 elements of row t/2 (K half t%2) of each operand per step: two
-// 8-byte code loads, two 1-byte scale loads, then per pair of elements one
-// convert (two fp4 to two fp16, times the scale's power of two, exact) and one
-// packed fp16 multiply by the scale's significand (exact). Wave w computes rows
-// 64(w/2).. and columns 64(w%2).. as 2 x 2 32x32 accumulators. LDS holds two
-// fp16 tiles per operand (double buffer), rows padded to 144 bytes so that the
-// 16-byte operand reads of 8 consecutive rows cover all banks once.
+// 8-byte code loads and its two scale bytes (one dword load of the row's four
+// scale bytes of the step where the scale rows allow it, else two byte loads),
+// then per pair of elements one convert (two fp4 to two fp16, times the scale's
+// power of two, exact) and one packed fp16 multiply by the scale's significand
+// (exact). Wave w computes rows 64(w/2).. and columns 64(w%2).. as 2 x 2 32x32
+// accumulators. LDS holds two fp16 tiles per operand (double buffer), rows
+// padded to 144 bytes so that the 16-byte operand reads of 8 consecutive rows
+// cover all banks once. The problems' tiles are laid out longest K first, so
+// that the workgroups dispatched last (when the GPU is already full) are the
+// shortest ones.
+#include <algorithm>
+
 #include "host_common.hpp"
 
 namespace {
@@ -35,7 +41,7 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 constexpr int kNvBM = 128, kNvBN = 128, kNvBK = 64, kNvThreads = 256;
 constexpr int kNvRow = kNvBK + 8;        // fp16 per LDS row: 64 + 8 padding (144 bytes)
 constexpr int kNvTile = kNvBM * kNvRow;  // fp16 per operand tile (kNvBM == kNvBN)
-constexpr int kNvDepth = 4;              // K steps of loads in flight (even: the LDS buffer is j & 1)
+constexpr int kNvDepth = 2;              // K steps of loads in flight (even: the LDS buffer is j & 1)
 
 struct NvProblem {
   const uint8_t* Aq;  // codes [M, K/2], row stride lda bytes
@@ -77,26 +83,45 @@ __device__ __forceinline__ NvScale e4m3_split(uint32_t b) {
 
 // One operand row piece of a K step: 32 elements (16 code bytes, loaded as two
 // 8-byte halves so that rows need only 8-byte alignment) and their two scale
-// bytes (loaded one by one: scale rows need no alignment).
+// bytes. WS (word scales): one dword load of the row's 4 scale bytes of the step
+// (bytes kk/16 and kk/16 + 1 of it are this piece's), which needs scale rows on
+// 4-byte boundaries and K % 64 == 0 (no dword straddles the end of a row);
+// otherwise two byte loads (scale rows need no alignment). A byte load's value is
+// widened at its use, and with the load ring that widening lands at the loop
+// head, where it waits for the newest loads; a dword load needs no widening.
 struct Piece {
   u32x2 q0, q1;
   uint32_t s0, s1;
 };
 
+template <bool WS>
 __device__ __forceinline__ Piece load_piece(__amdgpu_buffer_rsrc_t qr, __amdgpu_buffer_rsrc_t sr, uint32_t row_q,
                                             uint32_t row_s, int kk) {
   Piece p;
   p.q0 = __builtin_amdgcn_raw_buffer_load_b64(qr, row_q + (uint32_t)(kk / 2), 0, 0);
   p.q1 = __builtin_amdgcn_raw_buffer_load_b64(qr, row_q + (uint32_t)(kk / 2) + 8u, 0, 0);
-  p.s0 = __builtin_amdgcn_raw_buffer_load_b8(sr, row_s + (uint32_t)(kk / 16), 0, 0);
-  p.s1 = __builtin_amdgcn_raw_buffer_load_b8(sr, row_s + (uint32_t)(kk / 16) + 1u, 0, 0);
+  if constexpr (WS) {
+    p.s0 = __builtin_amdgcn_raw_buffer_load_b32(sr, row_s + (uint32_t)((kk / 16) & ~3), 0, 0);
+    p.s1 = p.s0;
+  } else {
+    p.s0 = __builtin_amdgcn_raw_buffer_load_b8(sr, row_s + (uint32_t)(kk / 16), 0, 0);
+    p.s1 = __builtin_amdgcn_raw_buffer_load_b8(sr, row_s + (uint32_t)(kk / 16) + 1u, 0, 0);
+  }
   return p;
 }
 
 // Expands one piece to 32 fp16 in LDS at dst (16-byte aligned). Blocks at or past
 // K get significand 0: their products are zero whatever bytes the loads returned.
-__device__ __forceinline__ void expand_piece(const Piece& p, int kk, int K, _Float16* dst) {
-  NvScale s0 = e4m3_split(p.s0 & 0xffu), s1 = e4m3_split(p.s1 & 0xffu);
+template <bool WS>
+__device__ __forceinline__ void expand_piece(const Piece& pin, int kk, int K, _Float16* dst) {
+  Piece p = pin;
+  // Ties the piece's registers to this point: left free, the compiler hoists the
+  // scale decoding of every ring slot to the loop head, which then waits for the
+  // loads issued last.
+  asm volatile("" : "+v"(p.q0), "+v"(p.q1), "+v"(p.s0), "+v"(p.s1));
+  const int sh = WS ? 16 * ((kk >> 5) & 1) : 0;  // byte 2*(K half) of the step's scale dword
+  // e4m3_split masks every field it reads, so the bytes above need no clearing.
+  NvScale s0 = e4m3_split(p.s0 >> sh), s1 = e4m3_split(p.s1 >> (WS ? sh + 8 : 0));
   if (kk >= K) s0.sig = f16x2{(_Float16)0.0f, (_Float16)0.0f};
   if (kk + 16 >= K) s1.sig = f16x2{(_Float16)0.0f, (_Float16)0.0f};
   const uint32_t qw[4] = {p.q0.x, p.q0.y, p.q1.x, p.q1.y};
@@ -121,6 +146,7 @@ __device__ __forceinline__ void expand_piece(const Piece& p, int kk, int K, _Flo
   for (int c = 0; c < 4; ++c) d[c] = u32x4{out[4 * c], out[4 * c + 1], out[4 * c + 2], out[4 * c + 3]};
 }
 
+template <bool WS>
 __global__ __launch_bounds__(kNvThreads) void gemm_nvfp4_kernel(NvArgs a) {
   __shared__ __align__(16) _Float16 sA[2][kNvTile];
   __shared__ __align__(16) _Float16 sB[2][kNvTile];
@@ -163,13 +189,13 @@ __global__ __launch_bounds__(kNvThreads) void gemm_nvfp4_kernel(NvArgs a) {
 #pragma unroll
   for (int u = 0; u < kNvDepth; ++u) {
     const int kk = kNvBK * u + 32 * ph;
-    ra[u] = load_piece(aq, as, arq, ars, kk);
-    rb[u] = load_piece(bq, bs, brq, brs, kk);
+    ra[u] = load_piece<WS>(aq, as, arq, ars, kk);
+    rb[u] = load_piece<WS>(bq, bs, brq, brs, kk);
   }
-  expand_piece(ra[0], 32 * ph, q.K, &sA[0][dst]);
-  expand_piece(rb[0], 32 * ph, q.K, &sB[0][dst]);
-  ra[0] = load_piece(aq, as, arq, ars, kNvBK * kNvDepth + 32 * ph);
-  rb[0] = load_piece(bq, bs, brq, brs, kNvBK * kNvDepth + 32 * ph);
+  expand_piece<WS>(ra[0], 32 * ph, q.K, &sA[0][dst]);
+  expand_piece<WS>(rb[0], 32 * ph, q.K, &sB[0][dst]);
+  ra[0] = load_piece<WS>(aq, as, arq, ars, kNvBK * kNvDepth + 32 * ph);
+  rb[0] = load_piece<WS>(bq, bs, brq, brs, kNvBK * kNvDepth + 32 * ph);
   __syncthreads();
 
   const int wm = 64 * (wave >> 1), wn = 64 * (wave & 1);
@@ -180,29 +206,35 @@ __global__ __launch_bounds__(kNvThreads) void gemm_nvfp4_kernel(NvArgs a) {
       const int j = j0 + u;
       const _Float16* A = sA[u & 1];  // j & 1: kNvDepth is even
       const _Float16* B = sB[u & 1];
+      // All operand reads of the step first, then its 16 matrix instructions.
+      f16x8 fa[kNvBK / 16][2], fb[kNvBK / 16][2];
 #pragma unroll
-      for (int ks = 0; ks < kNvBK / 16; ++ks) {
-        f16x8 fa[2], fb[2];
+      for (int ks = 0; ks < kNvBK / 16; ++ks)
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-          fa[i] = *reinterpret_cast<const f16x8*>(&A[(wm + 32 * i) * kNvRow + orow + 16 * ks]);
-          fb[i] = *reinterpret_cast<const f16x8*>(&B[(wn + 32 * i) * kNvRow + orow + 16 * ks]);
+          fa[ks][i] = *reinterpret_cast<const f16x8*>(&A[(wm + 32 * i) * kNvRow + orow + 16 * ks]);
+          fb[ks][i] = *reinterpret_cast<const f16x8*>(&B[(wn + 32 * i) * kNvRow + orow + 16 * ks]);
         }
+#pragma unroll
+      for (int ks = 0; ks < kNvBK / 16; ++ks)
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj)
-            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[i], fb[jj], acc[i][jj], 0, 0, 0);
-      }
+            acc[i][jj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[ks][i], fb[ks][jj], acc[i][jj], 0, 0, 0);
       // Step j+1 into the other buffer (last read in step j-1, before the barrier
-      // that ended it), then its ring slot takes step j+1+kNvDepth.
+      // that ended it), then its ring slot takes step j+1+kNvDepth. The
+      // scheduling barriers keep the three phases in this order.
       const int un = (u + 1) % kNvDepth;
       const int kn = kNvBK * (j + 1) + 32 * ph;
-      expand_piece(ra[un], kn, q.K, &sA[(u + 1) & 1][dst]);
-      expand_piece(rb[un], kn, q.K, &sB[(u + 1) & 1][dst]);
-      ra[un] = load_piece(aq, as, arq, ars, kn + kNvBK * kNvDepth);
-      rb[un] = load_piece(bq, bs, brq, brs, kn + kNvBK * kNvDepth);
+      __builtin_amdgcn_sched_barrier(0);
+      expand_piece<WS>(ra[un], kn, q.K, &sA[(u + 1) & 1][dst]);
+      expand_piece<WS>(rb[un], kn, q.K, &sB[(u + 1) & 1][dst]);
+      __builtin_amdgcn_sched_barrier(0);
+      ra[un] = load_piece<WS>(aq, as, arq, ars, kn + kNvBK * kNvDepth);
+      rb[un] = load_piece<WS>(bq, bs, brq, brs, kn + kNvBK * kNvDepth);
       __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
@@ -229,6 +261,7 @@ extern "C" int grouped_gemm_nvfp4(const nvfp4_group* groups, int G, void* stream
   NvArgs a{};
   int P = 0;
   int64_t total = 0;
+  bool ws = true;  // every problem's scale rows allow the dword scale loads
   const int64_t lim = (int64_t)1 << 31;  // 32-bit buffer offsets, with a tile of rows to spare
   for (int g = 0; g < G; ++g) {
     const nvfp4_group& q = groups[g];
@@ -251,6 +284,9 @@ extern "C" int grouped_gemm_nvfp4(const nvfp4_group* groups, int G, void* stream
       if (q.strideA % 8 != 0 || q.strideB % 8 != 0) return MXFP4_ERR_ALIGN;
     }
     const int64_t tiles = mxh::cdiv(q.M, kNvBM) * mxh::cdiv(q.N, kNvBN);
+    if (q.K % 64 != 0 || q.ldas % 4 != 0 || q.ldbs % 4 != 0 || (q.L > 1 && (q.strideAs % 4 != 0 || q.strideBs % 4 != 0)) ||
+        !mxh::aligned(q.As, 4) || !mxh::aligned(q.Bs, 4))
+      ws = false;
     for (int64_t l = 0; l < q.L; ++l) {
       NvProblem& o = a.p[P];
       o.Aq = (const uint8_t*)q.Aq + l * q.strideA;
@@ -266,15 +302,27 @@ extern "C" int grouped_gemm_nvfp4(const nvfp4_group* groups, int G, void* stream
       o.M = (int)q.M;
       o.N = (int)q.N;
       o.K = (int)q.K;
-      a.tile_start[P] = (int)total;
       total += tiles;
       if (total > INT32_MAX) return MXFP4_ERR_SHAPE;
       ++P;
     }
   }
-  a.tile_start[P] = (int)total;
-  a.P = P;
-  void* args[] = {&a};
-  return mxh::launch_status(hipLaunchKernel((const void*)gemm_nvfp4_kernel, dim3((unsigned)total),
-                                            dim3(kNvThreads), args, 0, (hipStream_t)stream));
+  // Longest K first (a stable order): the hardware hands out workgroups in id
+  // order, so the tiles that start last, once the GPU is full, are the shortest.
+  int order[MXFP4_MAX_GROUPS];
+  for (int i = 0; i < P; ++i) order[i] = i;
+  std::stable_sort(order, order + P, [&](int x, int y) { return a.p[x].K > a.p[y].K; });
+  NvArgs b{};
+  int64_t start = 0;
+  for (int i = 0; i < P; ++i) {
+    const NvProblem& o = a.p[order[i]];
+    b.p[i] = o;
+    b.tile_start[i] = (int)start;
+    start += mxh::cdiv(o.M, kNvBM) * mxh::cdiv(o.N, kNvBN);
+  }
+  b.tile_start[P] = (int)start;
+  b.P = P;
+  void* args[] = {&b};
+  return mxh::launch_status(hipLaunchKernel(ws ? (const void*)gemm_nvfp4_kernel<true> : (const void*)gemm_nvfp4_kernel<false>,
+                                            dim3((unsigned)total), dim3(kNvThreads), args, 0, (hipStream_t)stream));
 }

@@ -109,6 +109,68 @@ def test_padded_rows_and_guard_band():
     assert_nv_tolerance(got[:, :N], oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs), "padded rows")
 
 
+def test_padded_rows_word_scales():
+    """Scale rows on 4-byte boundaries with K % 64 == 0 take the dword scale loads;
+    the NaN scale bytes past K/16 in each row must still be ignored."""
+    say("[nvfp4] padded rows, dword scale loads")
+    M, N, K = 70, 150, 320
+    aq, as_ = synth.make_nvfp4(M, K, 51)
+    bq, bs = synth.make_nvfp4(N, K, 52)
+    lda, ldas, ldb, ldbs, ldc = K // 2 + 16, K // 16 + 4, K // 2 + 8, K // 16 + 8, N + 3
+
+    def pad(x, ld, fill):
+        out = np.full((x.shape[0], ld), fill, dtype=np.uint8)
+        out[:, :x.shape[1]] = x
+        return to_dev_u8(out)[:, :x.shape[1]]
+
+    A, As = pad(aq, lda, 0xFF), pad(as_, ldas, 0x7F)
+    B, Bs = pad(bq, ldb, 0xFF), pad(bs, ldbs, 0x7F)
+    C = torch.full((M, ldc), 12345, dtype=torch.int16, device="cuda").view(torch.float16)
+    ops.grouped_gemm_nvfp4([(A, As, B, Bs)], out_list=[C[:, :N]])
+    torch.cuda.synchronize()
+    got = f16_of(C)
+    assert (got[:, N:] == 12345).all(), "C padding written"
+    assert_nv_tolerance(got[:, :N], oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs), "padded rows, dword scales")
+
+
+def test_misaligned_scales_take_byte_loads():
+    """A scale matrix that starts one byte past a 4-byte boundary makes the whole
+    launch read scales byte by byte; results are the same as the oracle's."""
+    say("[nvfp4] misaligned scale base")
+    shapes = [(64, 128, 256), (33, 200, 512)]
+    descs, refs = [], []
+    for gi, (M, N, K) in enumerate(shapes):
+        aq, as_ = synth.make_nvfp4(M, K, 53, (gi,))
+        bq, bs = synth.make_nvfp4(N, K, 54, (gi,))
+        buf = torch.zeros(as_.size + 1, dtype=torch.uint8, device="cuda")
+        buf[1:] = to_dev_u8(as_.reshape(-1))
+        As = buf[1:].view(M, K // 16)
+        descs.append((to_dev_u8(aq), As, to_dev_u8(bq), to_dev_u8(bs)))
+        refs.append(oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs))
+    outs = ops.grouped_gemm_nvfp4(descs)
+    torch.cuda.synchronize()
+    for gi, (c, r) in enumerate(zip(outs, refs)):
+        assert_nv_tolerance(f16_of(c), r, f"misaligned scales, group {gi}")
+
+
+def test_groups_reordered_by_k():
+    """Problems listed out of K order (the launch lays out the longest K first) land
+    in their own outputs; every K here allows the dword scale loads."""
+    say("[nvfp4] groups reordered by K")
+    shapes = [(100, 300, 512, 2), (1, 32, 64, 2), (257, 1024, 2048, 1), (130, 520, 4096, 1), (48, 96, 1024, 3)]
+    host, dev = [], []
+    for gi, (M, N, K, L) in enumerate(shapes):
+        ops_ = [synth.make_nvfp4(M, K, 55, (gi, l)) + synth.make_nvfp4(N, K, 56, (gi, l)) for l in range(L)]
+        host.append(ops_)
+        dev.append(tuple(torch.stack([to_dev_u8(o[i]) for o in ops_]) for i in range(4)))
+    outs = ops.grouped_gemm_nvfp4(dev)
+    torch.cuda.synchronize()
+    for gi, ((M, N, K, L), ops_, c) in enumerate(zip(shapes, host, outs)):
+        for l in range(L):
+            aq, as_, bq, bs = ops_[l]
+            assert_nv_tolerance(f16_of(c[l]), oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs), f"group {gi} batch {l}")
+
+
 def test_groups_and_batches_one_launch():
     say("[nvfp4] groups and batches")
     shapes = [(100, 300, 512, 2), (257, 1024, 2048, 1), (48, 96, 1056, 3), (1, 32, 64, 2), (130, 520, 4096, 1)]
