@@ -1033,7 +1033,8 @@ struct SkinnyShape {
   int MS, NB;
 };
 SkinnyShape choose_skinny(int64_t M, int64_t N, int64_t K) {
-  static const SkinnyShape cand[] = {{4, 1}, {4, 2}, {4, 4}, {8, 1}, {8, 2}, {8, 4}, {16, 1}, {16, 2}, {16, 4}};
+  // {16, 8}: 128 columns, 145 KB of LDS (the 16 partial tiles), one workgroup per CU.
+  static const SkinnyShape cand[] = {{4, 1}, {4, 2}, {4, 4}, {8, 1}, {8, 2}, {8, 4}, {16, 1}, {16, 2}, {16, 4}, {16, 8}};
   SkinnyShape best = {16, 1};
   double best_cost = -1.0;
   for (const SkinnyShape& c : cand) {
@@ -1125,6 +1126,7 @@ hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, in
       case 8 * 16 + 4: return launch_skinny<8, 4, 2>(o, d, M, st);
       case 16 * 16 + 1: return launch_skinny<16, 1, 2>(o, d, M, st);
       case 16 * 16 + 2: return launch_skinny<16, 2, 2>(o, d, M, st);
+      case 16 * 16 + 8: return launch_skinny<16, 8, 1>(o, d, M, st);
       default: return launch_skinny<16, 4, 2>(o, d, M, st);
     }
   }

@@ -199,7 +199,9 @@ EDGE = [(1, 1, 32), (1, 16, 128), (2, 100, 96), (4, 256, 512), (16, 2112, 7168),
         # odd K/64 with one K step per split (9 splits); the 64-split maximum; more K than 64 splits
         # can hold (falls back); a middle case; the 8-way N shard of skinny
         (3, 70, 352), (16, 130, 7232), (16, 130, 1088), (16, 64, 65536), (16, 48, 66560), (8, 1000, 6144),
-        (16, 264, 7168)]
+        (16, 264, 7168),
+        # 16 < M <= 64 on 128-column workgroups: an M tail, a ragged N, odd K/64 with a K tail
+        (50, 20000, 1056)]
 
 
 @pytest.mark.parametrize("M,N,K", EDGE)
