@@ -8,8 +8,8 @@
 // lane's 32-element chunk, and their fp4 conversions likewise use only the
 // exponent of the scale they are given; an E4M3 scale has three mantissa bits
 // and covers 16 elements. An E2M1 value (2 significant bits) times an E4M3 scale
-// (4 significant bits) has at most 6 significant bits and lies in [2^-10, 2880]
-// in magnitude (or is zero), so it is exact in fp16, normal. Each workgroup
+// (4 significant bits) has at most 6 significant bits and lies in [2^-10, 2688]
+// in magnitude (or is zero), so it is exact in fp16. Each workgroup
 // therefore expands its operand tiles to fp16 in LDS, exactly, and runs the
 // dense fp16 32x32x16 instruction: the sum is then that of the exact products,
 // in fp32.
@@ -18,9 +18,8 @@
 // expands 32 elements of row t/2 (K half t%2) of each operand per step: two
 // 8-byte code loads and its two scale bytes (one dword load of the row's four
 // scale bytes of the step where the scale rows allow it, else two byte loads),
-// then per pair of elements one convert (two fp4 to two fp16, times the scale's
-// power of two, exact) and one packed fp16 multiply by the scale's significand
-// (exact). Wave w computes rows 64(w/2).. and columns 64(w%2).. as 2 x 2 32x32
+// then per pair of elements one convert (two fp4 to two fp16, times 2^8, exact)
+// and one packed fp16 multiply by 2^-8 times the scale (exact). Wave w computes rows 64(w/2).. and columns 64(w%2).. as 2 x 2 32x32
 // accumulators. LDS holds two fp16 tiles per operand (double buffer), rows
 // padded to 144 bytes so that the 16-byte operand reads of 8 consecutive rows
 // cover all banks once. The problems' tiles are laid out longest K first, so
@@ -64,21 +63,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t nv_rsrc(const void* base, int6
 }
 
 // E4M3 byte (OCP 8-bit floating point, E4M3: bias 7, subnormals m/8 * 2^-6,
-// S.1111.111 is NaN) as p2 * sig: p2 = 2^(e-7) (2^-6 for e = 0) as an fp32
-// power of two, sig = +-(1 + m/8) (+-m/8 for e = 0) as an fp16 pair, exact.
-struct NvScale {
-  float p2;
-  f16x2 sig;
-};
-__device__ __forceinline__ NvScale e4m3_split(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  NvScale r;
-  r.p2 = __builtin_bit_cast(float, ((e ? e : 1u) + 120u) << 23);
-  _Float16 g = (_Float16)((float)(e ? 8u + m : m) * 0.125f);
-  if (e == 15u && m == 7u) g = (_Float16)__builtin_nanf("");
-  if (b & 0x80u) g = -g;
-  r.sig = f16x2{g, g};
-  return r;
+// S.1111.111 is NaN) as an fp16 pair (both halves) holding 2^-8 times its value:
+// the byte's exponent and mantissa fields shifted into fp16's (E4M3 field e is
+// 2^(e-7), fp16 field e is 2^(e-15); the subnormals line up likewise), the sign
+// into fp16's, and a NaN for S.1111.111. Exact.
+__device__ __forceinline__ uint32_t e4m3_f16x2_div256(uint32_t b) {
+  uint32_t h = ((b & 0x7fu) << 7) | ((b & 0x80u) << 8);
+  if ((b & 0x7fu) == 0x7fu) h |= 0x7e00u;  // exponent field all ones, mantissa non-zero
+  return h | (h << 16);
 }
 
 // One operand row piece of a K step: 32 elements (16 code bytes, loaded as two
@@ -111,7 +103,7 @@ __device__ __forceinline__ Piece load_piece(__amdgpu_buffer_rsrc_t qr, __amdgpu_
 }
 
 // Expands one piece to 32 fp16 in LDS at dst (16-byte aligned). Blocks at or past
-// K get significand 0: their products are zero whatever bytes the loads returned.
+// K get scale 0: their products are zero whatever bytes the loads returned.
 template <bool WS>
 __device__ __forceinline__ void expand_piece(const Piece& pin, int kk, int K, _Float16* dst) {
   Piece p = pin;
@@ -120,25 +112,29 @@ __device__ __forceinline__ void expand_piece(const Piece& pin, int kk, int K, _F
   // loads issued last.
   asm volatile("" : "+v"(p.q0), "+v"(p.q1), "+v"(p.s0), "+v"(p.s1));
   const int sh = WS ? 16 * ((kk >> 5) & 1) : 0;  // byte 2*(K half) of the step's scale dword
-  // e4m3_split masks every field it reads, so the bytes above need no clearing.
-  NvScale s0 = e4m3_split(p.s0 >> sh), s1 = e4m3_split(p.s1 >> (WS ? sh + 8 : 0));
-  if (kk >= K) s0.sig = f16x2{(_Float16)0.0f, (_Float16)0.0f};
-  if (kk + 16 >= K) s1.sig = f16x2{(_Float16)0.0f, (_Float16)0.0f};
+  // The decode masks every field it reads, so the bytes above need no clearing.
+  f16x2 s0 = __builtin_bit_cast(f16x2, e4m3_f16x2_div256(p.s0 >> sh));
+  f16x2 s1 = __builtin_bit_cast(f16x2, e4m3_f16x2_div256(p.s1 >> (WS ? sh + 8 : 0)));
+  if (kk >= K) s0 = f16x2{(_Float16)0.0f, (_Float16)0.0f};
+  if (kk + 16 >= K) s1 = f16x2{(_Float16)0.0f, (_Float16)0.0f};
   const uint32_t qw[4] = {p.q0.x, p.q0.y, p.q1.x, p.q1.y};
   uint32_t out[16];
+  // Each element: E2M1 * 2^8 from the convert (at most 1536: exact), times the
+  // scale's 2^-8 multiple: the exact product E2M1 * E4M3, which has at most 6
+  // significant bits and lies in [2^-10, 2688] (or is zero): exact in fp16.
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const NvScale& sc = i < 2 ? s0 : s1;
+    const f16x2 sc = i < 2 ? s0 : s1;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       f16x2 v;
       switch (j) {  // the byte select must be a constant
-        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw[i], sc.p2, 0); break;
-        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw[i], sc.p2, 1); break;
-        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw[i], sc.p2, 2); break;
-        default: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw[i], sc.p2, 3); break;
+        case 0: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw[i], 256.0f, 0); break;
+        case 1: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw[i], 256.0f, 1); break;
+        case 2: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw[i], 256.0f, 2); break;
+        default: v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(qw[i], 256.0f, 3); break;
       }
-      out[4 * i + j] = __builtin_bit_cast(uint32_t, v * sc.sig);  // element 2(4i+j) in the low half
+      out[4 * i + j] = __builtin_bit_cast(uint32_t, v * sc);  // element 2(4i+j) in the low half
     }
   }
   u32x4* d = reinterpret_cast<u32x4*>(dst);
