@@ -91,7 +91,7 @@ __device__ __forceinline__ float row_inv(double acc, int l, int K, float eps) {
   return (float)(1.0 / __builtin_sqrt(ms));
 }
 
-// KEEP > 0: rows of at most KEEP passes keep x (and w) in registers between
+// KEEP > 0 (even): rows of at most KEEP passes keep x in registers between
 // the two passes (one read of x). KEEP == 0: any K, x read again in pass two,
 // kBatch passes at a time.
 template <int KEEP>
@@ -103,18 +103,26 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
   const int passes = (a.K + 511) / 512;
 
   if constexpr (KEEP > 0) {
-    uint4 v[KEEP], wv[KEEP];
+    uint4 v[KEEP];
 #pragma unroll
     for (int c = 0; c < KEEP; ++c) v[c] = row_load16(xr, c < passes ? 512 * c + 8 * l : a.K);
-#pragma unroll
-    for (int c = 0; c < KEEP; ++c) wv[c] = row_load16(wr, c < passes ? 512 * c + 8 * l : a.K);
     double acc = 0.0;
 #pragma unroll
     for (int c = 0; c < KEEP; ++c) acc = add_squares(acc, v[c]);
+    // w is the same for every row (cache-resident): it is read two passes
+    // ahead of its use rather than held, which leaves registers for a third
+    // wave per SIMD at K <= 7168.
+    uint4 w0 = row_load16(wr, 8 * l), w1 = row_load16(wr, 1 < passes ? 512 + 8 * l : a.K);
     const float inv = row_inv(acc, l, a.K, a.eps);
 #pragma unroll
-    for (int c = 0; c < KEEP; ++c)
-      if (c < passes) norm_quant_pass(a, r, 512 * c + 8 * l, v[c], wv[c], inv, l);
+    for (int c = 0; c < KEEP; c += 2) {
+      const uint4 n0 = row_load16(wr, c + 2 < passes ? 512 * (c + 2) + 8 * l : a.K);
+      const uint4 n1 = row_load16(wr, c + 3 < passes ? 512 * (c + 3) + 8 * l : a.K);
+      if (c < passes) norm_quant_pass(a, r, 512 * c + 8 * l, v[c], w0, inv, l);
+      if (c + 1 < passes) norm_quant_pass(a, r, 512 * (c + 1) + 8 * l, v[c + 1], w1, inv, l);
+      w0 = n0;
+      w1 = n1;
+    }
   } else {
     double acc = 0.0;
     for (int c0 = 0; c0 < passes; c0 += kBatch) {
@@ -138,8 +146,9 @@ __global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
   }
 }
 
-// Rows of up to 16 passes (K <= 8192) take the register-resident kernel.
-constexpr int kKeepPasses = 16;
+// Rows of up to 14 passes (K <= 7168: three waves per SIMD) or 16 passes
+// (K <= 8192: two) take the register-resident kernel.
+constexpr int kKeepPasses = 16, kKeepPassesShort = 14;
 
 }  // namespace
 
@@ -154,8 +163,10 @@ extern "C" int mxfp4_rmsnorm_quant(const void* x, int64_t ldx, const void* w, fl
     return MXFP4_ERR_ALIGN;
   RmsArgs a{(const uint16_t*)x, ldx, (const uint16_t*)w, (uint8_t*)q, ldq, (uint8_t*)s, lds, M, (int)K, eps};
   void* args[] = {&a};
-  const void* kern = (K + 511) / 512 <= kKeepPasses ? (const void*)rmsnorm_quant_kernel<kKeepPasses>
-                                                     : (const void*)rmsnorm_quant_kernel<0>;
+  const int64_t passes = (K + 511) / 512;
+  const void* kern = passes <= kKeepPassesShort ? (const void*)rmsnorm_quant_kernel<kKeepPassesShort>
+                     : passes <= kKeepPasses    ? (const void*)rmsnorm_quant_kernel<kKeepPasses>
+                                                : (const void*)rmsnorm_quant_kernel<0>;
   return mxh::launch_status(hipLaunchKernel(kern, dim3((unsigned)mxh::cdiv(M, kRowsPerBlock)), dim3(256), args, 0,
                                             (hipStream_t)stream));
 }
