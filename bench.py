@@ -657,7 +657,8 @@ def main():
                dtype="mxfp4 (e2m1 x e8m0, fp32 accumulate, bf16 out)", data="synthetic", config=cfg,
                us_per_call=round(us, 3), tflops=round(tflops, 3), hbm_gbs=round(gbs, 2),
                roofline=dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
-                             frac=round(achieved / peak, 4), traffic=recorded_traffic(name),
+                             frac=round(achieved / peak, 4),
+                             traffic=recorded_traffic(name + "_unfused" if args.unfused else name),
                              algorithmic_bytes=total_bytes, algorithmic_flops=total_flops))
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")

@@ -605,12 +605,12 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   const int tail_k = d.K - 128 * (d.KT - 1);
 
   // A registers of one K step in flight: the bf16 pieces, or the pre-quantised
-  // codes and (waves 0 and 1) the row's scale bytes. Two sets alternate: the A of
-  // step j+1 is quantised at step j while the A of step j+2 is arriving.
+  // codes and scale byte of this thread's (row, chunk). Two sets alternate: the A
+  // of step j+1 is quantised at step j while the A of step j+2 is arriving.
   struct AStage {
     uint32_t raw[PREQ ? 1 : 4][4];
     uint4 q;
-    uint32_t qb[4];
+    uint32_t qb;
   };
   AStage s0, s1;
   // Pre-quantised A: row qr = tid/4, chunk qc = tid%4 of the step; in the operand
@@ -631,12 +631,11 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
 #pragma unroll
       for (int h = 0; h < 4; ++h) load_a_piece(j, S, h);
     } else {
+      // The codes and the scale byte of the same (row, chunk): one byte load per
+      // thread, 16 rows per wave. (Loading a row's 4 scale bytes per thread
+      // touches one cache line per lane and floods the L1 with requests.)
       S.q = bload16(aqr, (uint32_t)(qr * p.ldaq + 16 * qc), jo * 64);
-      // Row tid%128's 4 scale bytes: every wave loads (and later stores) them,
-      // waves 2..7 repeating 0 and 1, so that no branch splits the step.
-      const uint32_t so = (uint32_t)((tid & 127) * p.ldas);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) S.qb[c] = bload1(asr, so + c, jo * 4);
+      S.qb = bload1(asr, (uint32_t)(qr * p.ldas + qc), jo * 4);
     }
   };
   // LDS byte addresses of this thread's A stores in buffer 0 (buffer 1 follows).
@@ -644,19 +643,15 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   const uint32_t qa = lds_addr(&sm.a[0][0][0][0]) + (uint32_t)wbase * 4;
   const uint32_t qs = lds_addr(&sm.as[0][0][0]) + (uint32_t)sdw * 4;
   const uint32_t pa = lds_addr(&sm.a[0][qc >> 1][qr >> 5][qslot]);
-  const uint32_t ps = lds_addr(&sm.as[0][0][0]) + (uint32_t)((tid & 31) * 4 + ((tid >> 5) & 3));
-  // Pre-quantised: store the step's codes and scale bytes into LDS buffer `buf`
-  // (K tail chunks zeroed). Scale byte of chunk c: half c/2, unit lane
-  // (c%2)*32 + row%32, byte = 32-row tile, i.e. 128c bytes past chunk 0's.
+  // Scale byte of (row qr, chunk qc): half qc/2, unit lane (qc%2)*32 + qr%32,
+  // byte = 32-row tile qr/32.
+  const uint32_t ps = lds_addr(&sm.as[0][qc >> 1][(qc & 1) * 32 + (qr & 31)]) + (uint32_t)(qr >> 5);
+  // Pre-quantised: store the step's codes and scale byte into LDS buffer `buf`.
+  // A chunk past K gets zero codes and the neutral scale (never a NaN byte).
   auto store_preq = [&](int j, int buf, AStage& S) {
     const bool tl = j == d.KT - 1 && 32 * qc >= tail_k;  // K tail: not A
     lds_st128(pa + buf * kABuf, tl ? make_uint4(0u, 0u, 0u, 0u) : S.q);
-    const bool last = j == d.KT - 1;  // K tail chunks: neutral scale, never a NaN byte
-    const uint32_t sb = ps + buf * kSBuf;
-    lds_st8<0>(sb, S.qb[0]);
-    lds_st8<128>(sb, last && 32 >= tail_k ? mx::kScaleOne : S.qb[1]);
-    lds_st8<256>(sb, last && 64 >= tail_k ? mx::kScaleOne : S.qb[2]);
-    lds_st8<384>(sb, last && 96 >= tail_k ? mx::kScaleOne : S.qb[3]);
+    lds_st8<0>(ps + buf * kSBuf, tl ? mx::kScaleOne : S.qb);
   };
   // Quantise the bf16 A of step j held in S into LDS buffer j&1. The lanes of a
   // quad hold the same four scales and all store that dword. A 32-element block
@@ -793,10 +788,10 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Buffer loads a wave issues per A step: 4 (bf16 A), or 5 for pre-quantised A
-  // (codes and 4 scale bytes), and per B step 6. The waits below count the
+  // Buffer loads a wave issues per A step: 4 (bf16 A), or 2 for pre-quantised A
+  // (codes and a scale byte), and per B step 6. The waits below count the
   // loads issued after a ring stage's.
-  constexpr int kLa = PREQ ? 5 : 4, kDb = 6;
+  constexpr int kLa = PREQ ? 2 : 4, kDb = 6;
   // K step j. Every step requests B(j+2) into the ring stage read at step j-1,
   // one load behind each of its first six matrix pairs, and the A of step j+3
   // into the registers S, piece by piece as the quantisation of A(j+1) from S
