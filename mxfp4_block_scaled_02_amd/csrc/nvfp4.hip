@@ -19,10 +19,10 @@
 // 8-byte code loads and its two scale bytes (one dword load of the row's four
 // scale bytes of the step where the scale rows allow it, else two byte loads),
 // then per pair of elements one convert (two fp4 to two fp16, times 2^8, exact)
-// and one packed fp16 multiply by 2^-8 times the scale (exact). Wave w computes rows 64(w/2).. and columns 64(w%2).. as 2 x 2 32x32
-// accumulators. LDS holds two fp16 tiles per operand (double buffer), rows
-// padded to 144 bytes so that the 16-byte operand reads of 8 consecutive rows
-// cover all banks once. The problems' tiles are laid out longest K first, so
+// and one packed fp16 multiply by 2^-8 times the scale (exact). Wave w computes
+// rows 64(w/2).. and columns 64(w%2).. as 2 x 2 32x32 accumulators. LDS holds
+// two fp16 tiles per operand (double buffer), rows padded to 144 bytes so that
+// the 16-byte operand reads of 8 consecutive rows cover all banks once. The problems' tiles are laid out longest K first, so
 // that the workgroups dispatched last (when the GPU is already full) are the
 // shortest ones.
 #include <algorithm>
