@@ -70,6 +70,28 @@ def test_special_scales():
     assert_nv_tolerance(run_one(aq, as_, bq, bs), oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs), "special scales")
 
 
+@pytest.mark.parametrize("K", [16, 64])
+def test_every_scale_pair_exact(K):
+    """Every pair of E4M3 scale bytes: row m of A holds one element 1.0 under scale
+    byte m, row n of B one element 1.0 under scale byte n, so C[m, n] is the
+    product of the two decoded scales, exact in fp16 where it is in range, an
+    infinity past it, NaN for a NaN byte. K = 16 reads the scales byte by byte,
+    K = 64 (scale rows on 4-byte boundaries) with one dword load per row and step;
+    the blocks past the first hold zero codes under the scale 1.0."""
+    say(f"[nvfp4] every scale pair, K={K}")
+    aq = np.zeros((256, K // 2), dtype=np.uint8)
+    aq[:, 0] = 0x02  # element 0 = 1.0
+    sc = np.full((256, K // 16), 0x38, dtype=np.uint8)  # 0x38 = 1.0
+    sc[:, 0] = np.arange(256, dtype=np.uint8)
+    ref = oracle.nvfp4.nvfp4_gemm_ref(aq, sc, aq, sc)
+    got = run_one(aq, sc, aq, sc)
+    r = oracle.nvfp4.f16_bits_to_f64(ref)
+    g = oracle.nvfp4.f16_bits_to_f64(got)
+    assert np.array_equal(np.isnan(g), np.isnan(r)), "NaN positions differ"
+    fin = ~np.isnan(r)
+    assert np.array_equal(g[fin], r[fin]), f"{int((g[fin] != r[fin]).sum())} products differ"
+
+
 def test_overflow_and_nan():
     """Sums past the float16 range give infinities; a NaN scale makes its rows NaN."""
     say("[nvfp4] overflow and NaN")
