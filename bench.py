@@ -118,11 +118,19 @@ def _csv_rows(directory, suffix):
 
 
 def summarize_stats(directory):
+    """Per-kernel table from a rocprofv3 --kernel-trace --stats run: calls, mean, the
+    10th / 50th / 90th percentile of the per-dispatch durations (from the trace),
+    min, max and share of the total."""
     rows = _csv_rows(directory, "kernel_stats.csv")
-    print("| kernel | calls | avg µs | min µs | max µs | share % |")
-    print("|---|---|---|---|---|---|")
+    durs = {}
+    for r in _csv_rows(directory, "kernel_trace.csv"):
+        durs.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print("| kernel | calls | avg µs | p10 µs | median µs | p90 µs | min µs | max µs | share % |")
+    print("|---|---|---|---|---|---|---|---|---|")
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        print(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+        d = durs.get(r["Name"])
+        pct = "| — | — | — " if not d else "| {:.3f} | {:.3f} | {:.3f} ".format(*np.percentile(d, [10, 50, 90]))
+        print(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} {pct}| "
               f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.1f} |")
 
 
@@ -165,6 +173,35 @@ def summarize_counters(directory, kernel):
         out["mfma_busy_fraction"] = (sum(busy) / len(busy)) / (1024 * cycles)
         out["kernel_cycles"] = cycles
     print(json.dumps(out, indent=1))
+
+
+def env_info():
+    """What the run was on (best effort; a field that cannot be read is left out)."""
+    import glob
+    import torch
+    env = {}
+    try:
+        props = torch.cuda.get_device_properties(0)
+        env.update(gpu=props.name, compute_units=props.multi_processor_count,
+                   hbm_gib=round(props.total_memory / 2**30, 1))
+    except Exception:
+        pass
+    env.update(torch=torch.__version__, hip=getattr(torch.version, "hip", None))
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            env["rocm"] = f.read().strip()
+    except OSError:
+        pass
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                cur = [ln.split(":", 1)[1].strip().rstrip("*").strip() for ln in f if ln.strip().endswith("*")]
+        except OSError:
+            continue
+        if cur:
+            env["sclk_at_exit"] = cur[0]
+            break
+    return env
 
 
 def log(msg):
@@ -292,6 +329,7 @@ def bench_rmsnorm(args):
         out["cpu_baseline"] = dict(value=round(rms_bytes(rows, K) / t / 1e9, 6), unit="GB/s", cores=int(threads),
                                    kind="oracle", sample=f"oracle rmsnorm_quant on rows 0..{rows - 1} (K={K}); "
                                    f"median of {len(times)} runs, {t * 1e3:.1f} ms each")
+    out["env"] = env_info()
     print(json.dumps(out), flush=True)
 
 
@@ -402,6 +440,7 @@ def bench_grouped_mnk(args):
         out["cpu_baseline"] = dict(value=round(val, 6), unit=unit, cores=int(threads), kind="oracle",
                                    sample=f"oracle gemm_ref on rows 0..{rows - 1} of the first problem (N={N}, K={K}); "
                                           f"median of {len(times)} runs, {t * 1e3:.1f} ms each")
+    out["env"] = env_info()
     print(json.dumps(out), flush=True)
 
 
@@ -507,6 +546,7 @@ def bench_nvfp4(args):
         out["cpu_baseline"] = dict(value=round(val, 6), unit=unit, cores=int(threads), kind="oracle",
                                    sample=f"oracle nvfp4_gemm_ref on rows 0..{rows - 1} of the first problem "
                                           f"(N={N}, K={K}); median of {len(times)} runs, {t * 1e3:.1f} ms each")
+    out["env"] = env_info()
     print(json.dumps(out), flush=True)
 
 
@@ -663,6 +703,7 @@ def main():
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(w, unit)
+    out["env"] = env_info()
     print(json.dumps(out), flush=True)
 
 
