@@ -177,7 +177,6 @@ def summarize_counters(directory, kernel):
 
 def env_info():
     """What the run was on (best effort; a field that cannot be read is left out)."""
-    import glob
     import torch
     env = {}
     try:
@@ -192,15 +191,6 @@ def env_info():
             env["rocm"] = f.read().strip()
     except OSError:
         pass
-    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
-        try:
-            with open(path) as f:
-                cur = [ln.split(":", 1)[1].strip().rstrip("*").strip() for ln in f if ln.strip().endswith("*")]
-        except OSError:
-            continue
-        if cur:
-            env["sclk_at_exit"] = cur[0]
-            break
     return env
 
 
