@@ -1,8 +1,10 @@
 // mxfp4_quant: standalone per-1x32 MXFP4 quantisation of a bf16 matrix
 // (kernelbot amd-mxfp4-mm submission 683203, ``_quant_shuffled``: a tile of A
 // in, fp4x2 codes and E8M0 bytes out, with row tails masked; here scales are
-// stored row-major). One thread quantises one 32-element block with the same
-// register routine the fused GEMM uses.
+// stored row-major). A lane quad quantises one 32-element block with the
+// register routine the fused GEMM uses (quant8_quad, with the full zero-block
+// rule): lane 4b + p holds elements 8p .. 8p+7 of block b, so a wave reads 16
+// consecutive blocks, 1 KB, with one 16-byte load per lane.
 #include "host_common.hpp"
 #include "mx_device.hpp"
 
@@ -19,24 +21,21 @@ struct QuantArgs {
   int64_t G;  // blocks per row, K/32
 };
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
   const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= a.M * a.G) return;
-  const int64_t r = t / a.G, g = t - r * a.G;
-  const uint16_t* src = a.x + r * a.ldx + 32 * g;
-  uint32_t w[16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint4 v = mx::ldg16(src + 8 * i);
-    w[4 * i + 0] = v.x;
-    w[4 * i + 1] = v.y;
-    w[4 * i + 2] = v.z;
-    w[4 * i + 3] = v.w;
-  }
-  uint32_t q[4], sb;
-  mx::quant32(w, q, sb);
-  *reinterpret_cast<uint4*>(a.q + r * a.ldq + 16 * g) = make_uint4(q[0], q[1], q[2], q[3]);
-  a.s[r * a.lds + g] = (uint8_t)sb;
+  const int64_t b = t >> 2;  // block; whole quads leave together (256 % 4 == 0)
+  if (b >= a.M * a.G) return;
+  const int part = (int)(t & 3);
+  const int64_t r = b / a.G, g = b - r * a.G;
+  // Read once and written once: non-temporal (streaming) loads and stores.
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(a.x + r * a.ldx + 32 * g + 8 * part));
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t sb;
+  const uint32_t codes = mx::quant8_quad<true>(w, sb);
+  __builtin_nontemporal_store(codes, reinterpret_cast<uint32_t*>(a.q + r * a.ldq + 16 * g + 4 * part));
+  if (part == 0) __builtin_nontemporal_store((uint8_t)sb, a.s + r * a.lds + g);
 }
 
 }  // namespace
@@ -63,7 +62,7 @@ extern "C" int mxfp4_quant(const void* x, int64_t ldx, void* q, int64_t ldq, voi
   if (ldx < K || ldq < K / 2 || lds < K / 32) return MXFP4_ERR_SHAPE;
   if (!mxh::aligned(x, 16) || (ldx * 2) % 16 != 0 || !mxh::aligned(q, 16) || ldq % 16 != 0) return MXFP4_ERR_ALIGN;
   QuantArgs a{(const uint16_t*)x, ldx, (uint8_t*)q, ldq, (uint8_t*)s, lds, M, K / 32};
-  const int64_t n = M * (K / 32);
+  const int64_t n = M * (K / 32) * 4;  // four lanes per block
   void* args[] = {&a};
   return mxh::launch_status(hipLaunchKernel((const void*)quant_kernel, dim3((unsigned)mxh::cdiv(n, 256)), dim3(256),
                                             args, 0, (hipStream_t)stream));
