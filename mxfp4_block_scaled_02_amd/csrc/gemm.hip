@@ -355,6 +355,13 @@ __global__ __launch_bounds__(kSpT) void gemm_splitk_kernel(Operand p, Dims d, Sp
   const bool hi_unit = (s16 >> 1) != 0;
   uint4 bq[kSpMaxSteps];
   uint32_t bs[kSpMaxSteps];
+  // A scale dword covers two K steps (four 64-k units): one load per pair of
+  // steps, kSpMaxSteps/2 + 1 of them for a range that may start on an odd step.
+  constexpr int kSg = kSpMaxSteps / 2 + 1;
+  uint32_t bsg[kSg];
+  const int g0 = jb >> 1, glast = (jb + ns - 1) >> 1;
+#pragma unroll
+  for (int g = 0; g < kSg; ++g) bsg[g] = bload4(bss, soff, (uint32_t)min(g0 + g, glast) * 256);
 #pragma unroll
   for (int s = 0; s < kSpMaxSteps; ++s) {
     const int j = jb + min(s, ns - 1);
@@ -362,9 +369,12 @@ __global__ __launch_bounds__(kSpT) void gemm_splitk_kernel(Operand p, Dims d, Sp
     // (in range) and are zeroed below.
     const bool no_unit = 2 * j + 1 >= d.KU && hi_unit;
     bq[s] = bload16_nt(brs, no_unit ? boff - 1024 : boff, (uint32_t)j * 2048);  // read by this workgroup only
-    bs[s] = bload4(bss, soff, (uint32_t)(j >> 1) * 256);
     if (no_unit) bq[s] = make_uint4(0u, 0u, 0u, 0u);
   }
+  // Step s (< ns) lies in scale group ((jb + s) >> 1) - g0 = (s + jb % 2) >> 1.
+  const bool jodd = (jb & 1) != 0;  // uniform
+#pragma unroll
+  for (int s = 0; s < kSpMaxSteps; ++s) bs[s] = jodd ? bsg[(s + 1) >> 1] : bsg[s >> 1];
 
   // Quantise A into the operand layout of the 16x16x128 instruction.
   if constexpr (!PREQ) {
@@ -669,6 +679,9 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   // are consumed (the caller refills them there).
   const bool ktail_lane = 8 * (tid & 15) >= tail_k;
   auto quant_write = [&](int j, AStage& S, auto&& after_piece) {
+    // The quantisation phase at raised wave priority: the SIMD's other wave is
+    // in its matrix phase, whose instructions run on regardless (measured ~1 %).
+    __builtin_amdgcn_s_setprio(1);
     uint32_t c[4], sw = 0;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -689,6 +702,7 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
     lds_st2x32_st64<0, 4>(aa, c[0], c[1]);
     lds_st2x32_st64<8, 12>(aa, c[2], c[3]);
     lds_st32(qs + buf * kSBuf, sw);
+    __builtin_amdgcn_s_setprio(0);
   };
   // Step j's A into LDS buffer j&1 (K tail included).
   auto quant_store = [&](int j, AStage& S) {
