@@ -70,13 +70,14 @@ def test_special_scales():
     assert_nv_tolerance(run_one(aq, as_, bq, bs), oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs), "special scales")
 
 
-@pytest.mark.parametrize("K", [16, 64])
+@pytest.mark.parametrize("K", [16, 64, 256])
 def test_every_scale_pair_exact(K):
     """Every pair of E4M3 scale bytes: row m of A holds one element 1.0 under scale
     byte m, row n of B one element 1.0 under scale byte n, so C[m, n] is the
     product of the two decoded scales, exact in fp16 where it is in range, an
     infinity past it, NaN for a NaN byte. K = 16 reads the scales byte by byte,
-    K = 64 (scale rows on 4-byte boundaries) with one dword load per row and step;
+    K = 64 (scale rows on 4-byte boundaries) with one dword load per row and step,
+    K = 256 (16-byte boundaries) with one 16-byte load per row and four steps;
     the blocks past the first hold zero codes under the scale 1.0."""
     say(f"[nvfp4] every scale pair, K={K}")
     aq = np.zeros((256, K // 2), dtype=np.uint8)
@@ -153,6 +154,48 @@ def test_padded_rows_word_scales():
     got = f16_of(C)
     assert (got[:, N:] == 12345).all(), "C padding written"
     assert_nv_tolerance(got[:, :N], oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs), "padded rows, dword scales")
+
+
+def test_padded_rows_quad_scales():
+    """Scale rows on 16-byte boundaries with K % 256 == 0 take one 16-byte scale
+    load per row and four K steps; the NaN bytes past K/16 must be ignored, across
+    several 8-step turns and a padded last turn (K = 1792: 28 steps)."""
+    say("[nvfp4] padded rows, 16-byte scale loads")
+    M, N, K = 150, 70, 1792
+    aq, as_ = synth.make_nvfp4(M, K, 57)
+    bq, bs = synth.make_nvfp4(N, K, 58)
+    lda, ldas, ldb, ldbs, ldc = K // 2 + 8, K // 16 + 16, K // 2 + 16, K // 16 + 32, N + 5
+
+    def pad(x, ld, fill):
+        out = np.full((x.shape[0], ld), fill, dtype=np.uint8)
+        out[:, :x.shape[1]] = x
+        return to_dev_u8(out)[:, :x.shape[1]]
+
+    A, As = pad(aq, lda, 0xFF), pad(as_, ldas, 0x7F)
+    B, Bs = pad(bq, ldb, 0xFF), pad(bs, ldbs, 0x7F)
+    C = torch.full((M, ldc), 12345, dtype=torch.int16, device="cuda").view(torch.float16)
+    ops.grouped_gemm_nvfp4([(A, As, B, Bs)], out_list=[C[:, :N]])
+    torch.cuda.synchronize()
+    got = f16_of(C)
+    assert (got[:, N:] == 12345).all(), "C padding written"
+    assert_nv_tolerance(got[:, :N], oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs), "padded rows, 16-byte scales")
+
+
+def test_groups_batches_quad_scales():
+    """Groups and batches that all allow the 16-byte scale loads, listed out of K order."""
+    say("[nvfp4] groups and batches, 16-byte scale loads")
+    shapes = [(100, 300, 512, 2), (257, 1024, 2048, 1), (48, 96, 256, 3), (130, 520, 4096, 1), (5, 33, 768, 2)]
+    host, dev = [], []
+    for gi, (M, N, K, L) in enumerate(shapes):
+        ops_ = [synth.make_nvfp4(M, K, 59, (gi, l)) + synth.make_nvfp4(N, K, 60, (gi, l)) for l in range(L)]
+        host.append(ops_)
+        dev.append(tuple(torch.stack([to_dev_u8(o[i]) for o in ops_]) for i in range(4)))
+    outs = ops.grouped_gemm_nvfp4(dev)
+    torch.cuda.synchronize()
+    for gi, ((M, N, K, L), ops_, c) in enumerate(zip(shapes, host, outs)):
+        for l in range(L):
+            aq, as_, bq, bs = ops_[l]
+            assert_nv_tolerance(f16_of(c[l]), oracle.nvfp4.nvfp4_gemm_ref(aq, as_, bq, bs), f"group {gi} batch {l}")
 
 
 def test_misaligned_scales_take_byte_loads():
