@@ -747,9 +747,10 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
                                                (int)((uint32_t)l * 4 + (uint32_t)(jj >> 1) * 256), 0, 0, 0);
     }
   };
-  auto dma_b = [&](int jj, int st) {
+  auto dma_b = [&](int jj, int st, int parts) {
 #pragma unroll
-    for (int p = 0; p < 6; ++p) dma_part(jj, st, p);
+    for (int p = 0; p < 6; ++p)
+      if (p < parts) dma_part(jj, st, p);
   };
   const uint32_t rlane = lds_addr(ring + wave * kRingWave) + (uint32_t)l * 16;
   const uint32_t rlane_sc = lds_addr(ring + wave * kRingWave + 4096) + (uint32_t)l * 4;
@@ -757,23 +758,36 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   // the caller has waited for). B and the first 64-k half of A are read and
   // waited for; the second half's A reads are issued before the first matrix
   // instruction and land behind the first half's.
-  auto compute = [&](int j, int st, auto&& after_pair) {
+  uint32_t sck[2] = {0u, 0u};  // B scale dwords of the current pair of steps
+  auto compute = [&](auto odd, int j, int st, auto&& after_pair) {
     const int buf = j & 1;
     uint4 a0[4], a1[4];
     const uint32_t so = (uint32_t)(st * kRingStage);
     u32x4v b00 = ring_read16<0>(rlane + so), b01 = ring_read16<2048>(rlane + so);
     u32x4v b10 = ring_read16<1024>(rlane + so), b11 = ring_read16<3072>(rlane + so);
-    uint32_t sc0 = ring_read4<0>(rlane_sc + so), sc1 = ring_read4<256>(rlane_sc + so);
+    uint32_t sc0, sc1;
+    if constexpr (!decltype(odd)::value) {
+      sc0 = ring_read4<0>(rlane_sc + so);
+      sc1 = ring_read4<256>(rlane_sc + so);
+    }
     const uint32_t sa0 = sm.as[buf][0][l];
     const int sl0 = slot32(l, 0) * 4, sl1 = slot32(l, 1) * 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) a0[i] = *reinterpret_cast<const uint4*>(&sm.a[buf][0][i][sl0]);
     // Every LDS read so far has landed; binding the ring registers to this wait
     // keeps each of their uses below it.
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(b00), "+v"(b01), "+v"(b10), "+v"(b11), "+v"(sc0), "+v"(sc1)
-                 :
-                 : "memory");
+    if constexpr (!decltype(odd)::value) {
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(b00), "+v"(b01), "+v"(b10), "+v"(b11), "+v"(sc0), "+v"(sc1)
+                   :
+                   : "memory");
+      sck[0] = sc0;
+      sck[1] = sc1;
+    } else {
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(b00), "+v"(b01), "+v"(b10), "+v"(b11) : : "memory");
+      sc0 = sck[0];
+      sc1 = sck[1];
+    }
     __builtin_amdgcn_sched_barrier(0);
     const uint32_t sa1 = sm.as[buf][1][l];
     const uint4 b[2][2] = {{__builtin_bit_cast(uint4, b00), __builtin_bit_cast(uint4, b01)},
@@ -812,7 +826,9 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
     }
   };
   // Buffer loads a wave issues per A step: 4 (bf16 A), or 2 for pre-quantised A
-  // (codes and a scale byte), and per B step 6. The waits below count the
+  // (codes and a scale byte), and per B step 6 for an even step (4 code units,
+  // 2 scale dwords) and 4 for an odd one (a scale dword covers two steps: the odd
+  // step reuses the dwords its even predecessor read). The waits below count the
   // loads issued after a ring stage's.
   constexpr int kLa = PREQ ? 2 : 4, kDb = 6;
   // K step j. Every step requests B(j+2) into the ring stage read at step j-1,
@@ -827,23 +843,30 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   // wave's MFMAs run while the other wave's VALU quantisation runs. Loads
   // issued after B(j)'s, at B(j)'s use: matrix-first A(j+1), B(j+1), A(j+2);
   // quantisation-first A(j+2), B(j+1), A(j+3).
-  auto step = [&](auto mfma_first, int j, int st, AStage& S) {
+  auto step = [&](auto mfma_first, auto odd, int j, int st, AStage& S) {
+    constexpr bool kOdd = decltype(odd)::value;
     const int st2 = st == 0 ? 2 : st - 1;
     const int jb = j + 2 < d.KT ? j + 2 : d.KT - 1;
-    auto dma_hook = [&](int p) { dma_part(jb, st2, p); };
+    // B(j+2) has the parity of j: odd steps load no scale dwords (the even step
+    // before them read the dword both share).
+    auto dma_hook = [&](int p) {
+      if (!kOdd || p < 4) dma_part(jb, st2, p);
+    };
+    // Loads issued after B(j)'s include B(j+1): 4 loads if j+1 is odd, else 6.
+    constexpr int kDbNext = kOdd ? kDb : kDb - 2;
     __builtin_amdgcn_sched_barrier(0);
     lds_barrier();  // A(j) is complete; every wave is past its reads of the other buffer
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (decltype(mfma_first)::value) {
-      wait_vm<2 * kLa + kDb>();
-      compute(j, st, dma_hook);
+      wait_vm<2 * kLa + kDbNext>();
+      compute(odd, j, st, dma_hook);
       __builtin_amdgcn_sched_barrier(0);
       quant_then_load(j + 1, j + 3, S);
     } else {
       quant_then_load(j + 1, j + 3, S);
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<2 * kLa + kDb>();
-      compute(j, st, dma_hook);
+      wait_vm<2 * kLa + kDbNext>();
+      compute(odd, j, st, dma_hook);
     }
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -852,12 +875,12 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   auto run = [&](auto mfma_first) {
     int j = 0, st = 0;
     for (; j + 1 < d.KT; j += 2) {
-      step(mfma_first, j, st, s1);
+      step(mfma_first, std::false_type{}, j, st, s1);
       st = st == 2 ? 0 : st + 1;
-      step(mfma_first, j + 1, st, s0);
+      step(mfma_first, std::true_type{}, j + 1, st, s0);
       st = st == 2 ? 0 : st + 1;
     }
-    if (j < d.KT) step(mfma_first, j, st, s1);
+    if (j < d.KT) step(mfma_first, std::false_type{}, j, st, s1);
     // No buffer-to-LDS load may still be in flight when the workgroup's LDS is
     // released. Draining inside each branch also keeps the compiler's wait
     // analysis from carrying one order's loads into the other order's loop (its
@@ -870,8 +893,8 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   };
 
   // Prologue: B(0), B(1) and A(0..2) requested, A(0) quantised into buffer 0.
-  dma_b(0, 0);
-  dma_b(d.KT > 1 ? 1 : 0, 1);
+  dma_b(0, 0, 6);
+  dma_b(d.KT > 1 ? 1 : 0, 1, 4);
   load_a(0, s0);
   quant_store(0, s0);
   load_a(1, s1);
