@@ -565,8 +565,8 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); this build measures the single-GPU "
-              "kernel and has no multi-GPU path.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library is a single-GPU kernel "
+              "library with no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     if args.workload == "rmsnorm":
         bench_rmsnorm(args)
