@@ -38,6 +38,43 @@ __global__ __launch_bounds__(256) void quant_kernel(QuantArgs a) {
   if (part == 0) __builtin_nontemporal_store((uint8_t)sb, a.s + r * a.lds + g);
 }
 
+
+// The same with 32-bit indices (M * K/8 < 2^31) and two units per thread, 256
+// threads apart: both 16-byte loads are issued before either block is
+// quantised, so each wave keeps 2 KB in flight. Past the end the load index is
+// clamped to the last unit (read, never stored). Measured at M4096 K7168:
+// 14.4-14.5 us against 16.1-16.2 us for one unit per thread with 64-bit indices.
+constexpr int kQuantUnits = 2;
+__global__ __launch_bounds__(256) void quant_kernel_u32(QuantArgs a) {
+  const uint32_t n = (uint32_t)(a.M * a.G * 4), G = (uint32_t)a.G;
+  const uint32_t t0 = blockIdx.x * (256u * kQuantUnits) + threadIdx.x;
+  u32x4 v[kQuantUnits];
+  uint32_t rr[kQuantUnits], gg[kQuantUnits];
+#pragma unroll
+  for (int i = 0; i < kQuantUnits; ++i) {
+    const uint32_t t = min(t0 + 256u * i, n - 1);
+    const uint32_t b = t >> 2, part = t & 3;
+    rr[i] = b / G;
+    gg[i] = b - rr[i] * G;
+    v[i] = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(a.x + (int64_t)rr[i] * a.ldx + 32 * gg[i] + 8 * part));
+  }
+#pragma unroll
+  for (int i = 0; i < kQuantUnits; ++i) {
+    // Every lane of a quad runs the quantisation (it exchanges values within
+    // the quad); whole quads are past the end together, since n % 4 == 0.
+    const uint32_t t = t0 + 256u * i, part = t & 3;
+    const uint32_t w[4] = {v[i].x, v[i].y, v[i].z, v[i].w};
+    uint32_t sb;
+    const uint32_t codes = mx::quant8_quad<true>(w, sb);
+    if (t < n) {
+      __builtin_nontemporal_store(codes,
+                                  reinterpret_cast<uint32_t*>(a.q + (int64_t)rr[i] * a.ldq + 16 * gg[i] + 4 * part));
+      if (part == 0) __builtin_nontemporal_store((uint8_t)sb, a.s + (int64_t)rr[i] * a.lds + gg[i]);
+    }
+  }
+}
+
 }  // namespace
 
 extern "C" const char* mxfp4_status_str(int status) {
@@ -64,6 +101,10 @@ extern "C" int mxfp4_quant(const void* x, int64_t ldx, void* q, int64_t ldq, voi
   QuantArgs a{(const uint16_t*)x, ldx, (uint8_t*)q, ldq, (uint8_t*)s, lds, M, K / 32};
   const int64_t n = M * (K / 32) * 4;  // four lanes per block
   void* args[] = {&a};
+  if (n < ((int64_t)1 << 31))
+    return mxh::launch_status(hipLaunchKernel((const void*)quant_kernel_u32,
+                                              dim3((unsigned)mxh::cdiv(n, 256 * kQuantUnits)), dim3(256), args, 0,
+                                              (hipStream_t)stream));
   return mxh::launch_status(hipLaunchKernel((const void*)quant_kernel, dim3((unsigned)mxh::cdiv(n, 256)), dim3(256),
                                             args, 0, (hipStream_t)stream));
 }
