@@ -502,7 +502,7 @@ def bench_nvfp4(args):
         bound, achieved, peak, unit = "hbm", gbs, HBM_PEAK_GBS, "GB/s"
     out = dict(metric=NV_METRIC, value=round(achieved, 3), unit=unit, n_gpus=1, steps=args.steps,
                warmup=args.warmup, ms_per_step=round(ms_step, 6), higher_is_better=True, scaling="weak",
-               vs_baseline=None, dtype="nvfp4 (e2m1 x e4m3 per 16; exact bf16 products, fp32 accumulate, fp16 out)",
+               vs_baseline=None, dtype="nvfp4 (e2m1 x e4m3 per 16; exact fp16 products, fp32 accumulate, fp16 out)",
                data="synthetic",
                config=dict(workload="nvfp4_grouped", seed=seed, groups=[dict(M=M, N=N, K=K, L=L) for M, N, K, L in shapes],
                            cache="warm (1 set)" if R == 1 else f"cold ({R} rotated operand sets)",

@@ -12,8 +12,12 @@
  * zero is kept. Sources: kernelbot amd-mxfp4-mm submission 517169 (module
  * docstring: E2M1 grid, per-1x32 scales, low nibble first; the fused
  * quant + GEMM plan), submission 683203 (docstring: scale byte 127 = 2^0,
- * allocation-free hot path), the OCP MX v1.0 specification (shared-exponent
- * rule).
+ * allocation-free hot path). The pages state the shared exponent four
+ * different ways (517169's docstring, its scale helper's docstring and its
+ * code, and 683203's call into a helper whose body is absent) and round ties
+ * upward; the rule taken here instead is the conversion rule of the OCP MX
+ * v1.0 specification with round-to-nearest-even, the reading this library is
+ * built and tested to.
  *
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers unless stated otherwise; the caller owns
@@ -75,10 +79,13 @@ int mxfp4_quant(const void* x, int64_t ldx, void* q, int64_t ldq, void* s, int64
  * quantisation that page 683203 names (docstring trick 1, and the comment above
  * ``_quant_shuffled``) as the step before the GEMM in a transformer layer; the
  * pages print none of its arithmetic, so the norm is the standard one:
- *   ss  = sum_k x[k]^2 in float64, in a fixed order (64 lane sums, lane t
- *         adding k = 512c + 8t + e for c = 0, 1, ... and e = 0..7 in that
- *         order, then a halving tree over the lanes), so results are
- *         reproducible bit for bit;
+ *   ss  = sum_k x[k]^2, the exact sum taken in float64; the library adds the
+ *         (exact) squares in one fixed order (64 lane sums, lane t adding
+ *         k = 512c + 8t + e for c = 0, 1, ... and e = 0..7 in that order, then
+ *         a halving tree over the lanes), so results are reproducible bit for
+ *         bit, and ss is within (K-1)*2^-53 relative of the exact sum; inv
+ *         below differs from the value the exact sum (rounded once) gives only
+ *         when that difference crosses an fp32 rounding boundary of inv;
  *   inv = fp32(1 / sqrt(ss / K + eps)), float64 steps;
  *   y   = bf16(fp32(fp32(x * inv) * w)), rounding to nearest even;
  *   (q, s) = the MXFP4 quantisation of y, exactly as mxfp4_quant.

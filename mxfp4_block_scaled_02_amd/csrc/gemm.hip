@@ -13,23 +13,26 @@
 // writes and the operand reads free of bank conflicts. B arrives pre-packed in
 // 32x64 operand units (mxfp4_pack_B), one 16-byte load per lane per unit.
 //
-// Two kernels:
-//  * skinny (M <= 64): a 1024-thread workgroup owns MS rows x 16*NB columns of C
-//    over the whole K; its 16 waves split K, each quantises its own A slice into
-//    a private LDS operand tile and runs the 16x16x128 instruction, and the 16
-//    partial tiles are summed in LDS. No cross-workgroup reduction: on this GPU a
-//    split-K hand-off through memory costs several microseconds, more than the
-//    whole skinny GEMM.
-//  * tiled (larger M): a 512-thread workgroup (8 waves, one per CU) owns a
-//    128 x 512 tile of C. Per 128-wide K step the workgroup quantises the
-//    128x128 bf16 A block once into a double-buffered LDS tile; wave w computes
-//    all 128 rows x columns [64w, 64w+64) with the 32x32x64 instruction from that
-//    shared A and its own B units, which stream from global memory straight into
-//    registers one K step ahead. The two waves sharing a SIMD run their matrix
-//    and quantisation phases in opposite orders so the two overlap. The C tile
-//    leaves through a per-wave LDS staging block as 16-byte row stores.
-//    Workgroups are ordered so that the ones sharing an XCD (and its L2) share A
-//    rows and B columns.
+// Three kernels:
+//  * split-K (M <= 16): the grid is 64-column tiles x K splits. Each workgroup
+//    issues all of its loads at once, quantises its A block once into LDS and
+//    runs the 16x16x128 instruction; the splits of a tile hand their fp32
+//    partials to the tile's last split (the owner) through the workspace,
+//    which sums them in split order and stores bf16 C.
+//  * skinny (16 < M <= 64): a 1024-thread workgroup owns MS rows x 16*NB
+//    columns of C over the whole K; its 16 waves split K, each quantises its own
+//    A slice into a private LDS operand tile and runs the 16x16x128 instruction,
+//    and the 16 partial tiles are summed in LDS.
+//  * tiled (larger M, and every grouped problem): a 512-thread workgroup (8
+//    waves, one per CU) owns a 128 x 512 tile of C. Per 128-wide K step the
+//    workgroup quantises the 128x128 bf16 A block once into a double-buffered
+//    LDS tile; wave w computes all 128 rows x columns [64w, 64w+64) with the
+//    32x32x64 instruction from that shared A and its own B units, which arrive
+//    by buffer-to-LDS loads in a three-stage per-wave LDS ring two K steps
+//    ahead. The two waves sharing a SIMD run their matrix and quantisation
+//    phases in opposite orders so the two overlap. The C tile leaves through a
+//    per-wave LDS staging block as 16-byte row stores. Workgroups are ordered
+//    so that the ones sharing an XCD (and its L2) share A rows and B columns.
 #include <algorithm>
 #include <type_traits>
 
@@ -1047,12 +1050,21 @@ Operand make_operand_q(const void* Aq, int64_t ldaq, const void* As, int64_t lda
   return o;
 }
 
+// The kernels address A and packed B through buffer resources with 32-bit
+// offsets: an A window spans at most kTBM rows from its base row, and one packed
+// 32-column tile of B spans ceil(K/64) KB. Both must stay below 2^31 bytes, or
+// the range check would silently clip in-range elements.
+bool offsets_fit(int64_t ld_elems, int64_t K) {
+  return (kTBM * ld_elems + K) * 2 < ((int64_t)1 << 31) && mxh::cdiv(K, 64) * 1024 < ((int64_t)1 << 31);
+}
+
 int check_problem(const void* A, int64_t lda, const void* Bp, const void* C, int64_t ldc, int64_t M, int64_t N,
                   int64_t K) {
   if (!A || !Bp || !C) return MXFP4_ERR_NULL;
   if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || M > mxh::kMaxDim || N > mxh::kMaxDim || K > mxh::kMaxDim)
     return MXFP4_ERR_SHAPE;
   if (lda < K || ldc < N) return MXFP4_ERR_SHAPE;
+  if (!offsets_fit(lda, K)) return MXFP4_ERR_SHAPE;
   if (!mxh::aligned(A, 16) || (lda * 2) % 16 != 0 || !mxh::aligned(Bp, 16) || !mxh::aligned(C, 2))
     return MXFP4_ERR_ALIGN;
   return MXFP4_OK;
@@ -1209,6 +1221,7 @@ extern "C" int gemm_a4w4(const void* Aq, int64_t ldaq, const void* As, int64_t l
     return MXFP4_ERR_SHAPE;
   if (ldaq < K / 2 || ldas < K / 32 || ldc < N) return MXFP4_ERR_SHAPE;
   if (ldaq > (int64_t)1 << 24 || ldas > (int64_t)1 << 24) return MXFP4_ERR_SHAPE;  // 32-bit buffer offsets over 128 rows
+  if (!offsets_fit(0, K)) return MXFP4_ERR_SHAPE;                                  // one packed B tile below 2^31 bytes
   if (!mxh::aligned(Aq, 16) || ldaq % 16 != 0 || !mxh::aligned(Bp, 16) || !mxh::aligned(C, 2)) return MXFP4_ERR_ALIGN;
   if (mxh::cdiv(M, kTBM) * mxh::cdiv(N, kTBN) > INT32_MAX) return MXFP4_ERR_SHAPE;
   const Operand o = make_operand_q(Aq, ldaq, As, ldas, Bp, C, ldc, M, N, K);

@@ -70,6 +70,7 @@ extern "C" int mxfp4_pack_B(const void* bq, const void* bs, int64_t N, int64_t K
   PackArgs a{(const uint8_t*)bq, (const uint8_t*)bs, (uint8_t*)out, N, K, g.NT, g.KU, g.KG};
   void* args[] = {&a};
   const int64_t n1 = g.NT * g.KU * 64, n2 = g.NT * g.KG * 64;
+  if (mxh::cdiv(n1, 256) > INT32_MAX) return MXFP4_ERR_SHAPE;  // grid size limit (n2 <= n1)
   hipError_t e = hipLaunchKernel((const void*)pack_codes_kernel, dim3((unsigned)mxh::cdiv(n1, 256)), dim3(256), args,
                                  0, (hipStream_t)stream);
   if (e != hipSuccess) return MXFP4_ERR_HIP;

@@ -100,6 +100,7 @@ extern "C" int mxfp4_quant(const void* x, int64_t ldx, void* q, int64_t ldq, voi
   if (!mxh::aligned(x, 16) || (ldx * 2) % 16 != 0 || !mxh::aligned(q, 16) || ldq % 16 != 0) return MXFP4_ERR_ALIGN;
   QuantArgs a{(const uint16_t*)x, ldx, (uint8_t*)q, ldq, (uint8_t*)s, lds, M, K / 32};
   const int64_t n = M * (K / 32) * 4;  // four lanes per block
+  if (mxh::cdiv(n, 256) > INT32_MAX) return MXFP4_ERR_SHAPE;  // grid size limit
   void* args[] = {&a};
   if (n < ((int64_t)1 << 31))
     return mxh::launch_status(hipLaunchKernel((const void*)quant_kernel_u32,

@@ -9,7 +9,10 @@
 // pass covers 1 KB of the row. Pass one sums the squares in float64, each lane
 // in pass-then-element order, and the 64 lane sums meet in a halving tree
 // (S[t] += S[t+s], s = 32 .. 1): a fixed order, so the result, and with it
-// every quantised code, is the same on every run. inv = fp32(1 / sqrt(ss/K +
+// every quantised code, is the same on every run. The squares are exact; the
+// sum is within (K-1)*2^-53 relative of the exact sum of squares, which is
+// what the norm's definition asks for (an fp32 inv that this moves across a
+// rounding boundary would differ from the exact one). inv = fp32(1 / sqrt(ss/K +
 // eps)) with float64 steps; pass two forms y = bf16((x * inv) * w) in fp32 and
 // quantises it with the lane-quad routine of the GEMM, storing codes and scale
 // bytes row-major as mxfp4_quant does.

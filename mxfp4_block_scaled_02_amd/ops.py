@@ -13,7 +13,9 @@ import threading
 
 import torch
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so")
+# MXFP4_LIB names another build of the same library (the sanitizer check build);
+# it must exist like the default one.
+_LIB_PATH = os.environ.get("MXFP4_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxfp4.so")
 _lib = None
 _lock = threading.Lock()
 
@@ -107,13 +109,20 @@ def _require(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
         raise ValueError(f"{name} must be 2-D with unit column stride")
 
 
-# Workspace per device: zeroed once at allocation, grown on demand. The library
-# leaves it zeroed after every call, so it is reused without clearing.
+# Workspace per (device, stream): zeroed once at allocation, grown on demand.
+# The library leaves it zeroed after every call, so it is reused without
+# clearing. Calls that may overlap need distinct workspaces; calls on one stream
+# never overlap, so one buffer per stream is enough. A grown buffer replaces the
+# old one only after the stream's earlier work (which may still use the old
+# buffer) is ordered before its release by the caching allocator.
 _ws: dict = {}
 
 
-def workspace(device: torch.device, nbytes: int) -> torch.Tensor:
-    key = device.index if device.index is not None else torch.cuda.current_device()
+def workspace(device: torch.device, nbytes: int, stream: int | None = None) -> torch.Tensor:
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    key = (dev, int(stream))
     buf = _ws.get(key)
     if nbytes > 0 and (buf is None or buf.numel() < nbytes):
         buf = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
@@ -188,9 +197,10 @@ def gemm(a: torch.Tensor, bp: torch.Tensor, N: int, out: torch.Tensor | None = N
         out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
     _require(out, torch.bfloat16, "out")
     wsz = int(lib().gemm_a4w4_workspace_bytes(M, N, K))
-    ws = workspace(a.device, wsz)
+    st = _stream(a)
+    ws = workspace(a.device, wsz, st)
     _check(lib().gemm_a4w4_fused(a.data_ptr(), a.stride(0), bp.data_ptr(), out.data_ptr(), out.stride(0), M, N, K,
-                                 ws.data_ptr() if wsz else None, ws.numel() if wsz else 0, _stream(a)),
+                                 ws.data_ptr() if wsz else None, ws.numel() if wsz else 0, st),
            "gemm_a4w4_fused")
     return out
 
@@ -211,10 +221,11 @@ def gemm_a4w4(aq: torch.Tensor, a_scale: torch.Tensor, bp: torch.Tensor, N: int,
         out = torch.empty((M, N), dtype=torch.bfloat16, device=aq.device)
     _require(out, torch.bfloat16, "out")
     wsz = int(lib().gemm_a4w4_workspace_bytes(M, N, K))
-    ws = workspace(aq.device, wsz)
+    st = _stream(aq)
+    ws = workspace(aq.device, wsz, st)
     _check(lib().gemm_a4w4(aq.data_ptr(), aq.stride(0), a_scale.data_ptr(), a_scale.stride(0), bp.data_ptr(),
                            out.data_ptr(), out.stride(0), M, N, K, ws.data_ptr() if wsz else None,
-                           ws.numel() if wsz else 0, _stream(aq)), "gemm_a4w4")
+                           ws.numel() if wsz else 0, st), "gemm_a4w4")
     return out
 
 
@@ -236,9 +247,10 @@ def grouped_gemm(a_list, bp_list, N: int, out_list=None):
             raise ValueError("all groups share K")
         arr[g] = Group(a.data_ptr(), a.stride(0), bp.data_ptr(), c.data_ptr(), c.stride(0), a.shape[0])
     wsz = int(lib().grouped_gemm_a4w4_workspace_bytes(arr, G, N, K))
-    ws = workspace(a_list[0].device, wsz)
-    _check(lib().grouped_gemm_a4w4(arr, G, N, K, ws.data_ptr() if wsz else None, ws.numel() if wsz else 0,
-                                   _stream(a_list[0])), "grouped_gemm_a4w4")
+    st = _stream(a_list[0])
+    ws = workspace(a_list[0].device, wsz, st)
+    _check(lib().grouped_gemm_a4w4(arr, G, N, K, ws.data_ptr() if wsz else None, ws.numel() if wsz else 0, st),
+           "grouped_gemm_a4w4")
     return out_list
 
 

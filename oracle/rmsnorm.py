@@ -13,12 +13,11 @@ followed by the MXFP4 rule of ``oracle.mx.quant_mx``.
 Readings taken because the pages are silent (each also listed in the design
 notes):
   - w is a bf16 vector [K]; eps is an fp32 value > 0.
-  - The sum of squares is taken in float64 in one fixed order, so that every
-    implementation decides the quantised integers identically. Each x^2 is exact
-    in float64. Lane t of 64 accumulates, in this order, its elements
-    k = 512c + 8t + e (c = 0, 1, ...; e = 0..7; k < K). The 64 lane sums are then
-    combined by a halving tree: S[t] += S[t + s] for s = 32, 16, 8, 4, 2, 1 and
-    t < s. The sum is S[0].
+  - The sum of squares is the exact real sum of x_k^2 over the row, rounded
+    once to float64 (nearest, ties to even). Each x_k^2 of a bf16 x_k is exact
+    in float64 (8-bit significands), and math.fsum returns the correctly
+    rounded sum of its float64 terms, so the result is independent of any
+    summation order.
   - inv = fp32(1 / sqrt(ss / K + eps)). Each float64 operation is correctly
     rounded, and so is the final conversion to fp32.
   - y_k = bf16(fp32(fp32(x_k * inv) * w_k)), each rounding to nearest, ties to
@@ -28,34 +27,20 @@ notes):
 """
 from __future__ import annotations
 
+import math
+
 import numpy as np
 
 from .mx import bf16_bits_to_f64, f64_to_bf16_bits, quant_mx
 
-LANES = 64      # partial sums, one per lane of a 64-wide wave
-CHUNK = 8       # consecutive elements a lane takes per pass
-PASS = LANES * CHUNK  # 512 elements per pass over the row
-
 
 def rms_sum_squares(x_bits: np.ndarray) -> np.ndarray:
-    """Per-row sum of squares, float64, in the fixed order stated in the module docstring."""
+    """Per-row sum of x^2: the exact sum rounded once to float64."""
     x = bf16_bits_to_f64(np.asarray(x_bits, dtype=np.uint16))
     if x.ndim != 2:
         raise ValueError("rms_sum_squares expects a 2-D [R, K] bf16 bit array")
-    R, K = x.shape
-    passes = -(-K // PASS)
-    xx = np.zeros((R, passes * PASS), dtype=np.float64)
-    xx[:, :K] = x * x  # exact; padding adds +0.0, which leaves every sum unchanged
-    xx = xx.reshape(R, passes, LANES, CHUNK)
-    lane = np.zeros((R, LANES), dtype=np.float64)
-    for c in range(passes):          # lane order: pass by pass ...
-        for e in range(CHUNK):       # ... and element by element within a pass
-            lane = lane + xx[:, c, :, e]
-    s = LANES // 2
-    while s >= 1:                    # halving tree over the lanes
-        lane[:, :s] = lane[:, :s] + lane[:, s:2 * s]
-        s //= 2
-    return lane[:, 0].copy()
+    sq = x * x  # exact: a bf16 square has at most 16 significant bits
+    return np.array([math.fsum(row) for row in sq], dtype=np.float64)
 
 
 def rms_inv(ss: np.ndarray, K: int, eps: float) -> np.ndarray:

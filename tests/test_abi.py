@@ -89,6 +89,7 @@ OK_Q = dict(x=P, ldx=64, q=P, ldq=32, s=P, lds=2, M=4, K=64)
     (dict(x=None), 1), (dict(q=None), 1), (dict(s=None), 1),
     (dict(M=0), 2), (dict(K=0), 2), (dict(K=48), 2), (dict(ldx=32), 2), (dict(ldq=16), 2), (dict(lds=1), 2),
     (dict(x=P + 2), 3), (dict(q=P + 8), 3), (dict(ldx=68), 3), (dict(ldq=40), 3),
+    (dict(M=1 << 30, K=1 << 30, ldx=1 << 30, ldq=1 << 29, lds=1 << 25), 2),  # grid past 2^31 workgroups
 ])
 def test_quant_validation(change, status):
     a = dict(OK_Q, **change)
@@ -115,6 +116,7 @@ def test_rmsnorm_quant_validation(change, status):
 @pytest.mark.parametrize("change,status", [
     (dict(bq=None), 1), (dict(out=None), 1), (dict(N=0), 2), (dict(K=40), 2),
     (dict(bq=P + 4), 3), (dict(out=P + 1), 3), (dict(out_bytes=1000), 7),
+    (dict(N=1 << 30, K=1 << 30, out_bytes=1 << 62), 2),  # grid past 2^31 workgroups
 ])
 def test_pack_B_validation(change, status):
     a = dict(dict(bq=P, bs=P, N=16, K=128, out=P, out_bytes=2 * 1024 + 256), **change)
@@ -129,6 +131,9 @@ OK_G = dict(A=P, lda=7168, Bp=P, C=P, ldc=2112, M=16, N=2112, K=7168, ws=P, wsb=
     (dict(A=None), 1), (dict(Bp=None), 1), (dict(C=None), 1),
     (dict(M=0), 2), (dict(N=0), 2), (dict(K=7000), 2), (dict(lda=7000), 2), (dict(ldc=2000), 2),
     (dict(M=1 << 31), 2),
+    # 32-bit buffer offsets: a 128-row A window and a packed 32-column B tile stay below 2^31 bytes
+    (dict(lda=1 << 23), 2), (dict(lda=8388552), 2), (dict(M=17, lda=1 << 23), 2),
+    (dict(M=4096, lda=1 << 23), 2), (dict(K=1 << 27, lda=1 << 27), 2), (dict(K=(1 << 27) - 64, lda=(1 << 27) - 64), 2),
     (dict(A=P + 2), 3), (dict(lda=7172), 3), (dict(Bp=P + 8), 3), (dict(C=P + 1), 3),
     (dict(ws=None), 4), (dict(wsb=1024), 4), (dict(ws=P + 16), 3),
 ])
@@ -146,6 +151,7 @@ OK_Q4 = dict(Aq=P, ldaq=3584, As=P, ldas=224, Bp=P, C=P, ldc=2112, M=16, N=2112,
     (dict(Aq=None), 1), (dict(As=None), 1), (dict(Bp=None), 1), (dict(C=None), 1),
     (dict(M=0), 2), (dict(K=7000), 2), (dict(ldaq=3000), 2), (dict(ldas=200), 2), (dict(ldc=2000), 2),
     (dict(ldaq=1 << 25), 2),
+    (dict(K=1 << 27, ldaq=1 << 24, ldas=1 << 22), 2),  # a packed B tile of ceil(K/64) KB reaches 2^31 bytes
     (dict(Aq=P + 8), 3), (dict(ldaq=3592), 3), (dict(Bp=P + 8), 3), (dict(C=P + 1), 3),
     (dict(ws=None), 4), (dict(wsb=1024), 4), (dict(ws=P + 16), 3),
 ])
@@ -169,6 +175,8 @@ def test_grouped_validation():
     assert L.grouped_gemm_a4w4(g, 2, 4096, 7168, None, 0, None) == 1
     g[1] = ops.Group(P + 2, 7168, P, P, 4096, 64)
     assert L.grouped_gemm_a4w4(g, 2, 4096, 7168, None, 0, None) == 3
+    g[1] = ops.Group(P, 1 << 23, P, P, 4096, 64)  # a 128-row window of A past 2^31 bytes
+    assert L.grouped_gemm_a4w4(g, 2, 4096, 7168, None, 0, None) == 2
 
 
 def _mnk(**kw):
@@ -182,6 +190,7 @@ def _mnk(**kw):
     ([_mnk(A=None)], 1), ([_mnk(C=None)], 1),
     ([_mnk(L=0)], 2), ([_mnk(K=48)], 2), ([_mnk(lda=256)], 2), ([_mnk(ldc=32)], 2), ([_mnk(M=0)], 2),
     ([_mnk(A=P + 8)], 3), ([_mnk(Bp=P + 4)], 3), ([_mnk(lda=516)], 3),
+    ([_mnk(lda=1 << 23)], 2),  # 32-bit buffer offsets over a 128-row A window
     # batches: C slices must not overlap, B slices must hold a packed image, strides keep alignment
     ([_mnk(L=2, strideA=512 * 16, strideB=1 << 20, strideC=16 * 64 - 1)], 2),
     ([_mnk(L=2, strideA=512 * 16, strideB=100, strideC=16 * 64)], 2),

@@ -4,7 +4,7 @@ E2M1 with one E4M3 scale per 16 along K, float16 C) with the CPU oracle, on an M
 Each C must be within |C - C_ref| <= 2^-7 |C_ref| + 1e-3 max|C_ref| of the
 oracle's fp64 product of the dequantised operands rounded to float16, over the
 finite entries; infinities and NaNs must sit at the same places with the same
-sign. The kernel's products are exact (bf16 holds E2M1 x E4M3 exactly), so the
+sign. The kernel's products are exact (fp16 holds E2M1 x E4M3 exactly), so the
 only differences are fp32 accumulation and the one float16 rounding.
 """
 import numpy as np

@@ -4,9 +4,10 @@ The pages name a kernel that fuses an RMSNorm with the MXFP4 quantisation
 (kernelbot amd-mxfp4-mm submission 683203, docstring trick 1 and the comment
 above ``_quant_shuffled``) but print none of its arithmetic, so these pins come
 from the definition y = x / sqrt(mean(x^2) + eps) * w and from mathematics:
-exact integer sums, the rounding-error bound of a float64 sum against the exact
-rational sum, a closed form for constant rows, invariance under power-of-two
-scaling of x, linearity in w, unit mean square, zero rows, and brute force over
+exact integer sums; the sum of squares equal to the exact rational sum rounded
+once, on rows whose squares span many binades (where every fixed-order float64
+sum loses bits); a closed form for constant rows; invariance under power-of-two
+scaling of x; linearity in w; unit mean square; zero rows; and brute force over
 a tiny row with Python's correctly rounded arithmetic. The ``test_planted_*``
 tests plant plausible mistakes in the oracle and check that the pins catch them.
 """
@@ -35,18 +36,41 @@ def test_sum_of_squares_exact_on_integers():
     assert np.array_equal(ss, (x.astype(np.int64) ** 2).sum(axis=1).astype(np.float64))
 
 
+def exact_sum_squares(bits):
+    """The exact rational sum of x^2 over a bf16 row, rounded once to float64 (Python's
+    int / int division is correctly rounded)."""
+    x = mx.bf16_bits_to_f64(bits)
+    tot = sum(Fraction(float(v)) ** 2 for v in x)
+    return tot.numerator / tot.denominator
+
+
+def wide_rows(rng, K):
+    """Rows whose squares span many binades, where any fixed-order float64 sum loses bits:
+    one huge element among ones (2^54 + n with every +1 absorbed by naive summation), a
+    row with exponents spread over +-40 binades, and one with tiny and huge values mixed."""
+    big = np.ones(K)
+    big[0] = 2.0**27
+    spread = rng.standard_normal(K) * np.exp2(rng.integers(-40, 40, size=K))
+    mixed = rng.standard_normal(K) * np.where(rng.random(K) < 0.01, 2.0**30, 2.0**-20)
+    return [bf16_bits(big), bf16_bits(spread), bf16_bits(mixed)]
+
+
 @pytest.mark.parametrize("K", [32, 96, 512, 1056, 7168])
-def test_sum_of_squares_within_float64_bound(K):
+def test_sum_of_squares_is_the_exact_sum_rounded_once(K):
     rng = np.random.default_rng(K)
-    rows = [rand_rows(rng, 1, K)[0], rand_rows(rng, 1, K, 1e3)[0]]
-    wide = rng.standard_normal(K) * np.exp2(rng.integers(-40, 40, size=K))
-    rows.append(bf16_bits(wide))
-    for bits in rows:
-        ss = rn.rms_sum_squares(bits[None, :])[0]
-        x = mx.bf16_bits_to_f64(bits)
-        exact = sum(Fraction(float(v)) ** 2 for v in x)
-        # recursive summation of n non-negative terms: |error| <= (n-1) u sum, u = 2^-53
-        assert abs(Fraction(float(ss)) - exact) <= Fraction(K - 1, 2**53) * exact
+    rows = [rand_rows(rng, 1, K)[0], rand_rows(rng, 1, K, 1e3)[0]] + wide_rows(rng, K)
+    ss = rn.rms_sum_squares(np.stack(rows))
+    for i, bits in enumerate(rows):
+        assert ss[i] == exact_sum_squares(bits), (K, i)
+
+
+def test_sum_of_squares_absorbs_nothing():
+    """2^54 plus K-1 ones: the exact sum 2^54 + K - 1 is a float64 (K - 1 is a multiple of 4, the
+    spacing at 2^54); a left-to-right float64 sum would stay at 2^54."""
+    K = 7169
+    x = np.ones((1, K))
+    x[0, 0] = 2.0**27
+    assert rn.rms_sum_squares(bf16_bits(x))[0] == 2.0**54 + (K - 1)
 
 
 def test_constant_row_closed_form():
@@ -124,6 +148,28 @@ def test_rejects_bad_eps():
 
 
 # -- planted mistakes: each must break at least one pin above --------------------------
+
+def test_planted_fixed_order_sum_is_caught(monkeypatch):
+    """A float64 sum in any fixed order (here left to right) is not the exact sum rounded once."""
+    def naive(xb):
+        x = mx.bf16_bits_to_f64(xb)
+        out = np.zeros(x.shape[0])
+        for k in range(x.shape[1]):
+            out = out + x[:, k] * x[:, k]
+        return out
+    monkeypatch.setattr(rn, "rms_sum_squares", naive)
+    with pytest.raises(AssertionError):
+        test_sum_of_squares_absorbs_nothing()
+    with pytest.raises(AssertionError):
+        test_sum_of_squares_is_the_exact_sum_rounded_once(7168)
+
+
+def test_planted_pairwise_sum_is_caught(monkeypatch):
+    """numpy's pairwise summation is another fixed order: caught too."""
+    monkeypatch.setattr(rn, "rms_sum_squares", lambda xb: (mx.bf16_bits_to_f64(xb) ** 2).sum(axis=1))
+    with pytest.raises(AssertionError):
+        test_sum_of_squares_is_the_exact_sum_rounded_once(7168)
+
 
 def test_planted_missing_sqrt_is_caught(monkeypatch):
     monkeypatch.setattr(rn, "rms_inv", lambda ss, K, eps: (1.0 / (ss / K + eps)).astype(np.float32))
