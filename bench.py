@@ -1,18 +1,27 @@
 """Benchmark of the fused MXFP4 quant + a4w4 GEMM on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload skinny]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
 A step is one gemm_a4w4_fused call (dynamic quantisation of A, the
 block-scaled FP4 GEMM, bf16 store) on one batch of synthetic input; B is
 quantised and packed once beforehand (offline, untimed). Inputs are resident in
-HBM before the timed region. To measure HBM rather than the 256 MB Infinity
-Cache, the timed steps rotate through enough distinct operand sets (A, packed
-B, C) to exceed 512 MB. The K timed steps are captured once in a HIP graph and
-replayed between two HIP events on the launching stream, after W untimed warm-up
-steps. Prints ONE JSON line.
+HBM before the timed region.
 
-The CPU oracle is timed beside it (the cpu_baseline leg, rank 0 only) on a
-bounded sample of the same workload.
+By default the line's headline is the largest configuration the metric spans,
+square M=N=4096 K=7168 (MFMA-bound: TFLOP/s against the dense MXFP4 peak), and
+the other configurations (skinny, stress, tiny, grouped) ride on the same line
+under "workloads", each timed the same way. --workload NAME times one workload.
+
+Timing: W untimed warm-up steps; the K steps are captured once in a HIP graph,
+replayed once untimed, and replayed again between two HIP events on the
+launching stream. Cold runs (the default) rotate through enough distinct
+operand sets (A, packed B, C) to exceed 512 MB, whatever K is, and read 512 MB
+of another buffer just before the timed replay, so that no operand is left in
+the 256 MB Infinity Cache by the untimed runs. Prints ONE JSON line.
+
+The CPU oracle is timed beside it (the cpu_baseline leg) on a bounded sample of
+the headline workload, its BLAS on the CPUs this process may use (capped by
+OMP_NUM_THREADS when set).
 """
 from __future__ import annotations
 
@@ -51,15 +60,19 @@ def alg_flops(M, N, K):
     return 2 * M * N * K
 
 
+WORKLOADS = ["tiny", "skinny", "stress", "square", "grouped", "rmsnorm", "grouped_mnk", "skinny_shard8", "nvfp4_grouped"]
+HEADLINE = "square"                       # the largest single-GPU configuration the metric spans
+EXTRAS = ["skinny", "stress", "tiny", "grouped"]
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
-    p.add_argument("--workload", default="skinny",
-                   choices=["tiny", "skinny", "stress", "square", "grouped", "rmsnorm", "grouped_mnk", "skinny_shard8",
-                            "nvfp4_grouped"],
-                   help="rmsnorm times mxfp4_rmsnorm_quant (RMSNorm fused with MXFP4 quantisation) at M4096 K7168; "
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=None, choices=WORKLOADS,
+                   help="time one workload only (default: the square headline plus skinny, stress, tiny and grouped "
+                        "as extra keys of the same line). rmsnorm times mxfp4_rmsnorm_quant at M4096 K7168; "
                         "grouped_mnk times grouped_gemm_a4w4_mnk on seeded groups with their own (M, N, K, L)")
     p.add_argument("--seed", type=int, default=None)
     p.add_argument("--warm-cache", action="store_true", help="reuse one operand set (Infinity Cache resident)")
@@ -198,14 +211,46 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(w, unit, budget_s=12.0):
+def host_threads():
+    """Threads for the oracle's BLAS: the CPUs this process may run on, capped by OMP_NUM_THREADS when the
+    environment sets it (the share of a shared host this job is given). Returns (threads, affinity CPUs)."""
+    aff = len(os.sched_getaffinity(0))
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    n = min(aff, int(cap)) if cap.isdigit() and int(cap) > 0 else aff
+    return n, aff
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def time_oracle(fn, budget_s=12.0, max_runs=50):
+    """Median wall time of fn() over at least 3 runs (1 if a run exceeds 60 s), within about budget_s,
+    with the BLAS thread pool set to host_threads() (numpy's fp64 matmul is the only threaded step)."""
+    from threadpoolctl import threadpool_limits
+    n, aff = host_threads()
+    times = []
+    with threadpool_limits(limits=n):
+        t_end = time.perf_counter() + budget_s
+        while True:
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+            if times[-1] > 60 or (len(times) >= 3 and time.perf_counter() > t_end) or len(times) >= max_runs:
+                break
+    return float(np.median(times)), len(times), n, aff
+
+
+def cpu_baseline(w, unit):
     """Time the oracle (untuned) on a bounded sample of the workload, scaled to the metric's unit."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
     name = w["name"]
     if name == "grouped":
         a, b = w["A"][0], w["B"][0]
@@ -215,21 +260,69 @@ def cpu_baseline(w, unit, budget_s=12.0):
     N = b.shape[0]
     bq, bs = oracle.quant_mx(b)  # B's quantisation is offline for the GPU too: excluded
     rows = np.arange(min(M, 64))
-    sample_desc = (f"oracle gemm_ref (quant A, dequant A and B, fp64 matmul, bf16 round) on rows 0..{len(rows) - 1} "
-                   f"of A against the full B (N={N}, K={K})")
-    times = []
-    t_end = time.perf_counter() + budget_s
-    while True:
-        t0 = time.perf_counter()
-        oracle.gemm_ref(a[rows], bq, bs)
-        times.append(time.perf_counter() - t0)
-        if time.perf_counter() > t_end or len(times) >= 200:
-            break
-    t = float(np.median(times))
+    t, runs, n, aff = time_oracle(lambda: oracle.gemm_ref(a[rows], bq, bs))
     m = len(rows)
     value = alg_flops(m, N, K) / t / 1e12 if unit == "TFLOP/s" else alg_bytes(m, N, K) / t / 1e9
-    return dict(value=round(value, 6), unit=unit, cores=int(threads), kind="oracle",
-                sample=f"{sample_desc}; median of {len(times)} runs, {t * 1e3:.1f} ms each")
+    return dict(value=round(value, 6), unit=unit, cores=n, kind="oracle",
+                sample=f"oracle gemm_ref (quant A, dequant A and B, fp64 matmul, bf16 round) on rows 0..{m - 1} of "
+                       f"{'group 0' if name == 'grouped' else 'A'} against the full B (N={N}, K={K}); median of "
+                       f"{runs} runs, {t * 1e3:.1f} ms each; numpy's BLAS on {n} threads, the rest single-threaded",
+                affinity_cpus=aff, cpu_model=cpu_model())
+
+
+_evict = None
+
+
+def evict_infinity_cache():
+    """Read 512 MB (twice the 256 MB Infinity Cache) so no operand stays cached from the untimed runs."""
+    import torch
+    global _evict
+    if _evict is None:
+        _evict = torch.ones(ROTATE_BYTES // 4, dtype=torch.int32, device="cuda")
+    _evict.sum()
+
+
+def n_sets(args, set_bytes):
+    """Operand sets to rotate through: one (warm) or enough to exceed ROTATE_BYTES (never capped by --steps)."""
+    return 1 if args.warm_cache else max(1, math.ceil(ROTATE_BYTES / set_bytes))
+
+
+def cache_label(args, R, set_bytes):
+    if R == 1:
+        return "warm (1 operand set, reused)"
+    return (f"cold ({R} rotated operand sets, {R * set_bytes / 1e6:.0f} MB; Infinity Cache evicted by a 512 MB "
+            f"read before the timed replay)")
+
+
+def timed_steps(step, args):
+    """W untimed warm-up steps; the K steps captured in one HIP graph (an eager loop with --no-graph) and
+    replayed once untimed; then (cold runs) the Infinity Cache evicted; then the K steps replayed between
+    two HIP events on the launching stream. Returns ms per step."""
+    import torch
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    if args.no_graph:
+        runner = lambda: [step(i) for i in range(args.steps)]  # noqa: E731
+    else:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(args.steps):
+                step(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        runner = g.replay
+    if not args.warm_cache:
+        evict_infinity_cache()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    runner()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / args.steps
 
 
 RMS_METRIC = "µs/call and HBM GB/s (% of peak) for RMSNorm fused with MXFP4 quantisation, M=4096 K=7168"
@@ -257,8 +350,7 @@ def bench_rmsnorm(args):
 
     x0, w = bf16(xb), bf16(wb)
     set_bytes = rms_bytes(M, K)
-    R = 1 if args.warm_cache else max(1, math.ceil(ROTATE_BYTES / set_bytes))
-    R = min(R, args.steps)
+    R = n_sets(args, set_bytes)
     sets = [(x0.clone() if r else x0, torch.empty((M, K // 2), dtype=torch.uint8, device=dev),
              torch.empty((M, K // 32), dtype=torch.uint8, device=dev)) for r in range(R)]
 
@@ -266,34 +358,13 @@ def bench_rmsnorm(args):
         x, q, sc = sets[i % R]
         ops.rmsnorm_quant(x, w, RMS_EPS, out=(q, sc))
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    if args.no_graph:
-        runner = lambda: [step(i) for i in range(args.steps)]  # noqa: E731
-    else:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(args.steps):
-                step(i)
-        torch.cuda.synchronize()
-        g.replay()
-        torch.cuda.synchronize()
-        runner = g.replay
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    runner()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_step = timed_steps(step, args)
     gbs = set_bytes / (ms_step * 1e-3) / 1e9
     out = dict(metric=RMS_METRIC, value=round(gbs, 3), unit="GB/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
                ms_per_step=round(ms_step, 6), higher_is_better=True, scaling="weak", vs_baseline=None,
                dtype="bf16 in, f64 sum of squares, f32 scale, mxfp4 out", data="synthetic",
                config=dict(workload="rmsnorm", seed=seed, M=M, K=K, eps=RMS_EPS,
-                           cache="warm (1 set)" if R == 1 else f"cold ({R} rotated input sets)",
+                           cache=cache_label(args, R, set_bytes),
                            timing="hip graph replay" if not args.no_graph else "eager launch loop",
                            path="mxfp4_rmsnorm_quant"),
                us_per_call=round(ms_step * 1e3, 3), hbm_gbs=round(gbs, 2),
@@ -302,23 +373,12 @@ def bench_rmsnorm(args):
                              algorithmic_bytes=set_bytes))
     if not args.no_cpu_baseline:
         import oracle.rmsnorm as orn
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:
-            threads = 1
         rows = 64
-        times, t_end = [], time.perf_counter() + 12.0
-        while True:
-            t0 = time.perf_counter()
-            orn.rmsnorm_quant(xb[:rows], wb, RMS_EPS)
-            times.append(time.perf_counter() - t0)
-            if time.perf_counter() > t_end or len(times) >= 200:
-                break
-        t = float(np.median(times))
-        out["cpu_baseline"] = dict(value=round(rms_bytes(rows, K) / t / 1e9, 6), unit="GB/s", cores=int(threads),
+        t, runs, n, aff = time_oracle(lambda: orn.rmsnorm_quant(xb[:rows], wb, RMS_EPS))
+        out["cpu_baseline"] = dict(value=round(rms_bytes(rows, K) / t / 1e9, 6), unit="GB/s", cores=n,
                                    kind="oracle", sample=f"oracle rmsnorm_quant on rows 0..{rows - 1} (K={K}); "
-                                   f"median of {len(times)} runs, {t * 1e3:.1f} ms each")
+                                   f"median of {runs} runs, {t * 1e3:.1f} ms each; single-threaded numpy",
+                                   affinity_cpus=aff, cpu_model=cpu_model())
     out["env"] = env_info()
     print(json.dumps(out), flush=True)
 
@@ -355,8 +415,7 @@ def bench_grouped_mnk(args):
     flops = sum(L * alg_flops(M, N, K) for M, N, K, L in shapes)
     nbytes = sum(L * alg_bytes(M, N, K) for M, N, K, L in shapes)
     set_bytes = sum(A.numel() * 2 + Bp.numel() for A, Bp, _ in base) + sum(L * 2 * M * N for M, N, K, L in shapes)
-    R = 1 if args.warm_cache else max(1, math.ceil(ROTATE_BYTES / set_bytes))
-    R = min(R, args.steps)
+    R = n_sets(args, set_bytes)
     sets = []
     for r in range(R):
         probs = [(A.clone() if r else A, Bp.clone() if r else Bp, N) for A, Bp, N in base]
@@ -367,28 +426,7 @@ def bench_grouped_mnk(args):
         probs, outs = sets[i % R]
         ops.grouped_gemm_mnk(probs, out_list=outs)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    if args.no_graph:
-        runner = lambda: [step(i) for i in range(args.steps)]  # noqa: E731
-    else:
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            for i in range(args.steps):
-                step(i)
-        torch.cuda.synchronize()
-        gr.replay()
-        torch.cuda.synchronize()
-        runner = gr.replay
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    runner()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_step = timed_steps(step, args)
     tflops = flops / (ms_step * 1e-3) / 1e12
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     if flops / (FP4_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
@@ -399,7 +437,7 @@ def bench_grouped_mnk(args):
                warmup=args.warmup, ms_per_step=round(ms_step, 6), higher_is_better=True, scaling="weak",
                vs_baseline=None, dtype="mxfp4 (e2m1 x e8m0, fp32 accumulate, bf16 out)", data="synthetic",
                config=dict(workload="grouped_mnk", seed=seed, groups=[dict(M=M, N=N, K=K, L=L) for M, N, K, L in shapes],
-                           cache="warm (1 set)" if R == 1 else f"cold ({R} rotated operand sets)",
+                           cache=cache_label(args, R, set_bytes),
                            timing="hip graph replay" if not args.no_graph else "eager launch loop",
                            path="grouped_gemm_a4w4_mnk"),
                us_per_call=round(ms_step * 1e3, 3), tflops=round(tflops, 3), hbm_gbs=round(gbs, 2),
@@ -413,23 +451,12 @@ def bench_grouped_mnk(args):
         a = synth.make_a(M, K, seed, (0, 0))
         bq, bs = oracle.quant_mx(synth.make_b(N, K, seed, (0, 0)))
         rows = min(M, 64)
-        times, t_end = [], time.perf_counter() + 12.0
-        while True:
-            t0 = time.perf_counter()
-            oracle.gemm_ref(a[:rows], bq, bs)
-            times.append(time.perf_counter() - t0)
-            if time.perf_counter() > t_end or len(times) >= 200:
-                break
-        t = float(np.median(times))
+        t, runs, n, aff = time_oracle(lambda: oracle.gemm_ref(a[:rows], bq, bs))
         val = alg_flops(rows, N, K) / t / 1e12 if unit == "TFLOP/s" else alg_bytes(rows, N, K) / t / 1e9
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:
-            threads = 1
-        out["cpu_baseline"] = dict(value=round(val, 6), unit=unit, cores=int(threads), kind="oracle",
+        out["cpu_baseline"] = dict(value=round(val, 6), unit=unit, cores=n, kind="oracle",
                                    sample=f"oracle gemm_ref on rows 0..{rows - 1} of the first problem (N={N}, K={K}); "
-                                          f"median of {len(times)} runs, {t * 1e3:.1f} ms each")
+                                          f"median of {runs} runs, {t * 1e3:.1f} ms each; numpy's BLAS on {n} threads",
+                                   affinity_cpus=aff, cpu_model=cpu_model())
     out["env"] = env_info()
     print(json.dumps(out), flush=True)
 
@@ -460,8 +487,7 @@ def bench_nvfp4(args):
     flops = sum(L * alg_flops(M, N, K) for M, N, K, L in shapes)
     nbytes = sum(L * nv_bytes(M, N, K) for M, N, K, L in shapes)
     set_bytes = sum(sum(t.numel() for t in b) for b in base) + sum(L * 2 * M * N for M, N, K, L in shapes)
-    R = 1 if args.warm_cache else max(1, math.ceil(ROTATE_BYTES / set_bytes))
-    R = min(R, args.steps)
+    R = n_sets(args, set_bytes)
     sets = []
     for r in range(R):
         probs = [tuple(t.clone() if r else t for t in b) for b in base]
@@ -472,28 +498,7 @@ def bench_nvfp4(args):
         probs, outs = sets[i % R]
         ops.grouped_gemm_nvfp4(probs, out_list=outs)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    if args.no_graph:
-        runner = lambda: [step(i) for i in range(args.steps)]  # noqa: E731
-    else:
-        gr = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(gr):
-            for i in range(args.steps):
-                step(i)
-        torch.cuda.synchronize()
-        gr.replay()
-        torch.cuda.synchronize()
-        runner = gr.replay
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    runner()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    ms_step = timed_steps(step, args)
     tflops = flops / (ms_step * 1e-3) / 1e12
     gbs = nbytes / (ms_step * 1e-3) / 1e9
     if flops / (BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
@@ -505,7 +510,7 @@ def bench_nvfp4(args):
                vs_baseline=None, dtype="nvfp4 (e2m1 x e4m3 per 16; exact fp16 products, fp32 accumulate, fp16 out)",
                data="synthetic",
                config=dict(workload="nvfp4_grouped", seed=seed, groups=[dict(M=M, N=N, K=K, L=L) for M, N, K, L in shapes],
-                           cache="warm (1 set)" if R == 1 else f"cold ({R} rotated operand sets)",
+                           cache=cache_label(args, R, set_bytes),
                            timing="hip graph replay" if not args.no_graph else "eager launch loop",
                            path="grouped_gemm_nvfp4"),
                us_per_call=round(ms_step * 1e3, 3), tflops=round(tflops, 3), hbm_gbs=round(gbs, 2),
@@ -519,23 +524,12 @@ def bench_nvfp4(args):
         aq, as_ = synth.make_nvfp4(M, K, seed, (0, 0))
         bq, bs = synth.make_nvfp4(N, K, seed, (0, 100))
         rows = min(M, 64)
-        times, t_end = [], time.perf_counter() + 12.0
-        while True:
-            t0 = time.perf_counter()
-            oracle.nvfp4.nvfp4_gemm_ref(aq[:rows], as_[:rows], bq, bs)
-            times.append(time.perf_counter() - t0)
-            if time.perf_counter() > t_end or len(times) >= 200:
-                break
-        t = float(np.median(times))
+        t, runs, n, aff = time_oracle(lambda: oracle.nvfp4.nvfp4_gemm_ref(aq[:rows], as_[:rows], bq, bs))
         val = alg_flops(rows, N, K) / t / 1e12 if unit == "TFLOP/s" else nv_bytes(rows, N, K) / t / 1e9
-        try:
-            from threadpoolctl import threadpool_info
-            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-        except Exception:
-            threads = 1
-        out["cpu_baseline"] = dict(value=round(val, 6), unit=unit, cores=int(threads), kind="oracle",
+        out["cpu_baseline"] = dict(value=round(val, 6), unit=unit, cores=n, kind="oracle",
                                    sample=f"oracle nvfp4_gemm_ref on rows 0..{rows - 1} of the first problem "
-                                          f"(N={N}, K={K}); median of {len(times)} runs, {t * 1e3:.1f} ms each")
+                                          f"(N={N}, K={K}); median of {runs} runs, {t * 1e3:.1f} ms each; numpy's "
+                                          f"BLAS on {n} threads", affinity_cpus=aff, cpu_model=cpu_model())
     out["env"] = env_info()
     print(json.dumps(out), flush=True)
 
@@ -577,15 +571,48 @@ def main():
     if args.workload == "nvfp4_grouped":
         bench_nvfp4(args)
         return
+    if args.workload is not None:
+        out, w, unit = bench_gemm(args.workload, args)
+        if not args.no_cpu_baseline:
+            log("[bench] timing the CPU oracle on a bounded sample")
+            out["cpu_baseline"] = cpu_baseline(w, unit)
+        out["env"] = env_info()
+        print(json.dumps(out), flush=True)
+        return
+    # Default: the headline (the largest configuration the metric spans) and the other configurations as
+    # extra keys of the same line, each timed the same way.
+    out, w, unit = bench_gemm(HEADLINE, args)
+    del w
+    extras = {}
+    for name in EXTRAS:
+        o, _, _ = bench_gemm(name, args)
+        rf = o["roofline"]
+        extras[name] = dict(config=o["config"], us_per_call=o["us_per_call"], tflops=o["tflops"], hbm_gbs=o["hbm_gbs"],
+                            roofline=rf)
+    out["workloads"] = extras
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        out["cpu_baseline"] = cpu_baseline(synth_workload(HEADLINE, args), unit)
+    out["env"] = env_info()
+    print(json.dumps(out), flush=True)
+
+
+def synth_workload(name, args):
+    from mxfp4_block_scaled_02_amd import synth
+    return synth.workload(name, synth.default_seed(name) if args.seed is None else args.seed)
+
+
+def bench_gemm(name, args):
+    """One fused call (or, with --unfused, mxfp4_quant + gemm_a4w4) per step over rotated operand sets.
+    Returns (the JSON record, the workload's inputs, the roofline unit)."""
     import torch
-    from mxfp4_block_scaled_02_amd import ops, synth
+    from mxfp4_block_scaled_02_amd import ops
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    name = args.workload
-    seed = synth.default_seed(name) if args.seed is None else args.seed
+    w = synth_workload(name, args)
+    seed = w["seed"]
     log(f"[bench] workload={name} seed={seed}: generating inputs")
-    w = synth.workload(name, seed)
 
     def bf16(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -606,8 +633,7 @@ def main():
         total_bytes, total_flops = alg_bytes(M, N, K), alg_flops(M, N, K)
         a0, b0 = bf16(w["A"]), prep_b(w["B"])
         set_bytes = a0.numel() * 2 + b0.numel() + 2 * M * N
-    R = 1 if args.warm_cache else max(1, math.ceil(ROTATE_BYTES / set_bytes))
-    R = min(R, args.steps)
+    R = n_sets(args, set_bytes)
     log(f"[bench] operand set {set_bytes / 1e6:.2f} MB, rotating {R} sets")
     sets = []
     for r in range(R):
@@ -636,65 +662,35 @@ def main():
         else:
             ops.gemm(a, b, N, out=c)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    stream = torch.cuda.current_stream()
-    if args.no_graph:
-        runner = lambda: [step(i) for i in range(args.steps)]  # noqa: E731
-    else:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(args.steps):
-                step(i)
-        torch.cuda.synchronize()
-        g.replay()  # one untimed replay
-        torch.cuda.synchronize()
-        stream = torch.cuda.current_stream()
-        runner = g.replay
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    runner()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms_total = ev0.elapsed_time(ev1)
-    ms_step = ms_total / args.steps
+    ms_step = timed_steps(step, args)
     us = ms_step * 1e3
     gbs = total_bytes / (ms_step * 1e-3) / 1e9
     tflops = total_flops / (ms_step * 1e-3) / 1e12
-
-    if name == "square":
+    t_hbm, t_mfma = total_bytes / (HBM_PEAK_GBS * 1e9), total_flops / (FP4_PEAK_TFLOPS * 1e12)
+    if t_mfma > t_hbm:
         bound, achieved, peak, unit = "mfma", tflops, FP4_PEAK_TFLOPS, "TFLOP/s"
-    elif name == "grouped":
-        if total_flops / (FP4_PEAK_TFLOPS * 1e12) > total_bytes / (HBM_PEAK_GBS * 1e9):
-            bound, achieved, peak, unit = "mfma", tflops, FP4_PEAK_TFLOPS, "TFLOP/s"
-        else:
-            bound, achieved, peak, unit = "hbm", gbs, HBM_PEAK_GBS, "GB/s"
     else:
         bound, achieved, peak, unit = "hbm", gbs, HBM_PEAK_GBS, "GB/s"
-    value = achieved
-    cfg = dict(workload=name, seed=seed, cache="warm (1 set)" if R == 1 else f"cold ({R} rotated operand sets)",
+    cfg = dict(workload=name, seed=seed, cache=cache_label(args, R, set_bytes),
                timing="hip graph replay" if not args.no_graph else "eager launch loop",
-               path="unfused: mxfp4_quant + gemm_a4w4 (two launches)" if args.unfused else "fused: gemm_a4w4_fused")
+               path="unfused: mxfp4_quant + gemm_a4w4 (two launches)" if args.unfused else "fused: gemm_a4w4_fused"
+               if name != "grouped" else "fused: grouped_gemm_a4w4 (one launch)")
     if name == "grouped":
         cfg.update(G=len(Ms), Ms=Ms, N=N, K=K)
     else:
         cfg.update(M=M, N=N, K=K)
-    out = dict(metric=METRIC, value=round(value, 3), unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,
+    traffic = recorded_traffic(name + "_unfused" if args.unfused else name)
+    roof = dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit, frac=round(achieved / peak, 4),
+                traffic=traffic, algorithmic_bytes=total_bytes, algorithmic_flops=total_flops,
+                traffic_ratio=round(traffic / total_bytes, 3) if traffic else None,
+                frac_hbm=round(t_hbm / (ms_step * 1e-3), 4), frac_mfma=round(t_mfma / (ms_step * 1e-3), 4))
+    out = dict(metric=METRIC, value=round(achieved, 3), unit=unit, n_gpus=1, steps=args.steps, warmup=args.warmup,
                ms_per_step=round(ms_step, 6), higher_is_better=True, scaling="weak", vs_baseline=None,
                dtype="mxfp4 (e2m1 x e8m0, fp32 accumulate, bf16 out)", data="synthetic", config=cfg,
-               us_per_call=round(us, 3), tflops=round(tflops, 3), hbm_gbs=round(gbs, 2),
-               roofline=dict(bound=bound, achieved=round(achieved, 3), peak=peak, unit=unit,
-                             frac=round(achieved / peak, 4),
-                             traffic=recorded_traffic(name + "_unfused" if args.unfused else name),
-                             algorithmic_bytes=total_bytes, algorithmic_flops=total_flops))
-    if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        out["cpu_baseline"] = cpu_baseline(w, unit)
-    out["env"] = env_info()
-    print(json.dumps(out), flush=True)
+               us_per_call=round(us, 3), tflops=round(tflops, 3), hbm_gbs=round(gbs, 2), roofline=roof)
+    del sets, a0, b0
+    torch.cuda.empty_cache()
+    return out, w, unit
 
 
 if __name__ == "__main__":

@@ -151,6 +151,29 @@ int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t
                     int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * gemm_a4w4_fused_dump -- verification form of gemm_a4w4_fused: the same
+ * call (same kernel choice, tiling, arithmetic and C), whose kernels also
+ * write the quantised A they compute on chip, so that it can be compared byte
+ * for byte with the quantisation rule (page 517169 module docstring, step
+ * "quantise on chip"; the fused path otherwise never stores it). Every N-tile
+ * of the kernel quantises the whole of A again; each writes its own copy.
+ *   dump : device buffer of at least gemm_a4w4_fused_dump_bytes(M, N, K)
+ *          bytes, 16-byte aligned. With C = the number of copies (that size
+ *          divided by M*(K/2 + K/32)), it receives codes [C][M][K/2] (fp4x2,
+ *          rows contiguous) followed by scale bytes [C][M][K/32]. A scale
+ *          byte is the one the matrix instruction receives: as mxfp4_quant's,
+ *          except that an all-zero block (codes all 0 or 8) gets 0 instead of
+ *          127, which gives the same (zero) products.
+ *   Too small: MXFP4_ERR_BUFFER; NULL: MXFP4_ERR_NULL; misaligned:
+ *   MXFP4_ERR_ALIGN. Every other argument as for gemm_a4w4_fused. Slower than
+ *   gemm_a4w4_fused (the extra stores); meant for tests, not the hot path.
+ * ------------------------------------------------------------------------- */
+size_t gemm_a4w4_fused_dump_bytes(int64_t M, int64_t N, int64_t K);
+int gemm_a4w4_fused_dump(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M,
+                         int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* dump,
+                         size_t dump_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * gemm_a4w4 -- C[M, N] = A_q . B^T with A ALREADY quantised (for example by
  * mxfp4_quant): the unfused pipeline of page 683203's anatomy (quantise A in
  * one launch, then run the block-scaled GEMM on A_q and its scales), kept as
@@ -190,6 +213,16 @@ typedef struct {
 size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K);
 int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* grouped_gemm_a4w4_dump -- verification form of grouped_gemm_a4w4 (same
+ * launch and C), also writing each group's on-chip quantised A as
+ * gemm_a4w4_fused_dump does: group g's block (C_g = ceil(N/512) copies: codes
+ * [C_g][M_g][K/2], then scale bytes [C_g][M_g][K/32]) follows group g-1's.
+ * dump: at least grouped_gemm_a4w4_dump_bytes(groups, G, N, K) bytes,
+ * 16-byte aligned. */
+size_t grouped_gemm_a4w4_dump_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K);
+int grouped_gemm_a4w4_dump(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,
+                           size_t workspace_bytes, void* dump, size_t dump_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * grouped_gemm_a4w4_mnk -- G groups of fused problems with their OWN (M, N, K)

@@ -54,7 +54,23 @@ struct Operand {
   int64_t ldc;
   int M;
   int pad_;
+  // Verification instances only (DUMP): the quantised A each workgroup computes
+  // on chip, codes [copy][M][K/2] at dq and E8M0 bytes [copy][M][K/32] at ds,
+  // one copy per N-tile (every N-tile quantises the same A again).
+  uint8_t* dq;
+  uint8_t* ds;
 };
+
+// Writes one lane's share of an on-chip quantised block into the dump: the 8
+// codes (4 bytes) of elements k0 .. k0+7 of row `row`, and, from the first lane
+// of the quad, the block's scale byte as the matrix instruction receives it.
+__device__ __forceinline__ void dump_piece(const Operand& p, int K, int copy, int row, int k0, uint32_t code,
+                                           uint32_t sb, bool quad_lead) {
+  if (row >= p.M || k0 >= K) return;
+  const int64_t r = (int64_t)copy * p.M + row;
+  *reinterpret_cast<uint32_t*>(p.dq + r * (K / 2) + k0 / 2) = code;
+  if (quad_lead) p.ds[r * (K / 32) + k0 / 32] = (uint8_t)sb;
+}
 
 struct Dims {
   int N, K;
@@ -139,7 +155,7 @@ constexpr int kSkWaves = 16;
 // rows x 4 chunks x 4 dwords) and each 16-lane operand read conflict-free.
 __device__ __forceinline__ int slot16(int row, int chunk) { return chunk * 16 + (row ^ (chunk << 2)); }
 
-template <int MS, int NB, int PF>
+template <int MS, int NB, int PF, bool DUMP>
 __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, Dims d) {
   static_assert(MS == 4 || MS == 8 || MS == 16, "rows per workgroup");
   constexpr int PIECES = MS / 4;  // 16-byte A pieces per lane per K step
@@ -233,6 +249,7 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, D
         for (int h = 0; h < PIECES; ++h) {
           uint32_t sb;
           const uint32_t code = mx::quant8_quad(w[s][h], sb);
+          if constexpr (DUMP) dump_piece(p, d.K, blockIdx.x, m0 + 4 * h + (l >> 4), 128 * j + 8 * (l & 15), code, sb, sub == 0);
           sAq[wave][wslot[h] * 4 + sub] = code;
           sAs[wave][wslot[h]] = (uint8_t)sb;  // the quad's four lanes store the same byte
         }
@@ -297,7 +314,7 @@ struct SplitArgs {
 
 // PREQ: A arrives pre-quantised (gemm_a4w4); each lane then loads its operand and
 // scale byte directly, and the quantisation and LDS stages are skipped.
-template <int MT, bool PREQ>
+template <int MT, bool PREQ, bool DUMP>
 __global__ __launch_bounds__(kSpT) void gemm_splitk_kernel(Operand p, Dims d, SplitArgs sk) {
   __shared__ __align__(16) uint32_t sAq[PREQ ? 1 : kSpMaxSteps][MT][64 * 4];  // A operand codes per step, row tile
   __shared__ uint8_t sAs[PREQ ? 1 : kSpMaxSteps][MT][64];                    // A operand scales
@@ -390,6 +407,7 @@ __global__ __launch_bounds__(kSpT) void gemm_splitk_kernel(Operand p, Dims d, Sp
         if (jb + s == d.KT - 1 && tail_k < 128 && 8 * (tid & 15) >= tail_k) w[i][0] = w[i][1] = w[i][2] = w[i][3] = 0u;
         uint32_t sb;
         const uint32_t code = mx::quant8_quad(w[i], sb);
+        if constexpr (DUMP) dump_piece(p, d.K, tile, 16 * rt + (tid >> 4), 128 * (jb + s) + 8 * (tid & 15), code, sb, sub == 0);
         sAq[s][rt][wslot * 4 + sub] = code;
         sAs[s][rt][wslot] = (uint8_t)sb;  // the quad's four lanes store the same byte
       }
@@ -591,7 +609,7 @@ __device__ __forceinline__ void lds_st128(uint32_t addr, const uint4& v) {
 // bytes of row tid/4, 32-element chunk tid%4 of each K step (and row tid%128's
 // 4 scale bytes) and stores them into the same LDS operand layout; everything
 // else is shared with the fused path.
-template <bool PREQ>
+template <bool PREQ, bool DUMP = false>
 __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int mt, int nt, TiledSmem& sm,
                                            uint8_t* ring) {
   const int tid = threadIdx.x, l = tid & 63;
@@ -690,6 +708,8 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
     for (int h = 0; h < 4; ++h) {
       uint32_t sb;
       c[h] = mx::quant8_quad(S.raw[h], sb);
+      if constexpr (DUMP)
+        if (j < d.KT) dump_piece(p, d.K, nt, m0 + 32 * h + (tid >> 4), 128 * j + 8 * (tid & 15), c[h], sb, sub == 0);
       sw |= sb << (8 * h);
       __builtin_amdgcn_sched_barrier(0);
       after_piece(h);
@@ -953,12 +973,12 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   }
 }
 
-template <bool PREQ>
+template <bool PREQ, bool DUMP>
 __global__ __launch_bounds__(kTThreads) void gemm_tiled_kernel(Operand p, Dims d, int ntiles_n) {
   __shared__ __align__(16) TiledSmem sm;
   __shared__ __align__(16) uint8_t ring[kRingBytes];
   const int v = xcd_remap(blockIdx.x, gridDim.x);
-  tiled_tile<PREQ>(p, d, v / ntiles_n, v % ntiles_n, sm, ring);
+  tiled_tile<PREQ, DUMP>(p, d, v / ntiles_n, v % ntiles_n, sm, ring);
 }
 
 struct GroupedArgs {
@@ -968,6 +988,7 @@ struct GroupedArgs {
   int ntiles_n;
 };
 
+template <bool DUMP>
 __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, Dims d) {
   const int v = xcd_remap(blockIdx.x, gridDim.x);
   int g = 0;
@@ -975,7 +996,7 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, 
   const int local = v - a.tile_start[g];
   __shared__ __align__(16) TiledSmem sm;
   __shared__ __align__(16) uint8_t ring[kRingBytes];
-  tiled_tile<false>(a.g[g], d, local / a.ntiles_n, local % a.ntiles_n, sm, ring);
+  tiled_tile<false, DUMP>(a.g[g], d, local / a.ntiles_n, local % a.ntiles_n, sm, ring);
 }
 
 // ---------------------------------------------------------------------------
@@ -1071,12 +1092,14 @@ int check_problem(const void* A, int64_t lda, const void* Bp, const void* C, int
 }
 
 template <int MS, int NB, int PF>
-hipError_t launch_skinny(const Operand& o, const Dims& d, int64_t M, hipStream_t st) {
+hipError_t launch_skinny(const Operand& o, const Dims& d, int64_t M, bool dump, hipStream_t st) {
   Operand op = o;
   Dims dd = d;
   void* args[] = {&op, &dd};
   const dim3 grid((unsigned)mxh::cdiv(mxh::cdiv(d.N, 16), NB), (unsigned)mxh::cdiv(M, MS));
-  return hipLaunchKernel((const void*)gemm_skinny_kernel<MS, NB, PF>, grid, dim3(kSkWaves * 64), args, 0, st);
+  return hipLaunchKernel(dump ? (const void*)gemm_skinny_kernel<MS, NB, PF, true>
+                              : (const void*)gemm_skinny_kernel<MS, NB, PF, false>,
+                         grid, dim3(kSkWaves * 64), args, 0, st);
 }
 
 // Skinny tile shape (rows MS x 16*NB columns per workgroup). Every workgroup
@@ -1147,44 +1170,61 @@ SplitGeom split_geom(int64_t M, int64_t N, int64_t K) {
   return g;
 }
 
-hipError_t launch_splitk(const Operand& o, const Dims& d, const SplitGeom& g, void* ws, bool preq, hipStream_t st) {
+hipError_t launch_splitk(const Operand& o, const Dims& d, const SplitGeom& g, void* ws, bool preq, bool dump,
+                         hipStream_t st) {
   Operand op = o;
   Dims dd = d;
   SplitArgs sa{};
   sa.part = (uint32_t*)ws;
   sa.S = g.S;
   void* args[] = {&op, &dd, &sa};
-  return hipLaunchKernel(preq ? (const void*)gemm_splitk_kernel<1, true> : (const void*)gemm_splitk_kernel<1, false>,
-                         dim3((unsigned)(g.T * g.S)), dim3(kSpT), args, 0, st);
+  const void* k = preq ? (const void*)gemm_splitk_kernel<1, true, false>
+                  : dump ? (const void*)gemm_splitk_kernel<1, false, true>
+                         : (const void*)gemm_splitk_kernel<1, false, false>;
+  return hipLaunchKernel(k, dim3((unsigned)(g.T * g.S)), dim3(kSpT), args, 0, st);
 }
 
-hipError_t launch_tiled(const Operand& o, const Dims& d, int64_t M, int64_t N, bool preq, hipStream_t st) {
+hipError_t launch_tiled(const Operand& o, const Dims& d, int64_t M, int64_t N, bool preq, bool dump, hipStream_t st) {
   Operand op = o;
   Dims dd = d;
   int ntn = (int)mxh::cdiv(N, kTBN);
   void* args[] = {&op, &dd, &ntn};
   const int64_t tiles = mxh::cdiv(M, kTBM) * ntn;
-  return hipLaunchKernel(preq ? (const void*)gemm_tiled_kernel<true> : (const void*)gemm_tiled_kernel<false>,
-                         dim3((unsigned)tiles), dim3(kTThreads), args, 0, st);
+  const void* k = preq ? (const void*)gemm_tiled_kernel<true, false>
+                  : dump ? (const void*)gemm_tiled_kernel<false, true>
+                         : (const void*)gemm_tiled_kernel<false, false>;
+  return hipLaunchKernel(k, dim3((unsigned)tiles), dim3(kTThreads), args, 0, st);
 }
 
-hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, int64_t K, hipStream_t st) {
+hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, int64_t K, bool dump, hipStream_t st) {
   if (M <= 64) {
     const SkinnyShape sh = choose_skinny(M, N, K);
     switch (sh.MS * 16 + sh.NB) {
-      case 4 * 16 + 1: return launch_skinny<4, 1, 4>(o, d, M, st);
-      case 4 * 16 + 2: return launch_skinny<4, 2, 4>(o, d, M, st);
-      case 4 * 16 + 4: return launch_skinny<4, 4, 2>(o, d, M, st);
-      case 8 * 16 + 1: return launch_skinny<8, 1, 4>(o, d, M, st);
-      case 8 * 16 + 2: return launch_skinny<8, 2, 4>(o, d, M, st);
-      case 8 * 16 + 4: return launch_skinny<8, 4, 2>(o, d, M, st);
-      case 16 * 16 + 1: return launch_skinny<16, 1, 2>(o, d, M, st);
-      case 16 * 16 + 2: return launch_skinny<16, 2, 2>(o, d, M, st);
-      case 16 * 16 + 8: return launch_skinny<16, 8, 1>(o, d, M, st);
-      default: return launch_skinny<16, 4, 2>(o, d, M, st);
+      case 4 * 16 + 1: return launch_skinny<4, 1, 4>(o, d, M, dump, st);
+      case 4 * 16 + 2: return launch_skinny<4, 2, 4>(o, d, M, dump, st);
+      case 4 * 16 + 4: return launch_skinny<4, 4, 2>(o, d, M, dump, st);
+      case 8 * 16 + 1: return launch_skinny<8, 1, 4>(o, d, M, dump, st);
+      case 8 * 16 + 2: return launch_skinny<8, 2, 4>(o, d, M, dump, st);
+      case 8 * 16 + 4: return launch_skinny<8, 4, 2>(o, d, M, dump, st);
+      case 16 * 16 + 1: return launch_skinny<16, 1, 2>(o, d, M, dump, st);
+      case 16 * 16 + 2: return launch_skinny<16, 2, 2>(o, d, M, dump, st);
+      case 16 * 16 + 8: return launch_skinny<16, 8, 1>(o, d, M, dump, st);
+      default: return launch_skinny<16, 4, 2>(o, d, M, dump, st);
     }
   }
-  return launch_tiled(o, d, M, N, false, st);
+  return launch_tiled(o, d, M, N, false, dump, st);
+}
+
+// Copies of the quantised A that the fused call computes (one per N-tile of
+// the kernel it runs): the leading dimension of the verification dump.
+int64_t dump_copies(int64_t M, int64_t N, int64_t K) {
+  const SplitGeom g = split_geom(M, N, K);
+  if (g.ok) return g.T;
+  if (M <= 64) return mxh::cdiv(mxh::cdiv(N, 16), choose_skinny(M, N, K).NB);
+  return mxh::cdiv(N, kTBN);
+}
+size_t dump_bytes_of(int64_t M, int64_t N, int64_t K) {
+  return (size_t)(dump_copies(M, N, K) * M * (K / 2 + K / 32));
 }
 
 }  // namespace
@@ -1195,12 +1235,19 @@ extern "C" size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   return g.ok ? g.total() : 0;  // larger M: every output tile is reduced inside one workgroup
 }
 
-extern "C" int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M, int64_t N,
-                               int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+int fused_call(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+               void* workspace, size_t workspace_bytes, void* dump, size_t dump_bytes, void* stream) {
   const int st = check_problem(A, lda, Bp, C, ldc, M, N, K);
   if (st != MXFP4_OK) return st;
   if (mxh::cdiv(M, kTBM) * mxh::cdiv(N, kTBN) > INT32_MAX) return MXFP4_ERR_SHAPE;
-  const Operand o = make_operand(A, lda, Bp, C, ldc, M, N, K);
+  Operand o = make_operand(A, lda, Bp, C, ldc, M, N, K);
+  if (dump) {
+    if (dump_bytes < dump_bytes_of(M, N, K)) return MXFP4_ERR_BUFFER;
+    if (!mxh::aligned(dump, 16)) return MXFP4_ERR_ALIGN;
+    o.dq = (uint8_t*)dump;
+    o.ds = (uint8_t*)dump + dump_copies(M, N, K) * M * (K / 2);
+  }
   const Dims d = make_dims(N, K);
   const SplitGeom g = split_geom(M, N, K);
   if (g.ok) {
@@ -1208,9 +1255,27 @@ extern "C" int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void*
       if (!workspace || workspace_bytes < g.total()) return MXFP4_ERR_WORKSPACE;
       if (!mxh::aligned(workspace, 256)) return MXFP4_ERR_ALIGN;
     }
-    return mxh::launch_status(launch_splitk(o, d, g, workspace, false, (hipStream_t)stream));
+    return mxh::launch_status(launch_splitk(o, d, g, workspace, false, dump != nullptr, (hipStream_t)stream));
   }
-  return mxh::launch_status(launch_gemm(o, d, M, N, K, (hipStream_t)stream));
+  return mxh::launch_status(launch_gemm(o, d, M, N, K, dump != nullptr, (hipStream_t)stream));
+}
+}  // namespace
+
+extern "C" int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M, int64_t N,
+                               int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
+  return fused_call(A, lda, Bp, C, ldc, M, N, K, workspace, workspace_bytes, nullptr, 0, stream);
+}
+
+extern "C" size_t gemm_a4w4_fused_dump_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || M > mxh::kMaxDim || N > mxh::kMaxDim || K > mxh::kMaxDim) return 0;
+  return dump_bytes_of(M, N, K);
+}
+
+extern "C" int gemm_a4w4_fused_dump(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M,
+                                    int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* dump,
+                                    size_t dump_bytes, void* stream) {
+  if (!dump) return MXFP4_ERR_NULL;
+  return fused_call(A, lda, Bp, C, ldc, M, N, K, workspace, workspace_bytes, dump, dump_bytes, stream);
 }
 
 extern "C" int gemm_a4w4(const void* Aq, int64_t ldaq, const void* As, int64_t ldas, const void* Bp, void* C,
@@ -1232,9 +1297,9 @@ extern "C" int gemm_a4w4(const void* Aq, int64_t ldaq, const void* As, int64_t l
       if (!workspace || workspace_bytes < g.total()) return MXFP4_ERR_WORKSPACE;
       if (!mxh::aligned(workspace, 256)) return MXFP4_ERR_ALIGN;
     }
-    return mxh::launch_status(launch_splitk(o, d, g, workspace, true, (hipStream_t)stream));
+    return mxh::launch_status(launch_splitk(o, d, g, workspace, true, false, (hipStream_t)stream));
   }
-  return mxh::launch_status(launch_tiled(o, d, M, N, true, (hipStream_t)stream));
+  return mxh::launch_status(launch_tiled(o, d, M, N, true, false, (hipStream_t)stream));
 }
 
 extern "C" size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K) {
@@ -1245,10 +1310,16 @@ extern "C" size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, i
   return 0;
 }
 
-extern "C" int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,
-                                 size_t workspace_bytes, void* stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+namespace {
+// Verification dump of the grouped call: group g's block (copies = N-tiles,
+// codes then scales, as for the single call) follows group g-1's.
+size_t grouped_dump_bytes_of(const mxfp4_group* groups, int G, int64_t N, int64_t K) {
+  size_t t = 0;
+  for (int g = 0; g < G; ++g) t += (size_t)(mxh::cdiv(N, kTBN) * groups[g].M * (K / 2 + K / 32));
+  return t;
+}
+
+int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* dump, size_t dump_bytes, void* stream) {
   if (!groups) return MXFP4_ERR_NULL;
   if (G < 1 || G > MXFP4_MAX_GROUPS) return MXFP4_ERR_TOO_MANY_GROUPS;
   GroupedArgs a{};
@@ -1263,13 +1334,47 @@ extern "C" int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, in
     total += mxh::cdiv(q.M, kTBM) * ntn;
     if (total > INT32_MAX) return MXFP4_ERR_SHAPE;
   }
+  if (dump) {
+    if (dump_bytes < grouped_dump_bytes_of(groups, G, N, K)) return MXFP4_ERR_BUFFER;
+    if (!mxh::aligned(dump, 16)) return MXFP4_ERR_ALIGN;
+    uint8_t* at = (uint8_t*)dump;
+    for (int g = 0; g < G; ++g) {
+      a.g[g].dq = at;
+      a.g[g].ds = at + ntn * groups[g].M * (K / 2);
+      at += ntn * groups[g].M * (K / 2 + K / 32);
+    }
+  }
   a.tile_start[G] = (int)total;
   a.G = G;
   a.ntiles_n = (int)ntn;
   Dims d = make_dims(N, K);
   void* args[] = {&a, &d};
-  return mxh::launch_status(hipLaunchKernel((const void*)gemm_grouped_kernel, dim3((unsigned)total),
-                                            dim3(kTThreads), args, 0, (hipStream_t)stream));
+  return mxh::launch_status(hipLaunchKernel(
+      dump ? (const void*)gemm_grouped_kernel<true> : (const void*)gemm_grouped_kernel<false>, dim3((unsigned)total),
+      dim3(kTThreads), args, 0, (hipStream_t)stream));
+}
+}  // namespace
+
+extern "C" int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  return grouped_call(groups, G, N, K, nullptr, 0, stream);
+}
+
+extern "C" size_t grouped_gemm_a4w4_dump_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K) {
+  if (!groups || G < 1 || G > MXFP4_MAX_GROUPS || N < 1 || K < 32 || K % 32 != 0) return 0;
+  for (int g = 0; g < G; ++g)
+    if (groups[g].M < 1 || groups[g].M > mxh::kMaxDim) return 0;
+  return grouped_dump_bytes_of(groups, G, N, K);
+}
+
+extern "C" int grouped_gemm_a4w4_dump(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,
+                                      size_t workspace_bytes, void* dump, size_t dump_bytes, void* stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (!dump) return MXFP4_ERR_NULL;
+  return grouped_call(groups, G, N, K, dump, dump_bytes, stream);
 }
 
 extern "C" int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void* stream) {

@@ -22,9 +22,10 @@ _lock = threading.Lock()
 MXFP4_MAX_GROUPS = 32
 STATUS = {0: "MXFP4_OK", 1: "MXFP4_ERR_NULL", 2: "MXFP4_ERR_SHAPE", 3: "MXFP4_ERR_ALIGN", 4: "MXFP4_ERR_WORKSPACE",
           5: "MXFP4_ERR_TOO_MANY_GROUPS", 6: "MXFP4_ERR_HIP", 7: "MXFP4_ERR_BUFFER", 8: "MXFP4_ERR_ARG"}
-EXPORTED = ["mxfp4_status_str", "mxfp4_quant", "mxfp4_rmsnorm_quant", "mxfp4_pack_B_bytes", "mxfp4_pack_B", "gemm_a4w4_workspace_bytes",
-            "gemm_a4w4_fused", "gemm_a4w4", "grouped_gemm_a4w4_workspace_bytes", "grouped_gemm_a4w4",
-            "grouped_gemm_a4w4_mnk", "grouped_gemm_nvfp4"]
+EXPORTED = ["mxfp4_status_str", "mxfp4_quant", "mxfp4_rmsnorm_quant", "mxfp4_pack_B_bytes", "mxfp4_pack_B",
+            "gemm_a4w4_workspace_bytes", "gemm_a4w4_fused", "gemm_a4w4_fused_dump_bytes", "gemm_a4w4_fused_dump",
+            "gemm_a4w4", "grouped_gemm_a4w4_workspace_bytes", "grouped_gemm_a4w4", "grouped_gemm_a4w4_dump_bytes",
+            "grouped_gemm_a4w4_dump", "grouped_gemm_a4w4_mnk", "grouped_gemm_nvfp4"]
 
 
 class Mxfp4Error(RuntimeError):
@@ -78,6 +79,13 @@ def lib() -> ctypes.CDLL:
         L.gemm_a4w4_workspace_bytes.argtypes, L.gemm_a4w4_workspace_bytes.restype = [i64, i64, i64], sz
         L.gemm_a4w4_fused.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp]
         L.gemm_a4w4_fused.restype = i32
+        L.gemm_a4w4_fused_dump_bytes.argtypes, L.gemm_a4w4_fused_dump_bytes.restype = [i64, i64, i64], sz
+        L.gemm_a4w4_fused_dump.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp, sz, vp]
+        L.gemm_a4w4_fused_dump.restype = i32
+        L.grouped_gemm_a4w4_dump_bytes.argtypes = [ctypes.POINTER(Group), i32, i64, i64]
+        L.grouped_gemm_a4w4_dump_bytes.restype = sz
+        L.grouped_gemm_a4w4_dump.argtypes = [ctypes.POINTER(Group), i32, i64, i64, vp, sz, vp, sz, vp]
+        L.grouped_gemm_a4w4_dump.restype = i32
         L.gemm_a4w4.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp]
         L.gemm_a4w4.restype = i32
         L.grouped_gemm_a4w4_workspace_bytes.argtypes = [ctypes.POINTER(Group), i32, i64, i64]
@@ -205,6 +213,27 @@ def gemm(a: torch.Tensor, bp: torch.Tensor, N: int, out: torch.Tensor | None = N
     return out
 
 
+def gemm_dump(a: torch.Tensor, bp: torch.Tensor, N: int):
+    """Verification form of gemm(): returns (C, codes [copies, M, K/2], scales [copies, M, K/32]), the
+    quantised A that each N-tile of the fused kernel computed on chip (uint8)."""
+    _require(a, torch.bfloat16, "a")
+    M, K = a.shape
+    if bp.numel() < pack_B_bytes(N, K):
+        raise ValueError("packed B is smaller than pack_B_bytes(N, K)")
+    out = torch.empty((M, N), dtype=torch.bfloat16, device=a.device)
+    wsz = int(lib().gemm_a4w4_workspace_bytes(M, N, K))
+    st = _stream(a)
+    ws = workspace(a.device, wsz, st)
+    dsz = int(lib().gemm_a4w4_fused_dump_bytes(M, N, K))
+    copies = dsz // (M * (K // 2 + K // 32))
+    dump = torch.full((dsz,), 0xEE, dtype=torch.uint8, device=a.device)
+    _check(lib().gemm_a4w4_fused_dump(a.data_ptr(), a.stride(0), bp.data_ptr(), out.data_ptr(), out.stride(0), M, N, K,
+                                      ws.data_ptr() if wsz else None, ws.numel() if wsz else 0, dump.data_ptr(), dsz,
+                                      st), "gemm_a4w4_fused_dump")
+    nq = copies * M * (K // 2)
+    return out, dump[:nq].view(copies, M, K // 2), dump[nq:].view(copies, M, K // 32)
+
+
 def gemm_a4w4(aq: torch.Tensor, a_scale: torch.Tensor, bp: torch.Tensor, N: int,
               out: torch.Tensor | None = None) -> torch.Tensor:
     """C[M, N] = A_q . B^T with A already quantised: aq fp4x2 [M, K/2], a_scale E8M0 [M, K/32] (uint8,
@@ -252,6 +281,29 @@ def grouped_gemm(a_list, bp_list, N: int, out_list=None):
     _check(lib().grouped_gemm_a4w4(arr, G, N, K, ws.data_ptr() if wsz else None, ws.numel() if wsz else 0, st),
            "grouped_gemm_a4w4")
     return out_list
+
+
+def grouped_gemm_dump(a_list, bp_list, N: int):
+    """Verification form of grouped_gemm(): returns (list of C, list of (codes [copies, M_g, K/2],
+    scales [copies, M_g, K/32])), the quantised A each N-tile computed on chip per group."""
+    G = len(a_list)
+    K = a_list[0].shape[1]
+    outs = [torch.empty((a.shape[0], N), dtype=torch.bfloat16, device=a.device) for a in a_list]
+    arr = (Group * G)()
+    for g, (a, bp, c) in enumerate(zip(a_list, bp_list, outs)):
+        _require(a, torch.bfloat16, "a_g")
+        arr[g] = Group(a.data_ptr(), a.stride(0), bp.data_ptr(), c.data_ptr(), c.stride(0), a.shape[0])
+    dsz = int(lib().grouped_gemm_a4w4_dump_bytes(arr, G, N, K))
+    dump = torch.full((dsz,), 0xEE, dtype=torch.uint8, device=a_list[0].device)
+    _check(lib().grouped_gemm_a4w4_dump(arr, G, N, K, None, 0, dump.data_ptr(), dsz, _stream(a_list[0])),
+           "grouped_gemm_a4w4_dump")
+    copies, at, res = -(-N // 512), 0, []
+    for a in a_list:
+        M = a.shape[0]
+        nq, ns = copies * M * (K // 2), copies * M * (K // 32)
+        res.append((dump[at:at + nq].view(copies, M, K // 2), dump[at + nq:at + nq + ns].view(copies, M, K // 32)))
+        at += nq + ns
+    return outs, res
 
 
 def grouped_gemm_mnk(problems, out_list=None):

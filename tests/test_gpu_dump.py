@@ -1,0 +1,103 @@
+"""The fused kernels' on-chip quantisation, byte for byte (on an MI355X).
+
+gemm_a4w4_fused_dump and grouped_gemm_a4w4_dump run the same kernels as the
+production calls and also store the E2M1 codes and E8M0 bytes each workgroup
+computed in registers, one copy per N-tile (every N-tile quantises A again).
+Every copy must equal the oracle's quant_mx(A) bit for bit (page 517169, module
+docstring: the fused plan quantises on chip), with one stated exception: inside
+the GEMM an all-zero block gets scale byte 0 instead of 127 (its codes are zero,
+so every product is zero under either scale). Which blocks are all-zero is read
+from the input, not from the kernel's output. C must equal the production
+call's C bit for bit (same arithmetic). Covers the split-K kernel (tiny, skinny),
+the skinny kernel (stress), the tiled kernel (square) and the grouped kernel
+(grouped), plus K, M and N tails.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from mxfp4_block_scaled_02_amd import ops, synth
+from tests.helpers import bits_of, quant_groups_in_pool, to_dev_bf16, to_dev_u8
+
+pytestmark = pytest.mark.gpu
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def expected(a_bits):
+    """Oracle bytes, with the GEMM's scale byte for all-zero input blocks (0 instead of 127)."""
+    q0, s0 = oracle.quant_mx(a_bits)
+    M, K = a_bits.shape
+    zero_blk = (np.asarray(a_bits, np.uint16).reshape(M, K // 32, 32) & 0x7FFF).max(axis=2) == 0
+    return q0, np.where(zero_blk, np.uint8(0), s0)
+
+
+def check_copies(codes, scales, a_bits, what):
+    q0, s0 = expected(a_bits)
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    assert codes.shape[1:] == q0.shape and scales.shape[1:] == s0.shape
+    for c in range(codes.shape[0]):
+        assert np.array_equal(scales[c], s0), f"{what}: scale bytes of copy {c} differ"
+        assert np.array_equal(codes[c], q0), f"{what}: codes of copy {c} differ"
+
+
+def run_single(a_bits, b_bits, N, what):
+    bq, bs = oracle.quant_mx(b_bits)
+    a, bp = to_dev_bf16(a_bits), ops.pack_B(to_dev_u8(bq), to_dev_u8(bs))
+    c_dump, codes, scales = ops.gemm_dump(a, bp, N)
+    c_prod = ops.gemm(a, bp, N)
+    torch.cuda.synchronize()
+    say(f"{what}: {codes.shape[0]} copies")
+    check_copies(codes, scales, a_bits, what)
+    assert np.array_equal(bits_of(c_dump), bits_of(c_prod)), f"{what}: C of the dump instance differs"
+
+
+@pytest.mark.parametrize("name", ["tiny", "skinny", "stress", "square"])
+def test_fused_quant_bytes_workloads(name):
+    say(f"dump workload {name}")
+    w = synth.workload(name, synth.default_seed(name))
+    run_single(w["A"], w["B"], w["N"], name)
+
+
+@pytest.mark.timeout(600)
+def test_fused_quant_bytes_grouped():
+    say("dump workload grouped")
+    w = synth.workload("grouped", synth.default_seed("grouped"))
+    qs = quant_groups_in_pool(w["B"])
+    a_dev = [to_dev_bf16(a) for a in w["A"]]
+    bp = [ops.pack_B(to_dev_u8(bq), to_dev_u8(bs)) for bq, bs in qs]
+    cs, dumps = ops.grouped_gemm_dump(a_dev, bp, w["N"])
+    prod = ops.grouped_gemm(a_dev, bp, w["N"])
+    torch.cuda.synchronize()
+    for g, (a, (codes, scales), c, cp) in enumerate(zip(w["A"], dumps, cs, prod)):
+        check_copies(codes, scales, a, f"group {g} (M={a.shape[0]})")
+        assert np.array_equal(bits_of(c), bits_of(cp)), f"group {g}: C of the dump instance differs"
+
+
+# Split-K with M and K tails; the skinny kernel with an M tail, ragged N and a K
+# tail on odd K/64; the tiled kernel with M, N and K tails; the stress recipe
+# (outliers, all-zero blocks) on the tiled kernel; -0.0 blocks and bf16 extremes.
+EDGE = [(3, 70, 352), (16, 130, 7232), (50, 20000, 1056), (33, 64, 352), (127, 257, 1056), (65, 130, 288),
+        (300, 600, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE)
+def test_fused_quant_bytes_edges(M, N, K):
+    g = np.random.default_rng(M * 31 + N + K)
+    x = g.standard_normal((M, K)) * np.exp2(g.integers(-20, 20, (M, 1)))
+    a = synth.f32_to_bf16_bits(x.astype(np.float32))
+    a[0, :32] = 0x8000          # an all -0.0 block: codes 8, scale 0 in the GEMM
+    a[-1, -32:] = 0             # an all +0.0 block
+    a[M // 2, 0] = 0x7F7F       # bf16 max
+    a[M // 2, 1] = 0x0001       # smallest subnormal
+    b = synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    run_single(a, b, N, f"M={M} N={N} K={K}")
+
+
+def test_fused_quant_bytes_stress_recipe_on_tiled_kernel():
+    M, N, K = 256, 1024, 2048
+    a = synth.make_stress_a(M, K, 77)
+    run_single(a, synth.make_stress_b(N, K, 77), N, "stress recipe M=256")

@@ -67,6 +67,19 @@ def test_quant_workload_bytes(name):
         assert np.array_equal(q, q0), f"{name} {which} codes"
 
 
+@pytest.mark.timeout(600)
+def test_quant_workload_bytes_grouped():
+    say("quant workload grouped (every group's A and B)")
+    w = synth.workload("grouped", synth.default_seed("grouped"))
+    mats = list(w["A"]) + list(w["B"])
+    refs = quant_groups_in_pool(mats)
+    for i, (x, (q0, s0)) in enumerate(zip(mats, refs)):
+        q, s = gpu_quant(x)
+        what = f"grouped {'A' if i < len(w['A']) else 'B'}{i % len(w['A'])}"
+        assert np.array_equal(s, s0), f"{what} scales"
+        assert np.array_equal(q, q0), f"{what} codes"
+
+
 @pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (17, 32), (5, 7168), (300, 224)])
 def test_quant_edge_shapes_and_strides(M, K):
     say(f"quant edge M={M} K={K}")
@@ -328,3 +341,38 @@ def test_grouped_ragged_small():
     torch.cuda.synchronize()
     for x, (bq, bs), c in zip(a, qs, cs):
         assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
+
+
+def test_gemm_two_streams_use_their_own_workspaces():
+    """Split-K calls (M <= 16, partials through the workspace) issued on two streams at once: each stream
+    has its own workspace, both results equal the one-stream results bit for bit, and both workspaces
+    are left zeroed."""
+    say("gemm on two streams")
+    M, N, K = 16, 2112, 7168
+    g = np.random.default_rng(41)
+    a1 = synth.f32_to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    a2 = synth.f32_to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    b = synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    bq, bs = oracle.quant_mx(b)
+    bp = packed_b(bq, bs)
+    t1, t2 = to_dev_bf16(a1), to_dev_bf16(a2)
+    r1, r2 = bits_of(ops.gemm(t1, bp, N)), bits_of(ops.gemm(t2, bp, N))
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs1, outs2 = [], []
+    for _ in range(20):
+        with torch.cuda.stream(s1):
+            outs1.append(ops.gemm(t1, bp, N))
+        with torch.cuda.stream(s2):
+            outs2.append(ops.gemm(t2, bp, N))
+    torch.cuda.synchronize()
+    for c in outs1:
+        assert np.array_equal(bits_of(c), r1)
+    for c in outs2:
+        assert np.array_equal(bits_of(c), r2)
+    wsz = ops.lib().gemm_a4w4_workspace_bytes(M, N, K)
+    w1 = ops.workspace(t1.device, wsz, s1.cuda_stream)
+    w2 = ops.workspace(t2.device, wsz, s2.cuda_stream)
+    assert w1.data_ptr() != w2.data_ptr()
+    assert (w1[:wsz].cpu().numpy() == 0).all() and (w2[:wsz].cpu().numpy() == 0).all()
+    assert_in_tolerance(r1, oracle.gemm_ref(a1, bq, bs), "stream 1")
