@@ -151,6 +151,27 @@ int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t
                     int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * gemm_a4w4_fused_noalloc -- gemm_a4w4_fused without a workspace argument and
+ * without any allocation, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same kernels, tiling and arithmetic, so C equals
+ * gemm_a4w4_fused's bit for bit. The split-K partials (M <= 16) go to a fixed
+ * device array of MXFP4_NOALLOC_SCRATCH_BYTES bytes inside the library, one
+ * per GPU, held until the process ends; a call whose split-K geometry needs
+ * more (gemm_a4w4_workspace_bytes(M, N, K) > MXFP4_NOALLOC_SCRATCH_BYTES, e.g.
+ * very large N*K at M <= 16) returns MXFP4_ERR_WORKSPACE and launches nothing.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on one
+ * GPU (different streams, or concurrent host threads) race and must not be
+ * issued; use gemm_a4w4_fused with distinct workspaces for those. The first
+ * call on a device looks up the array's device address (a HIP call, no
+ * allocation); it runs on the device of `stream` (the current device for
+ * NULL). Other arguments and errors as for gemm_a4w4_fused.
+ * ------------------------------------------------------------------------- */
+#define MXFP4_NOALLOC_SCRATCH_BYTES (4u << 20)
+int gemm_a4w4_fused_noalloc(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M,
+                            int64_t N, int64_t K, void* stream);
+
+/* ---------------------------------------------------------------------------
  * gemm_a4w4_fused_dump -- verification form of gemm_a4w4_fused: the same
  * call (same kernel choice, tiling, arithmetic and C), whose kernels also
  * write the quantised A they compute on chip, so that it can be compared byte

@@ -34,6 +34,7 @@
 //    per-wave LDS staging block as 16-byte row stores. Workgroups are ordered
 //    so that the ones sharing an XCD (and its L2) share A rows and B columns.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "host_common.hpp"
@@ -1264,6 +1265,65 @@ int fused_call(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc,
 extern "C" int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M, int64_t N,
                                int64_t K, void* workspace, size_t workspace_bytes, void* stream) {
   return fused_call(A, lda, Bp, C, ldc, M, N, K, workspace, workspace_bytes, nullptr, 0, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free form of gemm_a4w4_fused, for callers that cannot allocate.
+// ---------------------------------------------------------------------------
+// The split-K partial slots (M <= 16) live in this fixed array instead of a
+// caller workspace. Each GPU the library runs on holds its own copy for the
+// life of the process; it is zero at load, and every completed call leaves the
+// slots it used zero again (the tile owners clear them), so no call has to
+// clear it first. Host code must not pass `scratch` itself to a kernel (that is
+// a host-side stand-in): its device address comes from hipGetSymbolAddress,
+// taken once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[MXFP4_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream).
+int scratch_address(void* stream, void** out) {
+  int cur = 0;
+  if (hipGetDevice(&cur) != hipSuccess) return MXFP4_ERR_HIP;
+  int dev = cur;
+  if (stream) {
+    hipDevice_t d = 0;
+    if (hipStreamGetDevice((hipStream_t)stream, &d) != hipSuccess) return MXFP4_ERR_HIP;
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MXFP4_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return MXFP4_ERR_HIP;
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || !p) return MXFP4_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MXFP4_OK;
+}
+}  // namespace
+
+extern "C" int gemm_a4w4_fused_noalloc(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M,
+                                       int64_t N, int64_t K, void* stream) {
+  const int st = check_problem(A, lda, Bp, C, ldc, M, N, K);
+  if (st != MXFP4_OK) return st;
+  const SplitGeom g = split_geom(M, N, K);
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (g.ok && g.total() > 0) {
+    if (g.total() > (size_t)MXFP4_NOALLOC_SCRATCH_BYTES) return MXFP4_ERR_WORKSPACE;  // beyond the fixed scratch
+    const int s2 = scratch_address(stream, &ws);
+    if (s2 != MXFP4_OK) return s2;
+    ws_bytes = MXFP4_NOALLOC_SCRATCH_BYTES;
+  }
+  return fused_call(A, lda, Bp, C, ldc, M, N, K, ws, ws_bytes, nullptr, 0, stream);
 }
 
 extern "C" size_t gemm_a4w4_fused_dump_bytes(int64_t M, int64_t N, int64_t K) {

@@ -144,6 +144,28 @@ def test_gemm_validation(change, status):
     assert got == status
 
 
+@pytest.mark.parametrize("change,status", [
+    (dict(A=None), 1), (dict(Bp=None), 1), (dict(C=None), 1),
+    (dict(M=0), 2), (dict(K=7000), 2), (dict(lda=7000), 2), (dict(lda=1 << 23), 2),
+    (dict(A=P + 2), 3), (dict(C=P + 1), 3),
+    # split-K needs 256 tiles x 63 splits x 4 KB of partials, more than the fixed scratch holds
+    (dict(M=16, N=16384, K=65536, lda=65536, ldc=16384), 4),
+])
+def test_gemm_noalloc_validation(change, status):
+    a = dict(OK_G, **change)
+    got = ops.lib().gemm_a4w4_fused_noalloc(a["A"], a["lda"], a["Bp"], a["C"], a["ldc"], a["M"], a["N"], a["K"], None)
+    assert got == status
+
+
+def test_noalloc_scratch_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MXFP4_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    limit = int(m.group(1)) << int(m.group(2))
+    L = ops.lib()
+    assert L.gemm_a4w4_workspace_bytes(16, 16384, 65536) > limit
+    assert 0 < L.gemm_a4w4_workspace_bytes(16, 2112, 7168) <= limit
+
+
 OK_Q4 = dict(Aq=P, ldaq=3584, As=P, ldas=224, Bp=P, C=P, ldc=2112, M=16, N=2112, K=7168, ws=P, wsb=1 << 30)
 
 
