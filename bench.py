@@ -82,7 +82,10 @@ def parse():
                    help="time the two-launch comparator instead: mxfp4_quant(A), then gemm_a4w4 on A_q")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain device copies of a known size (counter calibration)")
-    p.add_argument("--summarize-stats", metavar="DIR", help="print a summary of rocprofv3 --stats CSV output")
+    p.add_argument("--summarize-stats", metavar="DIR", help="print a summary of rocprofv3 --kernel-trace CSV output")
+    p.add_argument("--last", type=int, default=None, metavar="K",
+                   help="with --summarize-stats: only the last K dispatches of each kernel and grid (a bench "
+                        "run's timed replay is the last --steps dispatches of its workload's kernel)")
     p.add_argument("--summarize-pmc", nargs=3, metavar=("WORKLOAD_DIR", "COPY_DIR", "KERNEL"),
                    help="turn FETCH_SIZE/WRITE_SIZE runs into the traffic record for KERNEL")
     p.add_argument("--summarize-counters", nargs=2, metavar=("DIR", "KERNEL"),
@@ -130,21 +133,28 @@ def _csv_rows(directory, suffix):
     return rows
 
 
-def summarize_stats(directory):
-    """Per-kernel table from a rocprofv3 --kernel-trace --stats run: calls, mean, the
-    10th / 50th / 90th percentile of the per-dispatch durations (from the trace),
-    min, max and share of the total."""
-    rows = _csv_rows(directory, "kernel_stats.csv")
+def summarize_stats(directory, last=None):
+    """Per-kernel table from a rocprofv3 --kernel-trace run: one row per kernel and grid size (the split-K
+    kernel serves tiny and skinny with one instance), with the calls, the mean, the 10th / 50th / 90th
+    percentile, min and max of the per-dispatch durations, and the share of the total kernel time. With
+    `last`, only the last `last` dispatches (by start time) of each kernel and grid count."""
     durs = {}
-    for r in _csv_rows(directory, "kernel_trace.csv"):
-        durs.setdefault(r["Kernel_Name"], []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    print("| kernel | calls | avg µs | p10 µs | median µs | p90 µs | min µs | max µs | share % |")
-    print("|---|---|---|---|---|---|---|---|---|")
-    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        d = durs.get(r["Name"])
-        pct = "| — | — | — " if not d else "| {:.3f} | {:.3f} | {:.3f} ".format(*np.percentile(d, [10, 50, 90]))
-        print(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} {pct}| "
-              f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | {float(r['Percentage']):.1f} |")
+    rows = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    for r in rows:
+        wgs = 1
+        for ax in "XYZ":
+            wgs *= max(1, int(r[f"Grid_Size_{ax}"]) // max(1, int(r[f"Workgroup_Size_{ax}"])))
+        durs.setdefault((r["Kernel_Name"], wgs), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if last:
+        durs = {k: d[-last:] for k, d in durs.items()}
+    total = sum(sum(d) for d in durs.values()) or 1.0
+    print("| kernel | workgroups | calls | avg µs | p10 µs | median µs | p90 µs | min µs | max µs | share % |")
+    print("|---|---|---|---|---|---|---|---|---|---|")
+    for (name, wgs), d in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        p10, p50, p90 = np.percentile(d, [10, 50, 90])
+        print(f"| {name[:90]} | {wgs} | {len(d)} | {np.mean(d):.3f} | {p10:.3f} | {p50:.3f} | {p90:.3f} | "
+              f"{min(d):.3f} | {max(d):.3f} | {100 * sum(d) / total:.1f} |")
 
 
 def summarize_pmc(workload_dir, copy_dir, kernel):
@@ -547,7 +557,7 @@ def copy_calibration():
 def main():
     args = parse()
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats)
+        summarize_stats(args.summarize_stats, args.last)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
