@@ -60,9 +60,10 @@ def alg_flops(M, N, K):
     return 2 * M * N * K
 
 
-WORKLOADS = ["tiny", "skinny", "stress", "square", "grouped", "rmsnorm", "grouped_mnk", "skinny_shard8", "nvfp4_grouped"]
+WORKLOADS = ["tiny", "skinny", "stress", "square", "grouped", "grouped_decode", "rmsnorm", "grouped_mnk", "skinny_shard8",
+             "nvfp4_grouped"]
 HEADLINE = "square"                       # the largest single-GPU configuration the metric spans
-EXTRAS = ["skinny", "stress", "tiny", "grouped"]
+EXTRAS = ["skinny", "stress", "tiny", "grouped", "grouped_decode"]
 
 
 def parse():
@@ -261,8 +262,9 @@ def time_oracle(fn, budget_s=12.0, max_runs=50):
 def cpu_baseline(w, unit):
     """Time the oracle (untuned) on a bounded sample of the workload, scaled to the metric's unit."""
     import oracle
+    from mxfp4_block_scaled_02_amd import synth
     name = w["name"]
-    if name == "grouped":
+    if name in synth.GROUPED:
         a, b = w["A"][0], w["B"][0]
     else:
         a, b = w["A"], w["B"]
@@ -275,7 +277,7 @@ def cpu_baseline(w, unit):
     value = alg_flops(m, N, K) / t / 1e12 if unit == "TFLOP/s" else alg_bytes(m, N, K) / t / 1e9
     return dict(value=round(value, 6), unit=unit, cores=n, kind="oracle",
                 sample=f"oracle gemm_ref (quant A, dequant A and B, fp64 matmul, bf16 round) on rows 0..{m - 1} of "
-                       f"{'group 0' if name == 'grouped' else 'A'} against the full B (N={N}, K={K}); median of "
+                       f"{'group 0' if name in synth.GROUPED else 'A'} against the full B (N={N}, K={K}); median of "
                        f"{runs} runs, {t * 1e3:.1f} ms each; numpy's BLAS on {n} threads, the rest single-threaded",
                 affinity_cpus=aff, cpu_model=cpu_model())
 
@@ -616,7 +618,7 @@ def bench_gemm(name, args):
     """One fused call (or, with --unfused, mxfp4_quant + gemm_a4w4) per step over rotated operand sets.
     Returns (the JSON record, the workload's inputs, the roofline unit)."""
     import torch
-    from mxfp4_block_scaled_02_amd import ops
+    from mxfp4_block_scaled_02_amd import ops, synth
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -631,7 +633,7 @@ def bench_gemm(name, args):
         bq, bs = ops.quant(bf16(b_bits))  # offline weight quantisation on the GPU (same kernel family)
         return ops.pack_B(bq, bs)
 
-    if name == "grouped":
+    if name in synth.GROUPED:
         Ms, N, K = w["Ms"], w["N"], w["K"]
         total_bytes = sum(alg_bytes(m, N, K) for m in Ms)
         total_flops = sum(alg_flops(m, N, K) for m in Ms)
@@ -647,7 +649,7 @@ def bench_gemm(name, args):
     log(f"[bench] operand set {set_bytes / 1e6:.2f} MB, rotating {R} sets")
     sets = []
     for r in range(R):
-        if name == "grouped":
+        if name in synth.GROUPED:
             a = [x.clone() for x in a0] if r else a0
             b = [x.clone() for x in b0] if r else b0
             c = [torch.empty((m, N), dtype=torch.bfloat16, device=dev) for m in Ms]
@@ -657,14 +659,14 @@ def bench_gemm(name, args):
             c = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         sets.append((a, b, c))
     if args.unfused:
-        if name == "grouped":
+        if name in synth.GROUPED:
             raise SystemExit("--unfused covers the single-GEMM workloads")
         aq = torch.empty((M, K // 2), dtype=torch.uint8, device=dev)
         asc = torch.empty((M, K // 32), dtype=torch.uint8, device=dev)
 
     def step(i):
         a, b, c = sets[i % R]
-        if name == "grouped":
+        if name in synth.GROUPED:
             ops.grouped_gemm(a, b, N, out_list=c)
         elif args.unfused:
             ops.quant(a, out=(aq, asc))
@@ -684,8 +686,8 @@ def bench_gemm(name, args):
     cfg = dict(workload=name, seed=seed, cache=cache_label(args, R, set_bytes),
                timing="hip graph replay" if not args.no_graph else "eager launch loop",
                path="unfused: mxfp4_quant + gemm_a4w4 (two launches)" if args.unfused else "fused: gemm_a4w4_fused"
-               if name != "grouped" else "fused: grouped_gemm_a4w4 (one launch)")
-    if name == "grouped":
+               if name not in synth.GROUPED else "fused: grouped_gemm_a4w4 (one launch)")
+    if name in synth.GROUPED:
         cfg.update(G=len(Ms), Ms=Ms, N=N, K=K)
     else:
         cfg.update(M=M, N=N, K=K)

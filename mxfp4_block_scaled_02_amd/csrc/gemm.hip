@@ -156,18 +156,31 @@ constexpr int kSkWaves = 16;
 // rows x 4 chunks x 4 dwords) and each 16-lane operand read conflict-free.
 __device__ __forceinline__ int slot16(int row, int chunk) { return chunk * 16 + (row ^ (chunk << 2)); }
 
-template <int MS, int NB, int PF, bool DUMP>
-__global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, Dims d) {
+// LDS of one skinny tile: per-wave A operand codes and scales, and the waves'
+// partial C tiles.
+template <int WAVES, int NB>
+struct SkinnySmem {
+  uint32_t aq[WAVES][64 * 4];
+  uint8_t as[WAVES][64];
+  float red[WAVES][NB * 4][64];
+};
+
+// Rows m0 .. m0+MS-1 x 16-column tiles T0 .. T0+NB-1 of C over the whole K, by
+// the WAVES waves of the calling workgroup (all of its threads), each taking a
+// contiguous share of the K steps; the partial tiles are summed in LDS. `copy`
+// is the verification dump's copy index of this tile's quantised A.
+template <int WAVES, int MS, int NB, int PF, bool DUMP>
+__device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int m0, int T0, int copy,
+                                            SkinnySmem<WAVES, NB>& sm) {
   static_assert(MS == 4 || MS == 8 || MS == 16, "rows per workgroup");
   constexpr int PIECES = MS / 4;  // 16-byte A pieces per lane per K step
-  __shared__ __align__(16) uint32_t sAq[kSkWaves][64 * 4];  // per-wave A operand codes
-  __shared__ uint8_t sAs[kSkWaves][64];                    // per-wave A operand scales
-  __shared__ float red[kSkWaves][NB * 4][64];              // partial C tiles
+  auto& sAq = sm.aq;
+  auto& sAs = sm.as;
+  auto& red = sm.red;
 
   const int l = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
-  const int m0 = blockIdx.y * MS, T0 = blockIdx.x * NB;
-  const int jb = d.KT * wave / kSkWaves, je = d.KT * (wave + 1) / kSkWaves;
+  const int jb = d.KT * wave / WAVES, je = d.KT * (wave + 1) / WAVES;
 
   // Rows MS..15 of the operand are never written: zero codes, neutral scales.
 #pragma unroll
@@ -250,7 +263,7 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, D
         for (int h = 0; h < PIECES; ++h) {
           uint32_t sb;
           const uint32_t code = mx::quant8_quad(w[s][h], sb);
-          if constexpr (DUMP) dump_piece(p, d.K, blockIdx.x, m0 + 4 * h + (l >> 4), 128 * j + 8 * (l & 15), code, sb, sub == 0);
+          if constexpr (DUMP) dump_piece(p, d.K, copy, m0 + 4 * h + (l >> 4), 128 * j + 8 * (l & 15), code, sb, sub == 0);
           sAq[wave][wslot[h] * 4 + sub] = code;
           sAs[wave][wslot[h]] = (uint8_t)sb;  // the quad's four lanes store the same byte
         }
@@ -264,23 +277,29 @@ __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, D
     }
   }
 
-  // Sum the 16 waves' partial tiles in LDS and store bf16.
+  // Sum the waves' partial tiles in LDS and store bf16.
 #pragma unroll
   for (int t = 0; t < NB; ++t)
 #pragma unroll
     for (int e = 0; e < 4; ++e) red[wave][t * 4 + e][l] = acc[t][e];
   __syncthreads();
   constexpr int OUT = NB * 256;
-  for (int o = threadIdx.x; o < OUT; o += kSkWaves * 64) {
+  for (int o = threadIdx.x; o < OUT; o += WAVES * 64) {
     const int slot = o >> 6, ll = o & 63, t = slot >> 2, e = slot & 3;
     const int r = 4 * (ll >> 4) + e;
     if (r >= MS) continue;
     float sum = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < kSkWaves; ++w2) sum += red[w2][slot][ll];
+    for (int w2 = 0; w2 < WAVES; ++w2) sum += red[w2][slot][ll];
     const int row = m0 + r, col = (T0 + t) * 16 + (ll & 15);
     if (row < p.M && col < d.N) p.C[(int64_t)row * p.ldc + col] = mx::f32_to_bf16(sum);
   }
+}
+
+template <int MS, int NB, int PF, bool DUMP>
+__global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, Dims d) {
+  __shared__ __align__(16) SkinnySmem<kSkWaves, NB> sm;
+  skinny_tile<kSkWaves, MS, NB, PF, DUMP>(p, d, blockIdx.y * MS, blockIdx.x * NB, blockIdx.x, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -982,22 +1001,59 @@ __global__ __launch_bounds__(kTThreads) void gemm_tiled_kernel(Operand p, Dims d
   tiled_tile<PREQ, DUMP>(p, d, v / ntiles_n, v % ntiles_n, sm, ring);
 }
 
+// Grouped GEMM. A group of at most kGsMaxM rows is an HBM-bound problem (its B
+// is read once for very few rows): it takes small tiles of 16 rows x 128
+// columns over the whole K, the workgroup's 8 waves splitting K (the skinny
+// tile), so that its B spreads over many CUs; a 128 x 512 tile would give it one
+// CU per 512 columns and leave the matrix cores of that CU computing 128 rows
+// for 16 (at up to 48 rows the small tiles measured faster, at 64 slower).
+// Larger groups take the 128 x 512 tiled tiles. The large tiles take the first
+// workgroup ids, so the hardware starts them first (they run longest), and the
+// small tiles fill the other CUs beside them and whatever frees up. Each range
+// is remapped for the XCDs on its own (the large range padded to a multiple of
+// 8 ids with idle workgroups), and a small group's row tiles of one column tile
+// are adjacent (they share that B in one XCD's L2).
+constexpr int kGsMaxM = 48, kGsMS = 16, kGsNB = 8, kGsPF = 2;
+
 struct GroupedArgs {
   Operand g[MXFP4_MAX_GROUPS];
-  int tile_start[MXFP4_MAX_GROUPS + 1];  // prefix sums of per-group tile counts
+  int tile_start[MXFP4_MAX_GROUPS + 1];  // prefix sums of the entries' tile counts, in launch order
+  int order[MXFP4_MAX_GROUPS];           // group of launch entry e: large groups, then small ones
+  int rows[MXFP4_MAX_GROUPS];            // row tiles of entry e (16-row tiles for a small group)
+  int small_from;                        // first entry of a small group
+  int nlarge, nlarge_pad;                // large tiles, and their id range rounded up to a multiple of 8
   int G;
-  int ntiles_n;
+  int ntiles_n;                          // 512-column tiles of a large group
 };
 
 template <bool DUMP>
 __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, Dims d) {
-  const int v = xcd_remap(blockIdx.x, gridDim.x);
-  int g = 0;
-  while (g + 1 < a.G && a.tile_start[g + 1] <= v) ++g;
-  const int local = v - a.tile_start[g];
+  const int b = blockIdx.x;
+  int v;
+  if (b < a.nlarge_pad) {
+    if (b >= a.nlarge) return;  // padding: the whole workgroup leaves
+    v = xcd_remap(b, a.nlarge);
+  } else {
+    v = a.nlarge + xcd_remap(b - a.nlarge_pad, (int)gridDim.x - a.nlarge_pad);
+  }
+  int e = 0;
+  while (e + 1 < a.G && a.tile_start[e + 1] <= v) ++e;
+  const int local = v - a.tile_start[e];
+  const Operand& p = a.g[a.order[e]];
+  // The tiled tile's operand tiles and its B ring stay two LDS objects: the
+  // compiler then knows that the ring's buffer-to-LDS loads do not write the
+  // tiles it reads, and adds no wait for them. The skinny tile (no such loads)
+  // lives in the ring's bytes.
   __shared__ __align__(16) TiledSmem sm;
   __shared__ __align__(16) uint8_t ring[kRingBytes];
-  tiled_tile<false, DUMP>(a.g[g], d, local / a.ntiles_n, local % a.ntiles_n, sm, ring);
+  static_assert(sizeof(SkinnySmem<kTWaves, kGsNB>) <= sizeof(ring), "skinny tile LDS");
+  if (e >= a.small_from) {
+    const int c = local / a.rows[e], r = local - c * a.rows[e];
+    skinny_tile<kTWaves, kGsMS, kGsNB, kGsPF, DUMP>(p, d, r * kGsMS, c * kGsNB, c,
+                                                     *reinterpret_cast<SkinnySmem<kTWaves, kGsNB>*>(ring));
+  } else {
+    tiled_tile<false, DUMP>(p, d, local / a.ntiles_n, local % a.ntiles_n, sm, ring);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1371,11 +1427,15 @@ extern "C" size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, i
 }
 
 namespace {
-// Verification dump of the grouped call: group g's block (copies = N-tiles,
-// codes then scales, as for the single call) follows group g-1's.
+// Copies of a group's quantised A in the verification dump: one per column tile
+// of the tile kind the group takes.
+int64_t grouped_copies(int64_t M, int64_t N) { return M <= kGsMaxM ? mxh::cdiv(N, 16 * kGsNB) : mxh::cdiv(N, kTBN); }
+
+// Verification dump of the grouped call: group g's block (its copies, codes
+// then scales, as for the single call) follows group g-1's.
 size_t grouped_dump_bytes_of(const mxfp4_group* groups, int G, int64_t N, int64_t K) {
   size_t t = 0;
-  for (int g = 0; g < G; ++g) t += (size_t)(mxh::cdiv(N, kTBN) * groups[g].M * (K / 2 + K / 32));
+  for (int g = 0; g < G; ++g) t += (size_t)(grouped_copies(groups[g].M, N) * groups[g].M * (K / 2 + K / 32));
   return t;
 }
 
@@ -1384,33 +1444,53 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
   if (G < 1 || G > MXFP4_MAX_GROUPS) return MXFP4_ERR_TOO_MANY_GROUPS;
   GroupedArgs a{};
   const int64_t ntn = mxh::cdiv(N, kTBN);
-  int64_t total = 0;
   for (int g = 0; g < G; ++g) {
     const mxfp4_group& q = groups[g];
     const int st = check_problem(q.A, q.lda, q.Bp, q.C, q.ldc, q.M, N, K);
     if (st != MXFP4_OK) return st;
     a.g[g] = make_operand(q.A, q.lda, q.Bp, q.C, q.ldc, q.M, N, K);
-    a.tile_start[g] = (int)total;
-    total += mxh::cdiv(q.M, kTBM) * ntn;
-    if (total > INT32_MAX) return MXFP4_ERR_SHAPE;
+  }
+  // Launch entries: the large groups in their order, then the small ones.
+  int64_t total = 0;
+  int e = 0;
+  for (int small = 0; small < 2; ++small) {
+    if (small) {
+      a.small_from = e;
+      a.nlarge = (int)total;
+      a.nlarge_pad = (int)mxh::cdiv(total, 8) * 8;
+    }
+    for (int g = 0; g < G; ++g) {
+      const int64_t M = groups[g].M;
+      if ((M <= kGsMaxM) != (small != 0)) continue;
+      const int64_t rows = small ? mxh::cdiv(M, kGsMS) : mxh::cdiv(M, kTBM);
+      a.order[e] = g;
+      a.rows[e] = (int)rows;
+      a.tile_start[e] = (int)total;
+      total += rows * (small ? mxh::cdiv(N, 16 * kGsNB) : ntn);
+      if (total > INT32_MAX) return MXFP4_ERR_SHAPE;
+      ++e;
+    }
   }
   if (dump) {
     if (dump_bytes < grouped_dump_bytes_of(groups, G, N, K)) return MXFP4_ERR_BUFFER;
     if (!mxh::aligned(dump, 16)) return MXFP4_ERR_ALIGN;
     uint8_t* at = (uint8_t*)dump;
     for (int g = 0; g < G; ++g) {
+      const int64_t copies = grouped_copies(groups[g].M, N);
       a.g[g].dq = at;
-      a.g[g].ds = at + ntn * groups[g].M * (K / 2);
-      at += ntn * groups[g].M * (K / 2 + K / 32);
+      a.g[g].ds = at + copies * groups[g].M * (K / 2);
+      at += copies * groups[g].M * (K / 2 + K / 32);
     }
   }
   a.tile_start[G] = (int)total;
   a.G = G;
   a.ntiles_n = (int)ntn;
+  const int64_t grid = total + (a.nlarge_pad - a.nlarge);
+  if (grid > INT32_MAX) return MXFP4_ERR_SHAPE;
   Dims d = make_dims(N, K);
   void* args[] = {&a, &d};
   return mxh::launch_status(hipLaunchKernel(
-      dump ? (const void*)gemm_grouped_kernel<true> : (const void*)gemm_grouped_kernel<false>, dim3((unsigned)total),
+      dump ? (const void*)gemm_grouped_kernel<true> : (const void*)gemm_grouped_kernel<false>, dim3((unsigned)grid),
       dim3(kTThreads), args, 0, (hipStream_t)stream));
 }
 }  // namespace
@@ -1427,6 +1507,11 @@ extern "C" size_t grouped_gemm_a4w4_dump_bytes(const mxfp4_group* groups, int G,
   for (int g = 0; g < G; ++g)
     if (groups[g].M < 1 || groups[g].M > mxh::kMaxDim) return 0;
   return grouped_dump_bytes_of(groups, G, N, K);
+}
+
+extern "C" int64_t grouped_gemm_a4w4_dump_copies(int64_t M, int64_t N) {
+  if (M < 1 || M > mxh::kMaxDim || N < 1 || N > mxh::kMaxDim) return 0;
+  return grouped_copies(M, N);
 }
 
 extern "C" int grouped_gemm_a4w4_dump(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,

@@ -26,7 +26,7 @@ EXPORTED = ["mxfp4_status_str", "mxfp4_quant", "mxfp4_rmsnorm_quant", "mxfp4_pac
             "gemm_a4w4_workspace_bytes", "gemm_a4w4_fused", "gemm_a4w4_fused_noalloc", "gemm_a4w4_fused_dump_bytes",
             "gemm_a4w4_fused_dump",
             "gemm_a4w4", "grouped_gemm_a4w4_workspace_bytes", "grouped_gemm_a4w4", "grouped_gemm_a4w4_dump_bytes",
-            "grouped_gemm_a4w4_dump", "grouped_gemm_a4w4_mnk", "grouped_gemm_nvfp4"]
+            "grouped_gemm_a4w4_dump_copies", "grouped_gemm_a4w4_dump", "grouped_gemm_a4w4_mnk", "grouped_gemm_nvfp4"]
 
 
 class Mxfp4Error(RuntimeError):
@@ -87,6 +87,7 @@ def lib() -> ctypes.CDLL:
         L.gemm_a4w4_fused_dump.restype = i32
         L.grouped_gemm_a4w4_dump_bytes.argtypes = [ctypes.POINTER(Group), i32, i64, i64]
         L.grouped_gemm_a4w4_dump_bytes.restype = sz
+        L.grouped_gemm_a4w4_dump_copies.argtypes, L.grouped_gemm_a4w4_dump_copies.restype = [i64, i64], i64
         L.grouped_gemm_a4w4_dump.argtypes = [ctypes.POINTER(Group), i32, i64, i64, vp, sz, vp, sz, vp]
         L.grouped_gemm_a4w4_dump.restype = i32
         L.gemm_a4w4.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp]
@@ -300,9 +301,10 @@ def grouped_gemm_dump(a_list, bp_list, N: int):
     dump = torch.full((dsz,), 0xEE, dtype=torch.uint8, device=a_list[0].device)
     _check(lib().grouped_gemm_a4w4_dump(arr, G, N, K, None, 0, dump.data_ptr(), dsz, _stream(a_list[0])),
            "grouped_gemm_a4w4_dump")
-    copies, at, res = -(-N // 512), 0, []
+    at, res = 0, []
     for a in a_list:
         M = a.shape[0]
+        copies = int(lib().grouped_gemm_a4w4_dump_copies(M, N))
         nq, ns = copies * M * (K // 2), copies * M * (K // 32)
         res.append((dump[at:at + nq].view(copies, M, K // 2), dump[at + nq:at + nq + ns].view(copies, M, K // 32)))
         at += nq + ns

@@ -21,6 +21,9 @@ kernelbot nvfp4-group-gemm submission 496271):
            each group has its own A_g ~ N(0,1) and B_g ~ N(0,0.02)
   skinny_shard8  M=16 N=264 K7168: one GPU's share of skinny when N is split
            eight ways (skinny's A and the first 264 rows of its B, same seed)
+  grouped_decode  the grouped form with decode-sized groups: 8 groups sharing
+           N=4096, K=7168, M_g = 8*U{1..8} (each group's B read for a few rows,
+           the case where a group of the list is HBM-bound)
 
 Every tensor draws from its own stream:
 numpy PCG64(SeedSequence([seed, stream, *sub])). Streams: 0 = A, 1 = B,
@@ -37,8 +40,10 @@ WORKLOADS = {
     "square": dict(M=4096, N=4096, K=7168),
     "grouped": dict(G=8, N=4096, K=7168),
     "skinny_shard8": dict(M=16, N=264, K=7168),
+    "grouped_decode": dict(G=8, N=4096, K=7168),
 }
-WORKLOAD_ORDER = ["tiny", "skinny", "stress", "square", "grouped"]
+WORKLOAD_ORDER = ["tiny", "skinny", "stress", "square", "grouped", "grouped_decode"]
+GROUPED = ("grouped", "grouped_decode")
 SHARD_OF = {"skinny_shard8": "skinny"}  # a shard draws from its parent's seed
 
 STREAM_A, STREAM_B, STREAM_MASK, STREAM_ROWEXP, STREAM_GROUPS, STREAM_NORM_W = 0, 1, 2, 3, 4, 5
@@ -101,20 +106,24 @@ def group_sizes(seed: int, G: int = 8) -> list:
     return [128 + 64 * int(v) for v in rng(seed, STREAM_GROUPS).integers(0, 15, size=G)]
 
 
+def decode_group_sizes(seed: int, G: int = 8) -> list:
+    return [8 * int(v) for v in rng(seed, STREAM_GROUPS).integers(1, 9, size=G)]
+
+
 def workload(name: str, seed: int, rows=None):
     """Inputs of one workload: dict with M/N/K and bf16 bit arrays.
 
     ``rows`` (optional array of row indices) returns only those rows of A, drawn
     exactly as in the full tensor (the full A is generated, then sliced).
-    For "grouped" the dict holds lists ``A`` and ``B`` and ``Ms``.
+    For the grouped workloads the dict holds lists ``A`` and ``B`` and ``Ms``.
     """
     if name not in WORKLOADS:
         raise KeyError(name)
     w = dict(WORKLOADS[name])
     w["name"] = name
     w["seed"] = seed
-    if name == "grouped":
-        Ms = group_sizes(seed, w["G"])
+    if name in GROUPED:
+        Ms = (group_sizes if name == "grouped" else decode_group_sizes)(seed, w["G"])
         w["Ms"] = Ms
         w["A"] = [make_a(m, w["K"], seed, (g,)) for g, m in enumerate(Ms)]
         w["B"] = [make_b(w["N"], w["K"], seed, (g,)) for g in range(w["G"])]

@@ -19,7 +19,7 @@ def cdiv(a, b):
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?(?:int64_t|int|size_t|char\s*\*|const char\s*\*)\s*\*?\s*(\w+)\s*\(",
                                  text, flags=re.M)))
 
 
@@ -199,6 +199,20 @@ def test_grouped_validation():
     assert L.grouped_gemm_a4w4(g, 2, 4096, 7168, None, 0, None) == 3
     g[1] = ops.Group(P, 1 << 23, P, P, 4096, 64)  # a 128-row window of A past 2^31 bytes
     assert L.grouped_gemm_a4w4(g, 2, 4096, 7168, None, 0, None) == 2
+
+
+def test_grouped_dump_layout():
+    """A group of at most 48 rows takes 128-column tiles (one dump copy each), a larger one 512-column tiles."""
+    L = ops.lib()
+    assert [L.grouped_gemm_a4w4_dump_copies(M, 4096) for M in (1, 16, 48, 49, 128, 4096)] == [32, 32, 32, 8, 8, 8]
+    assert L.grouped_gemm_a4w4_dump_copies(16, 1000) == 8 and L.grouped_gemm_a4w4_dump_copies(100, 1000) == 2
+    assert L.grouped_gemm_a4w4_dump_copies(0, 4096) == 0 and L.grouped_gemm_a4w4_dump_copies(16, 0) == 0
+    g = (ops.Group * 3)()
+    Ms, N, K = (16, 200, 64), 1000, 832
+    for i, M in enumerate(Ms):
+        g[i] = ops.Group(P, K, P, P, N, M)
+    want = sum(L.grouped_gemm_a4w4_dump_copies(M, N) * M * (K // 2 + K // 32) for M in Ms)
+    assert L.grouped_gemm_a4w4_dump_bytes(g, 3, N, K) == want == (8 * 16 + 2 * 200 + 2 * 64) * (416 + 26)
 
 
 def _mnk(**kw):

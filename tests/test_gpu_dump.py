@@ -10,7 +10,8 @@ so every product is zero under either scale). Which blocks are all-zero is read
 from the input, not from the kernel's output. C must equal the production
 call's C bit for bit (same arithmetic). Covers the split-K kernel (tiny, skinny),
 the skinny kernel (stress), the tiled kernel (square) and the grouped kernel
-(grouped), plus K, M and N tails.
+(grouped, and decode-sized groups, which take the skinny tile inside the
+grouped launch), plus K, M and N tails.
 """
 import numpy as np
 import pytest
@@ -75,6 +76,41 @@ def test_fused_quant_bytes_grouped():
     for g, (a, (codes, scales), c, cp) in enumerate(zip(w["A"], dumps, cs, prod)):
         check_copies(codes, scales, a, f"group {g} (M={a.shape[0]})")
         assert np.array_equal(bits_of(c), bits_of(cp)), f"group {g}: C of the dump instance differs"
+
+
+def run_grouped(a_list, b_list, N, what):
+    qs = [oracle.quant_mx(b) for b in b_list]
+    a_dev = [to_dev_bf16(a) for a in a_list]
+    bp = [ops.pack_B(to_dev_u8(bq), to_dev_u8(bs)) for bq, bs in qs]
+    cs, dumps = ops.grouped_gemm_dump(a_dev, bp, N)
+    prod = ops.grouped_gemm(a_dev, bp, N)
+    torch.cuda.synchronize()
+    for g, (a, (codes, scales), c, cp) in enumerate(zip(a_list, dumps, cs, prod)):
+        say(f"{what} group {g} (M={a.shape[0]}): {codes.shape[0]} copies")
+        check_copies(codes, scales, a, f"{what} group {g} (M={a.shape[0]})")
+        assert np.array_equal(bits_of(c), bits_of(cp)), f"{what} group {g}: C of the dump instance differs"
+
+
+def test_fused_quant_bytes_grouped_small_and_large():
+    """Groups of at most 48 rows (16 x 128 tiles, one copy per 128 columns) beside larger ones (one copy
+    per 512 columns), with M, N and K tails and zero blocks."""
+    g = np.random.default_rng(21)
+    N, K = 1000, 832
+    Ms = [1, 17, 48, 49, 200, 40]
+    a_list = []
+    for m in Ms:
+        a = synth.f32_to_bf16_bits((g.standard_normal((m, K)) * np.exp2(g.integers(-20, 20, (m, 1)))).astype(np.float32))
+        a[0, :32] = 0x8000
+        a[-1, -32:] = 0
+        a_list.append(a)
+    b_list = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
+    run_grouped(a_list, b_list, N, "mixed groups")
+
+
+@pytest.mark.timeout(600)
+def test_fused_quant_bytes_grouped_decode():
+    w = synth.workload("grouped_decode", synth.default_seed("grouped_decode"))
+    run_grouped(w["A"], w["B"], w["N"], "grouped_decode")
 
 
 # Split-K with M and K tails; the skinny kernel with an M tail, ragged N and a K

@@ -343,6 +343,36 @@ def test_grouped_ragged_small():
         assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
 
 
+def test_grouped_small_groups_mixed():
+    """Groups of at most 48 rows take 16 x 128 tiles over the whole K (K split over the workgroup's waves),
+    larger ones 128 x 512 tiles, in one launch: M tails (1, 17, 33, 63), the boundary (48 / 49), N not a
+    multiple of 128 or 512, and a K tail on odd K/64. 26 large tiles (their id range padded to 32 with
+    idle workgroups) ahead of 80 small ones."""
+    say("grouped small groups mixed with large ones")
+    g = np.random.default_rng(12)
+    N, K = 1000, 832
+    Ms = [1, 16, 17, 48, 49, 300, 33, 63, 1024]
+    a = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
+    b = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
+    qs = [oracle.quant_mx(x) for x in b]
+    cs = ops.grouped_gemm([to_dev_bf16(x) for x in a], [packed_b(*q) for q in qs], N)
+    torch.cuda.synchronize()
+    for x, (bq, bs), c in zip(a, qs, cs):
+        assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
+
+
+@pytest.mark.timeout(600)
+def test_grouped_decode_workload():
+    """The decode-sized grouped workload (8 groups of 8..64 rows, N4096 K7168), every row."""
+    say("grouped_decode workload")
+    w = synth.workload("grouped_decode", synth.default_seed("grouped_decode"))
+    qs = quant_groups_in_pool(w["B"])
+    cs = ops.grouped_gemm([to_dev_bf16(a) for a in w["A"]], [packed_b(bq, bs) for bq, bs in qs], w["N"])
+    torch.cuda.synchronize()
+    for g, (a, (bq, bs), c) in enumerate(zip(w["A"], qs, cs)):
+        assert_in_tolerance(bits_of(c), oracle.gemm_ref(a, bq, bs), f"group {g} (M={a.shape[0]})")
+
+
 def test_gemm_two_streams_use_their_own_workspaces():
     """Split-K calls (M <= 16, partials through the workspace) issued on two streams at once: each stream
     has its own workspace, both results equal the one-stream results bit for bit, and both workspaces

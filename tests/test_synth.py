@@ -46,6 +46,17 @@ def test_group_sizes():
         assert len(ms) == 8 and all(128 <= m <= 1024 and (m - 128) % 64 == 0 for m in ms)
 
 
+def test_decode_group_sizes():
+    for seed in range(5):
+        ms = synth.decode_group_sizes(seed)
+        assert len(ms) == 8 and all(8 <= m <= 64 and m % 8 == 0 for m in ms)
+    w = synth.workload("grouped_decode", synth.default_seed("grouped_decode"))
+    assert w["Ms"] == synth.decode_group_sizes(synth.default_seed("grouped_decode"))
+    assert [a.shape for a in w["A"]] == [(m, 7168) for m in w["Ms"]] and all(b.shape == (4096, 7168) for b in w["B"])
+    # existing workloads keep their seeds
+    assert [synth.default_seed(n) for n in ("tiny", "skinny", "stress", "square", "grouped")] == [0, 1, 2, 3, 4]
+
+
 def test_shard_is_a_slice_of_its_parent():
     a, b = synth.workload("skinny_shard8", synth.default_seed("skinny_shard8")), synth.workload("skinny", 1)
     assert synth.default_seed("skinny_shard8") == synth.default_seed("skinny")
