@@ -34,6 +34,7 @@
 //    per-wave LDS staging block as 16-byte row stores. Workgroups are ordered
 //    so that the ones sharing an XCD (and its L2) share A rows and B columns.
 #include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -156,24 +157,26 @@ constexpr int kSkWaves = 16;
 // rows x 4 chunks x 4 dwords) and each 16-lane operand read conflict-free.
 __device__ __forceinline__ int slot16(int row, int chunk) { return chunk * 16 + (row ^ (chunk << 2)); }
 
-// LDS of one skinny tile: per-wave A operand codes and scales, and the waves'
-// partial C tiles.
-template <int WAVES, int NB>
+// LDS of one skinny tile: per-wave A operand codes and scales of its MT 16-row
+// sub-tiles, and the waves' partial C tiles of one sub-tile.
+template <int WAVES, int NB, int MT = 1>
 struct SkinnySmem {
-  uint32_t aq[WAVES][64 * 4];
-  uint8_t as[WAVES][64];
+  uint32_t aq[WAVES][MT][64 * 4];
+  uint8_t as[WAVES][MT][64];
   float red[WAVES][NB * 4][64];
 };
 
 // Rows m0 .. m0+MS-1 x 16-column tiles T0 .. T0+NB-1 of C over the whole K, by
 // the WAVES waves of the calling workgroup (all of its threads), each taking a
-// contiguous share of the K steps; the partial tiles are summed in LDS. `copy`
-// is the verification dump's copy index of this tile's quantised A.
+// contiguous share of the K steps; the partial tiles are summed in LDS. MS of
+// 32 or 48 is two or three 16-row sub-tiles that share each B operand the wave
+// loads. `copy` is the verification dump's copy index of this tile's quantised A.
 template <int WAVES, int MS, int NB, int PF, bool DUMP>
 __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int m0, int T0, int copy,
-                                            SkinnySmem<WAVES, NB>& sm) {
-  static_assert(MS == 4 || MS == 8 || MS == 16, "rows per workgroup");
-  constexpr int PIECES = MS / 4;  // 16-byte A pieces per lane per K step
+                                            SkinnySmem<WAVES, NB, (MS + 15) / 16>& sm) {
+  static_assert(MS == 4 || MS == 8 || MS == 16 || MS == 32 || MS == 48, "rows per workgroup");
+  constexpr int MT = (MS + 15) / 16;  // 16-row sub-tiles
+  constexpr int PIECES = MS / 4;      // 16-byte A pieces per lane per K step (piece h: sub-tile h/4)
   auto& sAq = sm.aq;
   auto& sAs = sm.as;
   auto& red = sm.red;
@@ -183,13 +186,17 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
   const int jb = d.KT * wave / WAVES, je = d.KT * (wave + 1) / WAVES;
 
   // Rows MS..15 of the operand are never written: zero codes, neutral scales.
+  if constexpr (MS < 16) {
 #pragma unroll
-  for (int x = 0; x < 4; ++x) sAq[wave][x * 64 + l] = 0u;
-  sAs[wave][l] = (uint8_t)mx::kScaleOne;
+    for (int x = 0; x < 4; ++x) sAq[wave][0][x * 64 + l] = 0u;
+    sAs[wave][0][l] = (uint8_t)mx::kScaleOne;
+  }
 
-  mx::v4f acc[NB];
+  mx::v4f acc[MT][NB];
 #pragma unroll
-  for (int t = 0; t < NB; ++t) acc[t] = mx::v4f{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int t = 0; t < NB; ++t) acc[mt][t] = mx::v4f{0.f, 0.f, 0.f, 0.f};
 
   // Per-lane constants. A piece h: row 4h + l/16 of the tile, 8 elements at
   // 8*(l%16) of the K step (a wave pass covers 4 whole rows: coalesced).
@@ -201,7 +208,7 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
   const int chunk = (l & 15) >> 2, sub = l & 3;
   int wslot[PIECES];
 #pragma unroll
-  for (int h = 0; h < PIECES; ++h) wslot[h] = slot16(4 * h + (l >> 4), chunk);
+  for (int h = 0; h < PIECES; ++h) wslot[h] = slot16((4 * h + (l >> 4)) & 15, chunk);
   const int aslot = slot16(l & 15, l >> 4);
   // B operand of 16-column tile T at step j: lane l reads unit 2j + (l/16)/2 of
   // packed tile T/2 at unit lane ((l/16)%2)*32 + 16*(T%2) + l%16.
@@ -264,35 +271,42 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
           uint32_t sb;
           const uint32_t code = mx::quant8_quad(w[s][h], sb);
           if constexpr (DUMP) dump_piece(p, d.K, copy, m0 + 4 * h + (l >> 4), 128 * j + 8 * (l & 15), code, sb, sub == 0);
-          sAq[wave][wslot[h] * 4 + sub] = code;
-          sAs[wave][wslot[h]] = (uint8_t)sb;  // the quad's four lanes store the same byte
+          sAq[wave][h >> 2][wslot[h] * 4 + sub] = code;
+          sAs[wave][h >> 2][wslot[h]] = (uint8_t)sb;  // the quad's four lanes store the same byte
         }
         // LDS operations of one wave complete in order: the reads see the writes.
-        const uint4 a = *reinterpret_cast<const uint4*>(&sAq[wave][aslot * 4]);
-        const uint32_t sa = sAs[wave][aslot];
         const int bsh = 8 * ((2 * j + (l >> 5)) & 3);
 #pragma unroll
-        for (int t = 0; t < NB; ++t) acc[t] = mx::mfma_fp4(a, bq[s][t], acc[t], sa, bs[s][t] >> bsh);
+        for (int mt = 0; mt < MT; ++mt) {
+          const uint4 a = *reinterpret_cast<const uint4*>(&sAq[wave][mt][aslot * 4]);
+          const uint32_t sa = sAs[wave][mt][aslot];
+#pragma unroll
+          for (int t = 0; t < NB; ++t) acc[mt][t] = mx::mfma_fp4(a, bq[s][t], acc[mt][t], sa, bs[s][t] >> bsh);
+        }
       }
     }
   }
 
-  // Sum the waves' partial tiles in LDS and store bf16.
-#pragma unroll
-  for (int t = 0; t < NB; ++t)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) red[wave][t * 4 + e][l] = acc[t][e];
-  __syncthreads();
+  // Sum the waves' partial tiles in LDS and store bf16, one 16-row sub-tile at a time.
   constexpr int OUT = NB * 256;
-  for (int o = threadIdx.x; o < OUT; o += WAVES * 64) {
-    const int slot = o >> 6, ll = o & 63, t = slot >> 2, e = slot & 3;
-    const int r = 4 * (ll >> 4) + e;
-    if (r >= MS) continue;
-    float sum = 0.f;
 #pragma unroll
-    for (int w2 = 0; w2 < WAVES; ++w2) sum += red[w2][slot][ll];
-    const int row = m0 + r, col = (T0 + t) * 16 + (ll & 15);
-    if (row < p.M && col < d.N) p.C[(int64_t)row * p.ldc + col] = mx::f32_to_bf16(sum);
+  for (int mt = 0; mt < MT; ++mt) {
+    if (mt > 0) __syncthreads();  // every thread is done reading the previous sub-tile
+#pragma unroll
+    for (int t = 0; t < NB; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) red[wave][t * 4 + e][l] = acc[mt][t][e];
+    __syncthreads();
+    for (int o = threadIdx.x; o < OUT; o += WAVES * 64) {
+      const int slot = o >> 6, ll = o & 63, t = slot >> 2, e = slot & 3;
+      const int r = 16 * mt + 4 * (ll >> 4) + e;
+      if (r >= MS) continue;
+      float sum = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < WAVES; ++w2) sum += red[w2][slot][ll];
+      const int row = m0 + r, col = (T0 + t) * 16 + (ll & 15);
+      if (row < p.M && col < d.N) p.C[(int64_t)row * p.ldc + col] = mx::f32_to_bf16(sum);
+    }
   }
 }
 
@@ -1002,24 +1016,26 @@ __global__ __launch_bounds__(kTThreads) void gemm_tiled_kernel(Operand p, Dims d
 }
 
 // Grouped GEMM. A group of at most kGsMaxM rows is an HBM-bound problem (its B
-// is read once for very few rows): it takes small tiles of 16 rows x 128
-// columns over the whole K, the workgroup's 8 waves splitting K (the skinny
-// tile), so that its B spreads over many CUs; a 128 x 512 tile would give it one
+// is read once for very few rows): it takes small tiles of all its rows (16, 32
+// or 48, one to three 16-row sub-tiles) x 128 columns over the whole K, the
+// workgroup's 8 waves splitting K (the skinny tile), so that its B spreads over
+// many CUs and each B byte is loaded once; a 128 x 512 tile would give it one
 // CU per 512 columns and leave the matrix cores of that CU computing 128 rows
-// for 16 (at up to 48 rows the small tiles measured faster, at 64 slower).
+// for a few.
 // Larger groups take the 128 x 512 tiled tiles. The large tiles take the first
 // workgroup ids, so the hardware starts them first (they run longest), and the
 // small tiles fill the other CUs beside them and whatever frees up. Each range
 // is remapped for the XCDs on its own (the large range padded to a multiple of
 // 8 ids with idle workgroups), and a small group's row tiles of one column tile
 // are adjacent (they share that B in one XCD's L2).
-constexpr int kGsMaxM = 48, kGsMS = 16, kGsNB = 8, kGsPF = 2;
+constexpr int kGsMaxM = 48, kGsNB = 8;
 
 struct GroupedArgs {
   Operand g[MXFP4_MAX_GROUPS];
   int tile_start[MXFP4_MAX_GROUPS + 1];  // prefix sums of the entries' tile counts, in launch order
   int order[MXFP4_MAX_GROUPS];           // group of launch entry e: large groups, then small ones
-  int rows[MXFP4_MAX_GROUPS];            // row tiles of entry e (16-row tiles for a small group)
+  int rows[MXFP4_MAX_GROUPS];            // row tiles of entry e
+  int mt[MXFP4_MAX_GROUPS];              // 16-row sub-tiles of a small entry's tile
   int small_from;                        // first entry of a small group
   int nlarge, nlarge_pad;                // large tiles, and their id range rounded up to a multiple of 8
   int G;
@@ -1046,11 +1062,18 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, 
   // lives in the ring's bytes.
   __shared__ __align__(16) TiledSmem sm;
   __shared__ __align__(16) uint8_t ring[kRingBytes];
-  static_assert(sizeof(SkinnySmem<kTWaves, kGsNB>) <= sizeof(ring), "skinny tile LDS");
+  static_assert(sizeof(SkinnySmem<kTWaves, kGsNB, 3>) <= sizeof(ring), "skinny tile LDS");
   if (e >= a.small_from) {
     const int c = local / a.rows[e], r = local - c * a.rows[e];
-    skinny_tile<kTWaves, kGsMS, kGsNB, kGsPF, DUMP>(p, d, r * kGsMS, c * kGsNB, c,
-                                                     *reinterpret_cast<SkinnySmem<kTWaves, kGsNB>*>(ring));
+    if (a.mt[e] == 1)
+      skinny_tile<kTWaves, 16, kGsNB, 2, DUMP>(p, d, r * 16, c * kGsNB, c,
+                                               *reinterpret_cast<SkinnySmem<kTWaves, kGsNB, 1>*>(ring));
+    else if (a.mt[e] == 2)
+      skinny_tile<kTWaves, 32, kGsNB, 1, DUMP>(p, d, r * 32, c * kGsNB, c,
+                                               *reinterpret_cast<SkinnySmem<kTWaves, kGsNB, 2>*>(ring));
+    else
+      skinny_tile<kTWaves, 48, kGsNB, 1, DUMP>(p, d, r * 48, c * kGsNB, c,
+                                               *reinterpret_cast<SkinnySmem<kTWaves, kGsNB, 3>*>(ring));
   } else {
     tiled_tile<false, DUMP>(p, d, local / a.ntiles_n, local % a.ntiles_n, sm, ring);
   }
@@ -1342,16 +1365,23 @@ void* g_scratch_ptr[kMaxDevices];
 
 // Device address of `scratch` on the device that runs `stream` (the current
 // device for the null stream).
-int scratch_address(void* stream, void** out) {
-  int cur = 0;
-  if (hipGetDevice(&cur) != hipSuccess) return MXFP4_ERR_HIP;
-  int dev = cur;
+// The device a stream runs on (the current device for the null stream), and
+// the current device.
+int stream_device(void* stream, int* dev, int* cur) {
+  if (hipGetDevice(cur) != hipSuccess) return MXFP4_ERR_HIP;
+  *dev = *cur;
   if (stream) {
     hipDevice_t d = 0;
     if (hipStreamGetDevice((hipStream_t)stream, &d) != hipSuccess) return MXFP4_ERR_HIP;
-    dev = (int)d;
+    *dev = (int)d;
   }
-  if (dev < 0 || dev >= kMaxDevices) return MXFP4_ERR_HIP;
+  return *dev >= 0 && *dev < kMaxDevices ? MXFP4_OK : MXFP4_ERR_HIP;
+}
+
+int scratch_address(void* stream, void** out) {
+  int cur = 0, dev = 0;
+  const int st = stream_device(stream, &dev, &cur);
+  if (st != MXFP4_OK) return st;
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
     if (dev != cur && hipSetDevice(dev) != hipSuccess) return MXFP4_ERR_HIP;
@@ -1362,6 +1392,22 @@ int scratch_address(void* stream, void** out) {
     g_scratch_ptr[dev] = p;
   }
   *out = g_scratch_ptr[dev];
+  return MXFP4_OK;
+}
+
+// Compute units of the stream's device, read once per device.
+std::atomic<int> g_cus[kMaxDevices];
+int device_cus(void* stream, int* cus) {
+  int cur = 0, dev = 0;
+  const int st = stream_device(stream, &dev, &cur);
+  if (st != MXFP4_OK) return st;
+  int n = g_cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return MXFP4_ERR_HIP;
+    g_cus[dev].store(n, std::memory_order_relaxed);
+  }
+  *cus = n;
   return MXFP4_OK;
 }
 }  // namespace
@@ -1450,6 +1496,24 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
     if (st != MXFP4_OK) return st;
     a.g[g] = make_operand(q.A, q.lda, q.Bp, q.C, q.ldc, q.M, N, K);
   }
+  // A small group takes one tile of all its rows per 128 columns (each B byte
+  // loaded once), or 16-row tiles when the whole launch then still fits one
+  // round of workgroups on the device's CUs (more CUs streaming its B).
+  int64_t large_tiles = 0, small16 = 0;
+  for (int g = 0; g < G; ++g) {
+    const int64_t M = groups[g].M;
+    if (M <= kGsMaxM)
+      small16 += mxh::cdiv(M, 16) * mxh::cdiv(N, 16 * kGsNB);
+    else
+      large_tiles += mxh::cdiv(M, kTBM) * ntn;
+  }
+  bool rows16 = false;
+  if (small16 > 0) {
+    int cus = 0;
+    const int st = device_cus(stream, &cus);
+    if (st != MXFP4_OK) return st;
+    rows16 = large_tiles + small16 <= cus;
+  }
   // Launch entries: the large groups in their order, then the small ones.
   int64_t total = 0;
   int e = 0;
@@ -1462,9 +1526,11 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
     for (int g = 0; g < G; ++g) {
       const int64_t M = groups[g].M;
       if ((M <= kGsMaxM) != (small != 0)) continue;
-      const int64_t rows = small ? mxh::cdiv(M, kGsMS) : mxh::cdiv(M, kTBM);
+      const int64_t mt = rows16 ? 1 : mxh::cdiv(M, 16);  // 16-row sub-tiles of a small tile
+      const int64_t rows = small ? mxh::cdiv(M, 16 * mt) : mxh::cdiv(M, kTBM);
       a.order[e] = g;
       a.rows[e] = (int)rows;
+      a.mt[e] = small ? (int)mt : 0;
       a.tile_start[e] = (int)total;
       total += rows * (small ? mxh::cdiv(N, 16 * kGsNB) : ntn);
       if (total > INT32_MAX) return MXFP4_ERR_SHAPE;

@@ -107,6 +107,18 @@ def test_fused_quant_bytes_grouped_small_and_large():
     run_grouped(a_list, b_list, N, "mixed groups")
 
 
+def test_fused_quant_bytes_grouped_small_subtiles():
+    """Small groups in tiles of all their rows (more 16-row tiles than one round of workgroups), ragged."""
+    g = np.random.default_rng(22)
+    N, K = 8200, 832
+    Ms = [17, 33, 48, 5]
+    a_list = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
+    for a in a_list:
+        a[-1, :32] = 0
+    b_list = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
+    run_grouped(a_list, b_list, N, "small sub-tiles")
+
+
 @pytest.mark.timeout(600)
 def test_fused_quant_bytes_grouped_decode():
     w = synth.workload("grouped_decode", synth.default_seed("grouped_decode"))

@@ -361,6 +361,23 @@ def test_grouped_small_groups_mixed():
         assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
 
 
+def test_grouped_small_subtiles_ragged():
+    """Small groups whose 16-row tiles would not fit one round of workgroups take one tile of all their
+    rows (one to three 16-row sub-tiles sharing each B load): M 5, 17, 33, 48, N with a tail of 8 columns
+    past the last 128, K with a tail on odd K/64."""
+    say("grouped small groups, multi-row tiles")
+    g = np.random.default_rng(13)
+    N, K = 8200, 832
+    Ms = [17, 33, 48, 5]
+    a = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
+    b = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
+    qs = [oracle.quant_mx(x) for x in b]
+    cs = ops.grouped_gemm([to_dev_bf16(x) for x in a], [packed_b(*q) for q in qs], N)
+    torch.cuda.synchronize()
+    for x, (bq, bs), c in zip(a, qs, cs):
+        assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
+
+
 @pytest.mark.timeout(600)
 def test_grouped_decode_workload():
     """The decode-sized grouped workload (8 groups of 8..64 rows, N4096 K7168), every row."""
