@@ -140,11 +140,13 @@ int mxfp4_pack_B(const void* bq, const void* bs, int64_t N, int64_t K, void* out
  *        bytes (may be NULL when that size is 0), 256-byte aligned, ZEROED BY
  *        THE CALLER ONCE after allocation; every call leaves it zeroed again.
  *        Calls that may run concurrently need distinct workspaces. It is used
- *        for M <= 16, where K is split over workgroups (page 683203, direct
+ *        for M <= 16 when K is split over workgroups (page 683203, direct
  *        GEMM call: its split-K argument) and each tile's last split sums the
- *        others' fp32 partials, which pass through the workspace; larger M
- *        needs none. Too small or NULL when needed: MXFP4_ERR_WORKSPACE; not
- *        256-byte aligned: MXFP4_ERR_ALIGN.
+ *        others' fp32 partials, which pass through the workspace. For M <= 16
+ *        with wide N the call may instead split K over the waves of one
+ *        workgroup (faster there, no workspace used); the size above is
+ *        always enough. Larger M needs none. Too small or NULL when needed:
+ *        MXFP4_ERR_WORKSPACE; not 256-byte aligned: MXFP4_ERR_ALIGN.
  * ------------------------------------------------------------------------- */
 size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M,
@@ -157,9 +159,10 @@ int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t
  * hipMalloc). Same kernels, tiling and arithmetic, so C equals
  * gemm_a4w4_fused's bit for bit. The split-K partials (M <= 16) go to a fixed
  * device array of MXFP4_NOALLOC_SCRATCH_BYTES bytes inside the library, one
- * per GPU, held until the process ends; a call whose split-K geometry needs
- * more (gemm_a4w4_workspace_bytes(M, N, K) > MXFP4_NOALLOC_SCRATCH_BYTES, e.g.
- * very large N*K at M <= 16) returns MXFP4_ERR_WORKSPACE and launches nothing.
+ * per GPU, held until the process ends; a call that would run the split-K
+ * kernel with more partials than that (gemm_a4w4_workspace_bytes(M, N, K) >
+ * MXFP4_NOALLOC_SCRATCH_BYTES, e.g. M16 N1088 K65536) returns
+ * MXFP4_ERR_WORKSPACE and launches nothing.
  * Every call on one GPU shares that GPU's array: calls that may overlap on one
  * GPU (different streams, or concurrent host threads) race and must not be
  * issued; use gemm_a4w4_fused with distinct workspaces for those. The first

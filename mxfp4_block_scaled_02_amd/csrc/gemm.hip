@@ -1214,6 +1214,7 @@ SkinnyShape choose_skinny(int64_t M, int64_t N, int64_t K) {
 struct SplitGeom {
   int MT = 0, T = 0, S = 0;
   size_t part_bytes = 0;
+  double t_us = 0.0;  // the model's time for the chosen S
   bool ok = false;
   size_t total() const { return part_bytes; }
 };
@@ -1246,8 +1247,29 @@ SplitGeom split_geom(int64_t M, int64_t N, int64_t K) {
   g.T = (int)T;
   g.S = (int)S;
   g.part_bytes = (size_t)T * (size_t)(S - 1) * kSpW * g.MT * 64 * 16;
+  g.t_us = best;
   g.ok = true;
   return g;
+}
+
+// Kernel of a fused call with M <= 16: the split-K kernel, unless its best
+// split needs a hand-off (S > 1) and the skinny kernel (no hand-off: one
+// workgroup's waves split K) is estimated at least 20 % faster (the two
+// models are rough; near a tie the split-K kernel measured faster). The skinny estimate counts
+// rounds of 256 workgroups, each a latency plus its bf16 A rows at the rate a
+// CU reaches when every workgroup reads the same A from L2 (~60 GB/s) plus its
+// packed B at one CU's HBM streaming rate (~25 GB/s). Wide N favours it
+// (measured, split-K against skinny: M1 N4096 K7168 8.3 / 6.3 us, M16 N7168
+// K2048 6.5 / 5.5 us), long K over few columns favours split-K (M16 N2112
+// K7168 6.7 / 9.3 us, M16 N264 K7168 6.2 / 6.6 us).
+bool fused_splitk(int64_t M, int64_t N, int64_t K, const SplitGeom& g) {
+  if (!g.ok) return false;
+  if (g.S == 1) return true;
+  const SkinnyShape sh = choose_skinny(M, N, K);
+  const int64_t wgs = mxh::cdiv(mxh::cdiv(N, 16), sh.NB) * mxh::cdiv(M, sh.MS);
+  const double a_bytes = (double)sh.MS * (double)K * 2.0, b_bytes = (double)sh.NB * 16.0 * (double)K * 17.0 / 32.0;
+  const double t = (double)mxh::cdiv(wgs, 256) * (1.0 + a_bytes / 60e3 + b_bytes / 25e3);
+  return t >= 0.8 * g.t_us;
 }
 
 hipError_t launch_splitk(const Operand& o, const Dims& d, const SplitGeom& g, void* ws, bool preq, bool dump,
@@ -1299,7 +1321,7 @@ hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, in
 // the kernel it runs): the leading dimension of the verification dump.
 int64_t dump_copies(int64_t M, int64_t N, int64_t K) {
   const SplitGeom g = split_geom(M, N, K);
-  if (g.ok) return g.T;
+  if (fused_splitk(M, N, K, g)) return g.T;
   if (M <= 64) return mxh::cdiv(mxh::cdiv(N, 16), choose_skinny(M, N, K).NB);
   return mxh::cdiv(N, kTBN);
 }
@@ -1312,6 +1334,8 @@ size_t dump_bytes_of(int64_t M, int64_t N, int64_t K) {
 extern "C" size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || M > mxh::kMaxDim || N > mxh::kMaxDim || K > mxh::kMaxDim) return 0;
   const SplitGeom g = split_geom(M, N, K);
+  // The split-K partials (gemm_a4w4 always runs that kernel for M <= 16; the
+  // fused call may run the skinny kernel instead and then uses none of it).
   return g.ok ? g.total() : 0;  // larger M: every output tile is reduced inside one workgroup
 }
 
@@ -1330,7 +1354,7 @@ int fused_call(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc,
   }
   const Dims d = make_dims(N, K);
   const SplitGeom g = split_geom(M, N, K);
-  if (g.ok) {
+  if (fused_splitk(M, N, K, g)) {
     if (g.total() > 0) {
       if (!workspace || workspace_bytes < g.total()) return MXFP4_ERR_WORKSPACE;
       if (!mxh::aligned(workspace, 256)) return MXFP4_ERR_ALIGN;
@@ -1419,7 +1443,7 @@ extern "C" int gemm_a4w4_fused_noalloc(const void* A, int64_t lda, const void* B
   const SplitGeom g = split_geom(M, N, K);
   void* ws = nullptr;
   size_t ws_bytes = 0;
-  if (g.ok && g.total() > 0) {
+  if (fused_splitk(M, N, K, g) && g.total() > 0) {
     if (g.total() > (size_t)MXFP4_NOALLOC_SCRATCH_BYTES) return MXFP4_ERR_WORKSPACE;  // beyond the fixed scratch
     const int s2 = scratch_address(stream, &ws);
     if (s2 != MXFP4_OK) return s2;

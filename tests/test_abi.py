@@ -148,8 +148,8 @@ def test_gemm_validation(change, status):
     (dict(A=None), 1), (dict(Bp=None), 1), (dict(C=None), 1),
     (dict(M=0), 2), (dict(K=7000), 2), (dict(lda=7000), 2), (dict(lda=1 << 23), 2),
     (dict(A=P + 2), 3), (dict(C=P + 1), 3),
-    # split-K needs 256 tiles x 63 splits x 4 KB of partials, more than the fixed scratch holds
-    (dict(M=16, N=16384, K=65536, lda=65536, ldc=16384), 4),
+    # split-K needs 17 tiles x 63 splits x 4 KB of partials, more than the fixed scratch holds
+    (dict(M=16, N=1088, K=65536, lda=65536, ldc=1088), 4),
 ])
 def test_gemm_noalloc_validation(change, status):
     a = dict(OK_G, **change)
@@ -162,7 +162,7 @@ def test_noalloc_scratch_limit_matches_header():
     m = re.search(r"#define MXFP4_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
     limit = int(m.group(1)) << int(m.group(2))
     L = ops.lib()
-    assert L.gemm_a4w4_workspace_bytes(16, 16384, 65536) > limit
+    assert L.gemm_a4w4_workspace_bytes(16, 1088, 65536) > limit
     assert 0 < L.gemm_a4w4_workspace_bytes(16, 2112, 7168) <= limit
 
 
@@ -199,6 +199,23 @@ def test_grouped_validation():
     assert L.grouped_gemm_a4w4(g, 2, 4096, 7168, None, 0, None) == 3
     g[1] = ops.Group(P, 1 << 23, P, P, 4096, 64)  # a 128-row window of A past 2^31 bytes
     assert L.grouped_gemm_a4w4(g, 2, 4096, 7168, None, 0, None) == 2
+
+
+def test_small_m_kernel_choice():
+    """For M <= 16 the fused call runs the split-K kernel (dump copies = its 64-column tiles) unless the split
+    needs a hand-off and the skinny kernel (16-column tiles, K split over one workgroup's waves) is estimated
+    faster: wide N. The verification dump's size shows which one a shape takes."""
+    L = ops.lib()
+    row = lambda K: K // 2 + K // 32
+    splitk = [(16, 2112, 7168), (16, 264, 7168), (4, 256, 512), (1, 16, 128), (16, 130, 7232), (16, 1088, 65536),
+              (16, 4096, 7168)]
+    for M, N, K in splitk:
+        assert L.gemm_a4w4_fused_dump_bytes(M, N, K) == cdiv(cdiv(N, 16), 4) * M * row(K), (M, N, K)
+    skinny = [(1, 4096, 7168, 1), (8, 4096, 7168, 2), (16, 7168, 2048, 4), (2, 4096, 4096, 1)]  # (.., NB)
+    for M, N, K, nb in skinny:
+        assert L.gemm_a4w4_fused_dump_bytes(M, N, K) == cdiv(cdiv(N, 16), nb) * M * row(K), (M, N, K)
+    # gemm_a4w4 always runs split-K at M <= 16: its workspace size is that kernel's
+    assert L.gemm_a4w4_workspace_bytes(1, 4096, 7168) > 0
 
 
 def test_grouped_dump_layout():

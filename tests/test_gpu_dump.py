@@ -129,7 +129,7 @@ def test_fused_quant_bytes_grouped_decode():
 # tail on odd K/64; the tiled kernel with M, N and K tails; the stress recipe
 # (outliers, all-zero blocks) on the tiled kernel; -0.0 blocks and bf16 extremes.
 EDGE = [(3, 70, 352), (16, 130, 7232), (50, 20000, 1056), (33, 64, 352), (127, 257, 1056), (65, 130, 288),
-        (300, 600, 4096)]
+        (300, 600, 4096), (2, 4096, 4096)]
 
 
 @pytest.mark.parametrize("M,N,K", EDGE)

@@ -209,10 +209,12 @@ def test_grouped_workload_sampled_rows():
 EDGE = [(1, 1, 32), (1, 16, 128), (2, 100, 96), (4, 256, 512), (16, 2112, 7168), (17, 50, 160), (33, 64, 352),
         (64, 130, 2048), (65, 130, 288), (127, 257, 1056), (255, 300, 4096), (1, 4096, 7168), (300, 33, 32),
         # split-K path (M <= 16): K tail with M < 16; odd K/64 with a K tail (9 splits of 6-7 steps);
-        # odd K/64 with one K step per split (9 splits); the 64-split maximum; more K than 64 splits
-        # can hold (falls back); a middle case; the 8-way N shard of skinny
-        (3, 70, 352), (16, 130, 7232), (16, 130, 1088), (16, 64, 65536), (16, 48, 66560), (8, 1000, 6144),
-        (16, 264, 7168),
+        # the 64-split maximum; more K than 64 splits can hold (falls back to the skinny kernel); a
+        # middle case; the 8-way N shard of skinny
+        (3, 70, 352), (16, 130, 7232), (16, 64, 65536), (16, 48, 66560), (8, 1000, 6144), (16, 264, 7168),
+        # M <= 16 where the skinny kernel (K split over one workgroup's waves, no hand-off) is estimated
+        # faster than split-K: wide N, or a short K that split-K would cut into one-step splits
+        (8, 4096, 7168), (16, 7168, 2048), (2, 4096, 4096), (16, 130, 1088), (5, 300, 1024),
         # 16 < M <= 64 on 128-column workgroups: an M tail, a ragged N, odd K/64 with a K tail
         (50, 20000, 1056)]
 
@@ -275,10 +277,19 @@ def test_gemm_repeat_identical_and_workspace_left_zero(M, N, K):
 
 
 # gemm_a4w4: the unfused comparator (A quantised by mxfp4_quant, then the GEMM on A_q).
-# Where it runs the same kernel and tiling as the fused call (M <= 16: split-K;
-# M > 64: tiled) its C must be bit-identical; elsewhere within the oracle's tolerance.
-A4W4_SHAPES = [(1, 16, 128), (4, 256, 512), (16, 2112, 7168), (3, 70, 352), (16, 130, 7232), (33, 64, 352),
-               (64, 130, 2048), (65, 130, 288), (127, 257, 1056), (300, 33, 32), (256, 512, 4096)]
+# Where it runs the same kernel and tiling as the fused call (the split-K kernel,
+# which these M <= 16 shapes take in both calls; M > 64: tiled) its C must be
+# bit-identical; elsewhere within the oracle's tolerance.
+A4W4_SHAPES = [(1, 16, 128), (4, 256, 512), (16, 2112, 7168), (3, 70, 352), (16, 130, 7232), (16, 130, 1088),
+               (33, 64, 352), (64, 130, 2048), (65, 130, 288), (127, 257, 1056), (300, 33, 32), (256, 512, 4096)]
+
+
+def splitk_in_fused(M, N, K):
+    """Whether the fused call runs the split-K kernel (as gemm_a4w4 does for M <= 16): its dump then holds one
+    copy per 64-column tile."""
+    if M > 16:
+        return False
+    return ops.lib().gemm_a4w4_fused_dump_bytes(M, N, K) == -(-(-(-N // 16)) // 4) * M * (K // 2 + K // 32)
 
 
 @pytest.mark.parametrize("M,N,K", A4W4_SHAPES)
@@ -292,7 +303,7 @@ def test_gemm_a4w4_matches_fused_and_oracle(M, N, K):
     aq, asc = ops.quant(at)
     c4 = bits_of(ops.gemm_a4w4(aq, asc, bp, N))
     cf = bits_of(ops.gemm(at, bp, N))
-    if M <= 16 or M > 64:
+    if splitk_in_fused(M, N, K) or M > 64:
         assert np.array_equal(c4, cf)
     assert_in_tolerance(c4, oracle.gemm_ref(a, bq, bs), f"a4w4 M={M} N={N} K={K}")
 
