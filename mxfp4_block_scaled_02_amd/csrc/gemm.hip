@@ -1084,7 +1084,10 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, 
 // ---------------------------------------------------------------------------
 // Per-problem list of grouped_gemm_a4w4_mnk: every group contributes L
 // problems with their own (M, N, K); tile_start holds the prefix sums of the
-// problems' output tiles (128 x 512 each).
+// problems' output tiles. As in the grouped kernel, a problem of at most
+// kGsMaxM rows takes skinny tiles of mt 16-row sub-tiles x 128 columns (rows
+// tiles per column), a larger one 128 x 512 tiled tiles; the large problems come
+// first and take the first workgroup ids.
 struct MnkProblem {
   const uint16_t* A;
   int64_t lda;
@@ -1092,16 +1095,26 @@ struct MnkProblem {
   const uint32_t* Bscale;
   uint16_t* C;
   int64_t ldc;
-  int M, N, K, pad_;
+  int M, N, K;
+  int mt;    // 0: tiled tiles; 1..3: skinny tiles of mt 16-row sub-tiles
+  int rows;  // skinny row tiles per column tile
 };
 struct MnkArgs {
   MnkProblem p[MXFP4_MAX_GROUPS];
   int tile_start[MXFP4_MAX_GROUPS + 1];
   int P;
+  int nlarge, nlarge_pad;  // large-problem tiles, and their id range rounded up to a multiple of 8
 };
 
 __global__ __launch_bounds__(kTThreads) void gemm_grouped_mnk_kernel(MnkArgs a) {
-  const int v = xcd_remap(blockIdx.x, gridDim.x);
+  const int b = blockIdx.x;
+  int v;
+  if (b < a.nlarge_pad) {
+    if (b >= a.nlarge) return;  // padding: the whole workgroup leaves
+    v = xcd_remap(b, a.nlarge);
+  } else {
+    v = a.nlarge + xcd_remap(b - a.nlarge_pad, (int)gridDim.x - a.nlarge_pad);
+  }
   int g = 0;
   while (g + 1 < a.P && a.tile_start[g + 1] <= v) ++g;
   const int local = v - a.tile_start[g];
@@ -1116,10 +1129,23 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_mnk_kernel(MnkArgs a) 
   o.M = q.M;
   const int ku = (q.K + 63) / 64;
   const Dims d{q.N, q.K, (q.K + 127) / 128, ku, (q.N + 31) / 32, (ku + 3) / 4};
-  const int ntn = (q.N + kTBN - 1) / kTBN;
   __shared__ __align__(16) TiledSmem sm;
   __shared__ __align__(16) uint8_t ring[kRingBytes];
-  tiled_tile<false>(o, d, local / ntn, local % ntn, sm, ring);
+  if (q.mt > 0) {
+    const int c = local / q.rows, r = local - c * q.rows;
+    if (q.mt == 1)
+      skinny_tile<kTWaves, 16, kGsNB, 2, false>(o, d, r * 16, c * kGsNB, c,
+                                                *reinterpret_cast<SkinnySmem<kTWaves, kGsNB, 1>*>(ring));
+    else if (q.mt == 2)
+      skinny_tile<kTWaves, 32, kGsNB, 1, false>(o, d, r * 32, c * kGsNB, c,
+                                                *reinterpret_cast<SkinnySmem<kTWaves, kGsNB, 2>*>(ring));
+    else
+      skinny_tile<kTWaves, 48, kGsNB, 1, false>(o, d, r * 48, c * kGsNB, c,
+                                                *reinterpret_cast<SkinnySmem<kTWaves, kGsNB, 3>*>(ring));
+  } else {
+    const int ntn = (q.N + kTBN - 1) / kTBN;
+    tiled_tile<false>(o, d, local / ntn, local % ntn, sm, ring);
+  }
 }
 
 Dims make_dims(int64_t N, int64_t K) {
@@ -1617,11 +1643,12 @@ extern "C" int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void*
   if (G < 1) return MXFP4_ERR_TOO_MANY_GROUPS;
   MnkArgs a{};
   int P = 0;
-  int64_t total = 0;
+  int64_t large_tiles = 0, small16 = 0;
   for (int g = 0; g < G; ++g) {
     const mxfp4_group_mnk& q = groups[g];
     if (q.L < 1) return MXFP4_ERR_SHAPE;
     if (q.L > MXFP4_MAX_GROUPS - P) return MXFP4_ERR_TOO_MANY_GROUPS;
+    P += (int)q.L;
     const int st = check_problem(q.A, q.lda, q.Bp, q.C, q.ldc, q.M, q.N, q.K);
     if (st != MXFP4_OK) return st;
     const mxh::PackedGeom pg(q.N, q.K);
@@ -1629,27 +1656,60 @@ extern "C" int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void*
       if (q.strideA < 0 || q.strideB < (int64_t)pg.total() || q.strideC < q.M * q.ldc) return MXFP4_ERR_SHAPE;
       if ((q.strideA * 2) % 16 != 0 || q.strideB % 16 != 0) return MXFP4_ERR_ALIGN;
     }
-    const int64_t tiles = mxh::cdiv(q.M, kTBM) * mxh::cdiv(q.N, kTBN);
-    for (int64_t l = 0; l < q.L; ++l) {
-      MnkProblem& o = a.p[P];
-      o.A = (const uint16_t*)q.A + l * q.strideA;
-      o.lda = q.lda;
-      o.Bunit = (const uint8_t*)q.Bp + l * q.strideB;
-      o.Bscale = (const uint32_t*)(o.Bunit + pg.code_bytes);
-      o.C = (uint16_t*)q.C + l * q.strideC;
-      o.ldc = q.ldc;
-      o.M = (int)q.M;
-      o.N = (int)q.N;
-      o.K = (int)q.K;
-      a.tile_start[P] = (int)total;
-      total += tiles;
-      if (total > INT32_MAX) return MXFP4_ERR_SHAPE;
-      ++P;
+    if (q.M <= kGsMaxM)
+      small16 += q.L * mxh::cdiv(q.M, 16) * mxh::cdiv(q.N, 16 * kGsNB);
+    else
+      large_tiles += q.L * mxh::cdiv(q.M, kTBM) * mxh::cdiv(q.N, kTBN);
+  }
+  // Small problems: 16-row tiles when the launch then fits one round of
+  // workgroups on the device's CUs, else one tile of all rows per 128 columns.
+  bool rows16 = false;
+  if (small16 > 0) {
+    int cus = 0;
+    const int st = device_cus(stream, &cus);
+    if (st != MXFP4_OK) return st;
+    rows16 = large_tiles + small16 <= cus;
+  }
+  P = 0;
+  int64_t total = 0;
+  for (int small = 0; small < 2; ++small) {
+    if (small) {
+      a.nlarge = (int)total;
+      a.nlarge_pad = (int)mxh::cdiv(total, 8) * 8;
+    }
+    for (int g = 0; g < G; ++g) {
+      const mxfp4_group_mnk& q = groups[g];
+      if ((q.M <= kGsMaxM) != (small != 0)) continue;
+      const mxh::PackedGeom pg(q.N, q.K);
+      const int64_t mt = small ? (rows16 ? 1 : mxh::cdiv(q.M, 16)) : 0;
+      const int64_t rows = small ? mxh::cdiv(q.M, 16 * mt) : 0;
+      const int64_t tiles =
+          small ? rows * mxh::cdiv(q.N, 16 * kGsNB) : mxh::cdiv(q.M, kTBM) * mxh::cdiv(q.N, kTBN);
+      for (int64_t l = 0; l < q.L; ++l) {
+        MnkProblem& o = a.p[P];
+        o.A = (const uint16_t*)q.A + l * q.strideA;
+        o.lda = q.lda;
+        o.Bunit = (const uint8_t*)q.Bp + l * q.strideB;
+        o.Bscale = (const uint32_t*)(o.Bunit + pg.code_bytes);
+        o.C = (uint16_t*)q.C + l * q.strideC;
+        o.ldc = q.ldc;
+        o.M = (int)q.M;
+        o.N = (int)q.N;
+        o.K = (int)q.K;
+        o.mt = (int)mt;
+        o.rows = (int)rows;
+        a.tile_start[P] = (int)total;
+        total += tiles;
+        if (total > INT32_MAX) return MXFP4_ERR_SHAPE;
+        ++P;
+      }
     }
   }
   a.tile_start[P] = (int)total;
   a.P = P;
+  const int64_t grid = total + (a.nlarge_pad - a.nlarge);
+  if (grid > INT32_MAX) return MXFP4_ERR_SHAPE;
   void* args[] = {&a};
-  return mxh::launch_status(hipLaunchKernel((const void*)gemm_grouped_mnk_kernel, dim3((unsigned)total),
+  return mxh::launch_status(hipLaunchKernel((const void*)gemm_grouped_mnk_kernel, dim3((unsigned)grid),
                                             dim3(kTThreads), args, 0, (hipStream_t)stream));
 }

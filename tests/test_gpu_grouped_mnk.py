@@ -4,7 +4,8 @@ count L, one launch; page 496271's problem form) with the CPU oracle, on an MI35
 Each batch's C must be within |C - C_ref| <= 2^-7 |C_ref| + 1e-3 max|C_ref| of
 the oracle's fp64 product of the dequantised operands rounded to bf16. Problems
 with M > 64 run the same tiled kernel as gemm_a4w4_fused, so there the bytes
-must also equal the single-problem call's.
+must also equal the single-problem call's. Problems of at most 48 rows take
+skinny tiles (K split over a workgroup's waves) in the same launch.
 """
 import numpy as np
 import pytest
@@ -40,6 +41,20 @@ def test_mixed_groups_match_oracle():
     outs = ops.grouped_gemm_mnk([(A, Bp, N) for (_, _, A, Bp), (M, N, K, L) in zip(groups, SHAPES)])
     torch.cuda.synchronize()
     for (a_bits, bq, _, _), (M, N, K, L), C in zip(groups, SHAPES, outs):
+        for l in range(L):
+            assert_in_tolerance(bits_of(C[l]), oracle.gemm_ref(a_bits[l], *bq[l]), f"group M{M} N{N} K{K} l{l}")
+
+
+def test_small_problems_beside_large_ones():
+    """Problems of at most 48 rows take skinny tiles (here one tile of all their rows per 128 columns: their
+    16-row tiles would not fit one round of workgroups) beside a large problem's tiled tiles: ragged N, a K
+    tail on odd K/64, batches."""
+    shapes = [(40, 4100, 1088, 3), (17, 2000, 832, 2), (300, 700, 1024, 1), (5, 4096, 512, 2), (48, 1000, 2048, 1)]
+    say(f"[mnk] small and large {shapes}")
+    groups = [make_group(gi, M, N, K, L, 35) for gi, (M, N, K, L) in enumerate(shapes)]
+    outs = ops.grouped_gemm_mnk([(A, Bp, N) for (_, _, A, Bp), (M, N, K, L) in zip(groups, shapes)])
+    torch.cuda.synchronize()
+    for (a_bits, bq, _, _), (M, N, K, L), C in zip(groups, shapes, outs):
         for l in range(L):
             assert_in_tolerance(bits_of(C[l]), oracle.gemm_ref(a_bits[l], *bq[l]), f"group M{M} N{N} K{K} l{l}")
 
