@@ -76,6 +76,9 @@ def parse():
                         "as extra keys of the same line). rmsnorm times mxfp4_rmsnorm_quant at M4096 K7168; "
                         "grouped_mnk times grouped_gemm_a4w4_mnk on seeded groups with their own (M, N, K, L)")
     p.add_argument("--seed", type=int, default=None)
+    p.add_argument("--sustained-steps", type=int, default=200,
+                   help="default run: also time the headline over one replay of this many calls (the sustained "
+                        "rate, after the power manager has settled; 0 skips it)")
     p.add_argument("--warm-cache", action="store_true", help="reuse one operand set (Infinity Cache resident)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="time an eager launch loop instead of a graph replay")
@@ -84,9 +87,10 @@ def parse():
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain device copies of a known size (counter calibration)")
     p.add_argument("--summarize-stats", metavar="DIR", help="print a summary of rocprofv3 --kernel-trace CSV output")
-    p.add_argument("--last", type=int, default=None, metavar="K",
-                   help="with --summarize-stats: only the last K dispatches of each kernel and grid (a bench "
-                        "run's timed replay is the last --steps dispatches of its workload's kernel)")
+    p.add_argument("--select", default=None, metavar="A:B",
+                   help="with --summarize-stats: only dispatches A..B-1 (in start order) of each kernel and grid; "
+                        "a default bench run gives each workload's kernel W warm-up calls, the untimed replay of "
+                        "K calls and the timed replay of K calls, so its timed calls are W+K:W+2K")
     p.add_argument("--summarize-pmc", nargs=3, metavar=("WORKLOAD_DIR", "COPY_DIR", "KERNEL"),
                    help="turn FETCH_SIZE/WRITE_SIZE runs into the traffic record for KERNEL")
     p.add_argument("--summarize-counters", nargs=2, metavar=("DIR", "KERNEL"),
@@ -134,11 +138,11 @@ def _csv_rows(directory, suffix):
     return rows
 
 
-def summarize_stats(directory, last=None):
+def summarize_stats(directory, select=None):
     """Per-kernel table from a rocprofv3 --kernel-trace run: one row per kernel and grid size (the split-K
     kernel serves tiny and skinny with one instance), with the calls, the mean, the 10th / 50th / 90th
     percentile, min and max of the per-dispatch durations, and the share of the total kernel time. With
-    `last`, only the last `last` dispatches (by start time) of each kernel and grid count."""
+    `select` ("A:B"), only dispatches A..B-1 (by start time) of each kernel and grid count."""
     durs = {}
     rows = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
     for r in rows:
@@ -147,8 +151,9 @@ def summarize_stats(directory, last=None):
             wgs *= max(1, int(r[f"Grid_Size_{ax}"]) // max(1, int(r[f"Workgroup_Size_{ax}"])))
         durs.setdefault((r["Kernel_Name"], wgs), []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    if last:
-        durs = {k: d[-last:] for k, d in durs.items()}
+    if select:
+        a, b = (int(x) if x else None for x in select.split(":"))
+        durs = {k: d[a:b] for k, d in durs.items() if d[a:b]}
     total = sum(sum(d) for d in durs.values()) or 1.0
     print("| kernel | workgroups | calls | avg µs | p10 µs | median µs | p90 µs | min µs | max µs | share % |")
     print("|---|---|---|---|---|---|---|---|---|---|")
@@ -559,7 +564,7 @@ def copy_calibration():
 def main():
     args = parse()
     if args.summarize_stats:
-        summarize_stats(args.summarize_stats, args.last)
+        summarize_stats(args.summarize_stats, args.select)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
@@ -593,7 +598,7 @@ def main():
         return
     # Default: the headline (the largest configuration the metric spans) and the other configurations as
     # extra keys of the same line, each timed the same way.
-    out, w, unit = bench_gemm(HEADLINE, args)
+    out, w, unit = bench_gemm(HEADLINE, args, sustained_steps=0 if args.no_graph else args.sustained_steps)
     del w
     extras = {}
     for name in EXTRAS:
@@ -614,8 +619,10 @@ def synth_workload(name, args):
     return synth.workload(name, synth.default_seed(name) if args.seed is None else args.seed)
 
 
-def bench_gemm(name, args):
+def bench_gemm(name, args, sustained_steps=0):
     """One fused call (or, with --unfused, mxfp4_quant + gemm_a4w4) per step over rotated operand sets.
+    With sustained_steps, the same calls are timed again over one replay of that many steps (a
+    longer run, in which the shader clock settles lower under full load) and reported apart.
     Returns (the JSON record, the workload's inputs, the roofline unit)."""
     import torch
     from mxfp4_block_scaled_02_amd import ops, synth
@@ -675,6 +682,12 @@ def bench_gemm(name, args):
             ops.gemm(a, b, N, out=c)
 
     ms_step = timed_steps(step, args)
+    ms_sustained = None
+    if sustained_steps > 0:
+        import copy
+        a2 = copy.copy(args)
+        a2.steps, a2.warmup = sustained_steps, 0
+        ms_sustained = timed_steps(step, a2)
     us = ms_step * 1e3
     gbs = total_bytes / (ms_step * 1e-3) / 1e9
     tflops = total_flops / (ms_step * 1e-3) / 1e12
@@ -700,6 +713,10 @@ def bench_gemm(name, args):
                ms_per_step=round(ms_step, 6), higher_is_better=True, scaling="weak", vs_baseline=None,
                dtype="mxfp4 (e2m1 x e8m0, fp32 accumulate, bf16 out)", data="synthetic", config=cfg,
                us_per_call=round(us, 3), tflops=round(tflops, 3), hbm_gbs=round(gbs, 2), roofline=roof)
+    if ms_sustained is not None:
+        rate = (total_flops / 1e12 if unit == "TFLOP/s" else total_bytes / 1e9) / (ms_sustained * 1e-3)
+        out["sustained"] = dict(steps=sustained_steps, us_per_call=round(ms_sustained * 1e3, 3),
+                                value=round(rate, 3), unit=unit, frac=round(rate / peak, 4))
     del sets, a0, b0
     torch.cuda.empty_cache()
     return out, w, unit
