@@ -19,20 +19,24 @@
 //    runs the 16x16x128 instruction; the splits of a tile hand their fp32
 //    partials to the tile's last split (the owner) through the workspace,
 //    which sums them in split order and stores bf16 C.
-//  * skinny (16 < M <= 64): a 1024-thread workgroup owns MS rows x 16*NB
-//    columns of C over the whole K; its 16 waves split K, each quantises its own
-//    A slice into a private LDS operand tile and runs the 16x16x128 instruction,
-//    and the 16 partial tiles are summed in LDS.
-//  * tiled (larger M, and every grouped problem): a 512-thread workgroup (8
-//    waves, one per CU) owns a 128 x 512 tile of C. Per 128-wide K step the
-//    workgroup quantises the 128x128 bf16 A block once into a double-buffered
-//    LDS tile; wave w computes all 128 rows x columns [64w, 64w+64) with the
-//    32x32x64 instruction from that shared A and its own B units, which arrive
-//    by buffer-to-LDS loads in a three-stage per-wave LDS ring two K steps
-//    ahead. The two waves sharing a SIMD run their matrix and quantisation
-//    phases in opposite orders so the two overlap. The C tile leaves through a
-//    per-wave LDS staging block as 16-byte row stores. Workgroups are ordered
-//    so that the ones sharing an XCD (and its L2) share A rows and B columns.
+//  * skinny (16 < M <= 64, and M <= 16 where a time model rates it faster
+//    than split-K): a 1024-thread workgroup owns MS rows x 16*NB columns of C
+//    over the whole K; its 16 waves split K, each quantises its own A slice
+//    into a private LDS operand tile and runs the 16x16x128 instruction, and
+//    the 16 partial tiles are summed in LDS. The same tile, on 8 waves and with
+//    up to three 16-row sub-tiles, serves the grouped calls' groups of at most
+//    48 rows.
+//  * tiled (larger M, and the grouped calls' larger groups): a 512-thread
+//    workgroup (8 waves, one per CU) owns a 128 x 512 tile of C. Per 128-wide
+//    K step the workgroup quantises the 128x128 bf16 A block once into a
+//    double-buffered LDS tile; wave w computes all 128 rows x columns
+//    [64w, 64w+64) with the 32x32x64 instruction from that shared A and its
+//    own B units, which arrive by buffer-to-LDS loads in a three-stage
+//    per-wave LDS ring two K steps ahead. The two waves sharing a SIMD run
+//    their matrix and quantisation phases in opposite orders so the two
+//    overlap. The C tile leaves through a per-wave LDS staging block as 16-byte
+//    row stores. Workgroups are ordered so that the ones sharing an XCD (and
+//    its L2) share A rows and B columns.
 #include <algorithm>
 #include <atomic>
 #include <mutex>
