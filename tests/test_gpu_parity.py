@@ -389,6 +389,27 @@ def test_grouped_small_subtiles_ragged():
         assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
 
 
+def test_grouped_on_a_side_stream():
+    """The grouped call reads the device's CU count through the stream it is given (a non-default stream
+    here); small and large groups, the same C as on the default stream."""
+    say("grouped on a side stream")
+    g = np.random.default_rng(14)
+    N, K = 600, 512
+    Ms = [9, 40, 130]
+    a = [to_dev_bf16(synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32))) for m in Ms]
+    b = [oracle.quant_mx(synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)))
+         for _ in Ms]
+    bp = [packed_b(*q) for q in b]
+    ref = [bits_of(c) for c in ops.grouped_gemm(a, bp, N)]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        cs = ops.grouped_gemm(a, bp, N)
+    side.synchronize()
+    for r, c in zip(ref, cs):
+        assert np.array_equal(r, bits_of(c))
+
+
 @pytest.mark.timeout(600)
 def test_grouped_decode_workload():
     """The decode-sized grouped workload (8 groups of 8..64 rows, N4096 K7168), every row."""
