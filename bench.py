@@ -220,7 +220,51 @@ def env_info():
             env["rocm"] = f.read().strip()
     except OSError:
         pass
+    smi = smi_info()
+    if smi:
+        env["smi"] = smi
     return env
+
+
+def smi_info():
+    """Shader and memory clock, package power and power cap of the GPU the run used, from rocm-smi, read
+    after the timed work (best effort: None when rocm-smi is missing or its card cannot be matched). The
+    card is matched by PCI bus number; if rocm-smi lists a single card, that one."""
+    import subprocess
+    import torch
+    try:
+        r = subprocess.run(["rocm-smi", "--showbus", "--showclocks", "--showpower", "--showmaxpower", "--json"],
+                           capture_output=True, text=True, timeout=20)
+        cards = json.loads(r.stdout)
+    except Exception:
+        return None
+    cards = {k: v for k, v in cards.items() if k.startswith("card") and isinstance(v, dict)}
+    pick = None
+    try:
+        bus = torch.cuda.get_device_properties(0).pci_bus_id
+        for k, v in cards.items():
+            b = next((x for n, x in v.items() if "bus" in n.lower()), "")
+            if isinstance(b, str) and b.count(":") >= 2 and int(b.split(":")[1], 16) == bus:
+                pick = k
+    except Exception:
+        pick = None
+    if pick is None and len(cards) == 1:
+        pick = next(iter(cards))
+    if pick is None:
+        return None
+    import re
+    out = {}
+    for n, v in cards[pick].items():
+        key = n.lower()
+        num = re.search(r"[\d.]+", str(v))
+        if not num:
+            continue
+        if key.startswith("mclk clock speed"):
+            out["mclk_mhz"] = float(num.group())
+        elif key.startswith("max graphics package power"):
+            out["power_cap_w"] = float(num.group())
+    # The shader clock read here, after the work, is the idle one; the clock under load is not sampled.
+    return dict(card=pick, **out) if out else None
 
 
 def log(msg):
