@@ -682,21 +682,25 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   const int sdw = qks * 64 + (chunk & 1) * 32 + (tid >> 4);
   const int tail_k = d.K - 128 * (d.KT - 1);
 
-  // A registers of one K step in flight: the bf16 pieces, or the pre-quantised
-  // codes and scale byte of this thread's (row, chunk). Two sets alternate: the A
-  // of step j+1 is quantised at step j while the A of step j+2 is arriving.
+  // A registers in flight. Fused: the bf16 pieces of one K step; two sets
+  // alternate, the A of step j+1 is quantised at step j while the A of step j+2
+  // is arriving. Pre-quantised: the codes and scale bytes of a PAIR of K steps
+  // (2p, 2p+1) for two rows of this thread; a wave's load then covers 8 rows x
+  // 128 bytes, whole cache lines (one step's 64 code bytes per row are half a
+  // line), and its scale-byte load 8 rows x 8 bytes. Set p%2 holds pair p.
   struct AStage {
     uint32_t raw[PREQ ? 1 : 4][4];
-    uint4 q;
-    uint32_t qb;
+    uint4 q[2];
+    uint32_t qb[2];
   };
   AStage s0, s1;
-  // Pre-quantised A: row qr = tid/4, chunk qc = tid%4 of the step; in the operand
+  // Pre-quantised A: thread tid holds, of a step pair, rows qr0 = tid/8 and
+  // qr0 + 64, 16-byte chunk qcc = tid%8 of the pair's 128 bytes, which is step
+  // 2p + qcc/4 and 32-element chunk qc = qcc%4 of that step; in the operand
   // layout that is 64-k half qc/2, 32-row tile qr/32, unit lane (qc%2)*32 + qr%32.
-  const int qr = tid >> 2, qc = tid & 3;
+  const int qr0 = tid >> 3, qcc = tid & 7, qc = qcc & 3, qhalf = qcc >> 2;
   const __amdgpu_buffer_rsrc_t aqr = row_window(p.Aq, p.ldaq, d.K / 2, p.M, m0);
   const __amdgpu_buffer_rsrc_t asr = row_window(p.As, p.ldas, d.K / 32, p.M, m0);
-  const int qslot = slot32((qc & 1) * 32 + (qr & 31), qc >> 1) * 4;
   // Step j's A (clamped to the last step: the loads run ahead of K and must stay
   // inside A, whose K offset is not range-checked; the extra copies go unused).
   auto load_a_piece = [&](int j, AStage& S, int h) {
@@ -709,27 +713,54 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
 #pragma unroll
       for (int h = 0; h < 4; ++h) load_a_piece(j, S, h);
     } else {
-      // The codes and the scale byte of the same (row, chunk): one byte load per
-      // thread, 16 rows per wave. (Loading a row's 4 scale bytes per thread
-      // touches one cache line per lane and floods the L1 with requests.)
-      S.q = bload16(aqr, (uint32_t)(qr * p.ldaq + 16 * qc), jo * 64);
-      S.qb = bload1(asr, (uint32_t)(qr * p.ldas + qc), jo * 4);
+      (void)jo;
+      (void)S;
+    }
+  };
+  // Pre-quantised: step pair p (clamped to the last pair that starts inside K;
+  // a pair's second step may lie past K, in row padding or the next row, and is
+  // never used) into set S: the codes and, from the same (row, step, chunk), the
+  // scale byte; a wave's scale-byte load covers 8 rows x 8 consecutive bytes.
+  auto load_pair = [&](int pr, AStage& S) {
+    const int last = (d.KT - 1) >> 1;
+    const uint32_t po = (uint32_t)(pr < last ? pr : last);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int r = qr0 + 64 * i;
+      S.q[i] = bload16(aqr, (uint32_t)(r * p.ldaq + 16 * qcc), po * 128);
+      S.qb[i] = bload1(asr, (uint32_t)(r * p.ldas + qcc), po * 8);
     }
   };
   // LDS byte addresses of this thread's A stores in buffer 0 (buffer 1 follows).
   constexpr uint32_t kABuf = sizeof(sm.a[0]), kSBuf = sizeof(sm.as[0]);
   const uint32_t qa = lds_addr(&sm.a[0][0][0][0]) + (uint32_t)wbase * 4;
   const uint32_t qs = lds_addr(&sm.as[0][0][0]) + (uint32_t)sdw * 4;
-  const uint32_t pa = lds_addr(&sm.a[0][qc >> 1][qr >> 5][qslot]);
-  // Scale byte of (row qr, chunk qc): half qc/2, unit lane (qc%2)*32 + qr%32,
-  // byte = 32-row tile qr/32.
-  const uint32_t ps = lds_addr(&sm.as[0][qc >> 1][(qc & 1) * 32 + (qr & 31)]) + (uint32_t)(qr >> 5);
-  // Pre-quantised: store the step's codes and scale byte into LDS buffer `buf`.
-  // A chunk past K gets zero codes and the neutral scale (never a NaN byte).
+  uint32_t pa[2], ps[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int qr = qr0 + 64 * i;
+    pa[i] = lds_addr(&sm.a[0][qc >> 1][qr >> 5][slot32((qc & 1) * 32 + (qr & 31), qc >> 1) * 4]);
+    // Scale byte of (row qr, chunk qc): half qc/2, unit lane (qc%2)*32 + qr%32,
+    // byte = 32-row tile qr/32.
+    ps[i] = lds_addr(&sm.as[0][qc >> 1][(qc & 1) * 32 + (qr & 31)]) + (uint32_t)(qr >> 5);
+  }
+  // Pre-quantised: step j's codes and scale bytes from set S into LDS buffer
+  // `buf`, by the threads whose half of the pair is step j (j%2). The other
+  // threads store too, into their own wave's C staging block (idle until the
+  // epilogue, which this wave alone writes after these stores): a select of
+  // the address rather than a branch, which would make the compiler keep the
+  // whole register set live across divergent code (it spilled). A chunk past K
+  // gets zero codes and the neutral scale (never a NaN byte).
+  const uint32_t sink = lds_addr(&sm.cst[wave][0]) + (uint32_t)l * 16;
+  const uint32_t sink_sc = lds_addr(&sm.cst[wave][0]) + 1024u + (uint32_t)l;
   auto store_preq = [&](int j, int buf, AStage& S) {
+    const bool mine = qhalf == (j & 1);
     const bool tl = j == d.KT - 1 && 32 * qc >= tail_k;  // K tail: not A
-    lds_st128(pa + buf * kABuf, tl ? make_uint4(0u, 0u, 0u, 0u) : S.q);
-    lds_st8<0>(ps + buf * kSBuf, tl ? mx::kScaleOne : S.qb);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      lds_st128(mine ? pa[i] + buf * kABuf : sink, tl ? make_uint4(0u, 0u, 0u, 0u) : S.q[i]);
+      lds_st8<0>(mine ? ps[i] + buf * kSBuf : sink_sc, tl ? mx::kScaleOne : S.qb[i]);
+    }
   };
   // Quantise the bf16 A of step j held in S into LDS buffer j&1. The lanes of a
   // quad hold the same four scales and all store that dword. A 32-element block
@@ -774,10 +805,17 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   };
   // Step jq's A from S into LDS buffer jq&1, and the A of step jl requested into
   // S: piece by piece for bf16 A, so that the loads spread over the VALU work.
-  auto quant_then_load = [&](int jq, int jl, AStage& S) {
+  // Pre-quantised, at step j = jq - 1 with phase PH = j % 4: step j+1 comes from
+  // set ((j+1)/2)%2 (sets 0, 1, 1, 0 for PH 0..3), and odd steps request pair
+  // (j+3)/2 into set ((j+3)/2)%2 (set 0 at PH 1, set 1 at PH 3) once both halves
+  // of the pair it held have been stored.
+  auto quant_then_load = [&](auto ph, int jq, int jl, AStage& S) {
     if constexpr (PREQ) {
-      store_preq(jq, jq & 1, S);
-      load_a(jl, S);
+      constexpr int PH = decltype(ph)::value;
+      (void)S;
+      store_preq(jq, jq & 1, (PH == 0 || PH == 3) ? s0 : s1);
+      if constexpr (PH == 1) load_pair((jq + 2) >> 1, s0);
+      if constexpr (PH == 3) load_pair((jq + 2) >> 1, s1);
     } else {
       quant_write(jq, S, [&](int h) { load_a_piece(jl, S, h); });
     }
@@ -886,11 +924,13 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Buffer loads a wave issues per A step: 4 (bf16 A), or 2 for pre-quantised A
-  // (codes and a scale byte), and per B step 6 for an even step (4 code units,
-  // 2 scale dwords) and 4 for an odd one (a scale dword covers two steps: the odd
-  // step reuses the dwords its even predecessor read). The waits below count the
-  // loads issued after a ring stage's.
+  // Buffer loads a wave issues per A step: 4 (bf16 A), or on average 2 for
+  // pre-quantised A (4 on odd steps: a pair's codes and scale bytes, none on
+  // even steps; any two consecutive steps hold exactly one odd one), and per B
+  // step 6 for an even step (4 code units, 2 scale dwords) and 4 for an odd one
+  // (a scale dword covers two steps: the odd step reuses the dwords its even
+  // predecessor read). The waits below count the loads issued after a ring
+  // stage's.
   constexpr int kLa = PREQ ? 2 : 4, kDb = 6;
   // K step j. Every step requests B(j+2) into the ring stage read at step j-1,
   // one load behind each of its first six matrix pairs, and the A of step j+3
@@ -904,7 +944,7 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   // wave's MFMAs run while the other wave's VALU quantisation runs. Loads
   // issued after B(j)'s, at B(j)'s use: matrix-first A(j+1), B(j+1), A(j+2);
   // quantisation-first A(j+2), B(j+1), A(j+3).
-  auto step = [&](auto mfma_first, auto odd, int j, int st, AStage& S) {
+  auto step = [&](auto mfma_first, auto odd, auto ph, int j, int st, AStage& S) {
     constexpr bool kOdd = decltype(odd)::value;
     const int st2 = st == 0 ? 2 : st - 1;
     const int jb = j + 2 < d.KT ? j + 2 : d.KT - 1;
@@ -922,9 +962,9 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
       wait_vm<2 * kLa + kDbNext>();
       compute(odd, j, st, dma_hook);
       __builtin_amdgcn_sched_barrier(0);
-      quant_then_load(j + 1, j + 3, S);
+      quant_then_load(ph, j + 1, j + 3, S);
     } else {
-      quant_then_load(j + 1, j + 3, S);
+      quant_then_load(ph, j + 1, j + 3, S);
       __builtin_amdgcn_sched_barrier(0);
       wait_vm<2 * kLa + kDbNext>();
       compute(odd, j, st, dma_hook);
@@ -933,15 +973,40 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
   };
   // Steps two at a time (the register sets alternate: even steps quantise from
   // s1), then an odd last step. Step j reads ring stage j % 3.
+  // (Pre-quantised A takes its register set by the step's phase modulo 4, so
+  // its loop runs four steps at a time.)
+  using Ph0 = std::integral_constant<int, 0>;
+  using Ph1 = std::integral_constant<int, 1>;
+  using Ph2 = std::integral_constant<int, 2>;
+  using Ph3 = std::integral_constant<int, 3>;
   auto run = [&](auto mfma_first) {
     int j = 0, st = 0;
-    for (; j + 1 < d.KT; j += 2) {
-      step(mfma_first, std::false_type{}, j, st, s1);
-      st = st == 2 ? 0 : st + 1;
-      step(mfma_first, std::true_type{}, j + 1, st, s0);
-      st = st == 2 ? 0 : st + 1;
+    auto next = [](int x) { return x == 2 ? 0 : x + 1; };
+    if constexpr (PREQ) {
+      for (; j + 3 < d.KT; j += 4) {
+        step(mfma_first, std::false_type{}, Ph0{}, j, st, s1);
+        st = next(st);
+        step(mfma_first, std::true_type{}, Ph1{}, j + 1, st, s0);
+        st = next(st);
+        step(mfma_first, std::false_type{}, Ph2{}, j + 2, st, s1);
+        st = next(st);
+        step(mfma_first, std::true_type{}, Ph3{}, j + 3, st, s0);
+        st = next(st);
+      }
+      if (j < d.KT) step(mfma_first, std::false_type{}, Ph0{}, j, st, s1);
+      st = next(st);
+      if (j + 1 < d.KT) step(mfma_first, std::true_type{}, Ph1{}, j + 1, st, s0);
+      st = next(st);
+      if (j + 2 < d.KT) step(mfma_first, std::false_type{}, Ph2{}, j + 2, st, s1);
+    } else {
+      for (; j + 1 < d.KT; j += 2) {
+        step(mfma_first, std::false_type{}, Ph0{}, j, st, s1);
+        st = next(st);
+        step(mfma_first, std::true_type{}, Ph1{}, j + 1, st, s0);
+        st = next(st);
+      }
+      if (j < d.KT) step(mfma_first, std::false_type{}, Ph0{}, j, st, s1);
     }
-    if (j < d.KT) step(mfma_first, std::false_type{}, j, st, s1);
     // No buffer-to-LDS load may still be in flight when the workgroup's LDS is
     // released. Draining inside each branch also keeps the compiler's wait
     // analysis from carrying one order's loads into the other order's loop (its
@@ -953,13 +1018,20 @@ __device__ __forceinline__ void tiled_tile(const Operand& p, const Dims& d, int 
       wait_vm<0>();
   };
 
-  // Prologue: B(0), B(1) and A(0..2) requested, A(0) quantised into buffer 0.
+  // Prologue: B(0), B(1) and A(0..2) requested (pre-quantised: step pairs 0 and
+  // 1), A(0) quantised into buffer 0.
   dma_b(0, 0, 6);
   dma_b(d.KT > 1 ? 1 : 0, 1, 4);
-  load_a(0, s0);
-  quant_store(0, s0);
-  load_a(1, s1);
-  load_a(2, s0);
+  if constexpr (PREQ) {
+    load_pair(0, s0);
+    load_pair(1, s1);
+    store_preq(0, 0, s0);
+  } else {
+    load_a(0, s0);
+    quant_store(0, s0);
+    load_a(1, s1);
+    load_a(2, s0);
+  }
   // Enter the loops with nothing in flight: the compiler's wait analysis would
   // otherwise carry the prologue's loads into the loop and wait on them there.
   wait_vm<0>();
