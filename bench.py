@@ -227,44 +227,40 @@ def env_info():
 
 
 def smi_info():
-    """Shader and memory clock, package power and power cap of the GPU the run used, from rocm-smi, read
-    after the timed work (best effort: None when rocm-smi is missing or its card cannot be matched). The
-    card is matched by PCI bus number; if rocm-smi lists a single card, that one."""
-    import subprocess
+    """Memory clock and package power cap of the GPU the run used, read from the amdgpu driver's sysfs files
+    (plain file reads: no child process is started, since a child of a profiled process would inherit the
+    profiler's preloaded library). The card is matched by PCI bus number. Best effort: None when the files
+    are absent or no card matches. The shader clock read after the work would be the idle one and is not
+    recorded."""
+    import glob
     import torch
     try:
-        r = subprocess.run(["rocm-smi", "--showbus", "--showclocks", "--showpower", "--showmaxpower", "--json"],
-                           capture_output=True, text=True, timeout=20)
-        cards = json.loads(r.stdout)
-    except Exception:
-        return None
-    cards = {k: v for k, v in cards.items() if k.startswith("card") and isinstance(v, dict)}
-    pick = None
-    try:
         bus = torch.cuda.get_device_properties(0).pci_bus_id
-        for k, v in cards.items():
-            b = next((x for n, x in v.items() if "bus" in n.lower()), "")
-            if isinstance(b, str) and b.count(":") >= 2 and int(b.split(":")[1], 16) == bus:
-                pick = k
     except Exception:
-        pick = None
-    if pick is None and len(cards) == 1:
-        pick = next(iter(cards))
-    if pick is None:
         return None
-    import re
-    out = {}
-    for n, v in cards[pick].items():
-        key = n.lower()
-        num = re.search(r"[\d.]+", str(v))
-        if not num:
+    for dev in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
+        try:
+            pci = os.path.basename(os.path.realpath(dev))  # e.g. 0000:a4:00.0
+            if int(pci.split(":")[1], 16) != bus:
+                continue
+        except (ValueError, IndexError):
             continue
-        if key.startswith("mclk clock speed"):
-            out["mclk_mhz"] = float(num.group())
-        elif key.startswith("max graphics package power"):
-            out["power_cap_w"] = float(num.group())
-    # The shader clock read here, after the work, is the idle one; the clock under load is not sampled.
-    return dict(card=pick, **out) if out else None
+        out = {"card": os.path.basename(os.path.dirname(dev)), "pci": pci}
+        try:
+            with open(os.path.join(dev, "pp_dpm_mclk")) as f:
+                for line in f:
+                    if "*" in line:
+                        out["mclk_mhz"] = float(line.split(":")[1].lower().split("mhz")[0])
+        except (OSError, ValueError, IndexError):
+            pass
+        for cap in glob.glob(os.path.join(dev, "hwmon", "hwmon*", "power1_cap")):
+            try:
+                with open(cap) as f:
+                    out["power_cap_w"] = int(f.read().strip()) / 1e6
+            except (OSError, ValueError):
+                pass
+        return out
+    return None
 
 
 def log(msg):

@@ -33,8 +33,10 @@ def case(M, N, K, seed):
 
 
 # The skinny decode shape, then smaller split-K calls (fewer tiles and splits than the first left
-# behind in the shared array), then the 16 < M <= 64 and tiled paths (no scratch), then split-K again.
-SEQUENCE = [(16, 2112, 7168), (5, 300, 1024), (1, 64, 128), (40, 500, 2048), (130, 600, 1024), (16, 2112, 7168)]
+# behind in the shared array), then calls that need no scratch (one split; the skinny kernel at M <= 16
+# and at 16 < M <= 64; the tiled kernel), then split-K again.
+SEQUENCE = [(16, 2112, 7168), (16, 264, 7168), (8, 1000, 6144), (1, 64, 128), (5, 300, 1024), (40, 500, 2048),
+            (130, 600, 1024), (16, 2112, 7168)]
 
 
 def test_noalloc_matches_fused_on_consecutive_calls():
@@ -66,3 +68,30 @@ def test_noalloc_rejects_geometry_beyond_the_scratch():
     assert rc == 4  # MXFP4_ERR_WORKSPACE, nothing launched
     torch.cuda.synchronize()
     assert (c == 5.0).all()
+
+
+def test_noalloc_captured_in_a_graph():
+    """The callers it is for: a HIP graph captures the call once (no allocation inside the capture) and
+    replays it on new data in the same buffers, with eager work in between; every replay must equal the
+    eager gemm_a4w4_fused on that data bit for bit (the split-K partials start from zero each time)."""
+    M, N, K = 16, 2112, 7168
+    _, _, _, a, bp = case(M, N, K, 11)
+    c = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        rc = ops.lib().gemm_a4w4_fused_noalloc(a.data_ptr(), K, bp.data_ptr(), c.data_ptr(), N, M, N, K,
+                                               torch.cuda.current_stream().cuda_stream)
+    assert rc == 0
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(12)
+    for r in range(4):
+        print(f"noalloc graph replay {r}", flush=True)
+        a.copy_(to_dev_bf16(synth.f32_to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))))
+        ref = ops.gemm(a, bp, N)      # eager, with its own workspace
+        torch.cuda.synchronize()
+        c.fill_(3.0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(c), bits_of(ref)), f"replay {r} differs from the eager call"
