@@ -84,6 +84,10 @@ def parse():
     p.add_argument("--no-graph", action="store_true", help="time an eager launch loop instead of a graph replay")
     p.add_argument("--unfused", action="store_true",
                    help="time the two-launch comparator instead: mxfp4_quant(A), then gemm_a4w4 on A_q")
+    p.add_argument("--no-library", action="store_true",
+                   help="default run: skip timing the library MXFP4 GEMM (torch._scaled_mm) on the headline")
+    p.add_argument("--library", action="store_true",
+                   help="with --workload (a single GEMM): also time the library MXFP4 GEMM on the same operands")
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run plain device copies of a known size (counter calibration)")
     p.add_argument("--summarize-stats", metavar="DIR", help="print a summary of rocprofv3 --kernel-trace CSV output")
@@ -630,6 +634,8 @@ def main():
         return
     if args.workload is not None:
         out, w, unit = bench_gemm(args.workload, args)
+        if args.library:
+            out["library"] = bench_library(args.workload, args)
         if not args.no_cpu_baseline:
             log("[bench] timing the CPU oracle on a bounded sample")
             out["cpu_baseline"] = cpu_baseline(w, unit)
@@ -647,6 +653,8 @@ def main():
         extras[name] = dict(config=o["config"], us_per_call=o["us_per_call"], tflops=o["tflops"], hbm_gbs=o["hbm_gbs"],
                             roofline=rf)
     out["workloads"] = extras
+    if not args.no_library:
+        out["library"] = bench_library(HEADLINE, args)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         out["cpu_baseline"] = cpu_baseline(synth_workload(HEADLINE, args), unit)
@@ -760,6 +768,62 @@ def bench_gemm(name, args, sustained_steps=0):
     del sets, a0, b0
     torch.cuda.empty_cache()
     return out, w, unit
+
+
+def bench_library(name, args):
+    """The platform library's MXFP4 GEMM on the same workload, for comparison: torch._scaled_mm with
+    float4_e2m1fn_x2 operands and float8_e8m0fnu block scales (hipBLASLt on ROCm). Its A and B are the
+    codes and scale bytes of mxfp4_quant, made outside the timed region, so it times the GEMM alone
+    (no quantisation of A), over rotated operand sets with the same protocol as bench_gemm. Its C is
+    checked against gemm_a4w4 on the same codes (the same exact products; only the fp32 summation
+    order may differ) with the tests' tolerance |d| <= 2^-7 |C| + 1e-3 max|C|."""
+    import torch
+    from mxfp4_block_scaled_02_amd import ops, synth
+    path = "torch._scaled_mm (float4_e2m1fn_x2 x float8_e8m0fnu 1x32 scales, bf16 out; hipBLASLt)"
+    if name in synth.GROUPED:
+        return dict(path=path, error="single-GEMM workloads only")
+    f4, e8 = getattr(torch, "float4_e2m1fn_x2", None), getattr(torch, "float8_e8m0fnu", None)
+    if f4 is None or e8 is None:
+        return dict(path=path, error="this torch has no float4_e2m1fn_x2 / float8_e8m0fnu")
+    dev = torch.device("cuda:0")
+    w = synth_workload(name, args)
+    M, N, K = w["M"], w["N"], w["K"]
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    aq, asc = ops.quant(bf16(w["A"]))
+    bq, bsc = ops.quant(bf16(w["B"]))
+    set_bytes = aq.numel() + asc.numel() + bq.numel() + bsc.numel() + 2 * M * N
+    R = n_sets(args, set_bytes)
+    sets = [tuple(x.clone() if r else x for x in (aq, asc, bq, bsc)) + (torch.empty((M, N), dtype=torch.bfloat16,
+                                                                                        device=dev),)
+            for r in range(R)]
+
+    def call(i):
+        a, sa, b, sb, c = sets[i % R]
+        c.copy_(torch._scaled_mm(a.view(f4), b.view(f4).t(), sa.view(e8), sb.view(e8), out_dtype=torch.bfloat16))
+
+    def lib_step(i):
+        a, sa, b, sb, _ = sets[i % R]
+        torch._scaled_mm(a.view(f4), b.view(f4).t(), sa.view(e8), sb.view(e8), out_dtype=torch.bfloat16)
+
+    try:
+        call(0)
+        ref = ops.gemm_a4w4(aq, asc, ops.pack_B(bq, bsc), N).float()
+        got = sets[0][4].float()
+        ok = bool(((got - ref).abs() <= 2.0 ** -7 * ref.abs() + 1e-3 * ref.abs().max()).all())
+        ms = timed_steps(lib_step, args)
+    except Exception as e:  # noqa: BLE001 - reported, never fatal to the bench line
+        return dict(path=path, error=f"{type(e).__name__}: {e}"[:300])
+    flops = alg_flops(M, N, K)
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = dict(path=path, operands="A and B quantised by mxfp4_quant outside the timed region: the GEMM alone",
+               us_per_call=round(ms * 1e3, 3), tflops=round(tflops, 3), frac_mfma=round(tflops / FP4_PEAK_TFLOPS, 4),
+               agrees_with_gemm_a4w4=ok, cache=cache_label(args, R, set_bytes))
+    del sets
+    torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":
