@@ -80,9 +80,11 @@ int mxfp4_quant(const void* x, int64_t ldx, void* q, int64_t ldq, void* s, int64
  * ``_quant_shuffled``) as the step before the GEMM in a transformer layer; the
  * pages print none of its arithmetic, so the norm is the standard one:
  *   ss  = sum_k x[k]^2, the exact sum taken in float64; the library adds the
- *         (exact) squares in one fixed order (64 lane sums, lane t adding
- *         k = 512c + 8t + e for c = 0, 1, ... and e = 0..7 in that order, then
- *         a halving tree over the lanes), so results are reproducible bit for
+ *         (exact) squares in one fixed order (64 lane sums per wave, lane t
+ *         adding k = 512c + 8t + e over the wave's 512-element passes c in
+ *         order and e = 0..7; a halving tree over the lanes; for K <= 8192
+ *         the row's passes are split over four waves in order and their sums
+ *         added in wave order), so results are reproducible bit for
  *         bit, and ss is within (K-1)*2^-53 relative of the exact sum; inv
  *         below differs from the value the exact sum (rounded once) gives only
  *         when that difference crosses an fp32 rounding boundary of inv;

@@ -4,16 +4,22 @@
 // without printing its arithmetic; the norm is the standard root-mean-square
 // normalisation).
 //
-// One wave per row. Lane l takes the 8 elements k = 512c + 8l .. +7 of pass c,
-// so a lane quad holds one 32-element block and one 16-byte load per lane per
-// pass covers 1 KB of the row. Pass one sums the squares in float64, each lane
-// in pass-then-element order, and the 64 lane sums meet in a halving tree
-// (S[t] += S[t+s], s = 32 .. 1): a fixed order, so the result, and with it
+// A row is read in passes of 512 elements: lane l of a wave takes the 8
+// elements k = 512c + 8l .. +7 of pass c, so a lane quad holds one 32-element
+// block and one 16-byte load per lane covers 1 KB of the row. Rows of up to 16
+// passes (K <= 8192) take one 256-thread workgroup each: wave v of its four
+// takes passes [P*v/4, P*(v+1)/4) and keeps them in registers (x is read once).
+// Longer rows take one wave each and read x again for the second phase.
+//
+// Phase one sums the squares in float64, each lane over its passes in
+// pass-then-element order; the 64 lane sums meet in a halving tree
+// (S[t] += S[t+s], s = 32 .. 1), and a row split over four waves adds the
+// waves' sums in wave order. The order is fixed, so the result, and with it
 // every quantised code, is the same on every run. The squares are exact; the
 // sum is within (K-1)*2^-53 relative of the exact sum of squares, which is
 // what the norm's definition asks for (an fp32 inv that this moves across a
 // rounding boundary would differ from the exact one). inv = fp32(1 / sqrt(ss/K +
-// eps)) with float64 steps; pass two forms y = bf16((x * inv) * w) in fp32 and
+// eps)) with float64 steps; phase two forms y = bf16((x * inv) * w) in fp32 and
 // quantises it with the lane-quad routine of the GEMM, storing codes and scale
 // bytes row-major as mxfp4_quant does.
 #include "host_common.hpp"
@@ -34,8 +40,10 @@ struct RmsArgs {
   float eps;
 };
 
-constexpr int kRowsPerBlock = 4;  // waves per 256-thread workgroup, one row each
-constexpr int kBatch = 8;         // passes whose loads are in flight together
+constexpr int kRowWaves = 4;      // waves per row (and per 256-thread workgroup), rows of <= kRowPasses passes
+constexpr int kRowPasses = 16;    // 4 passes per wave
+constexpr int kLongRows = 4;      // rows per 256-thread workgroup of the long-row kernel, one wave each
+constexpr int kBatch = 8;         // passes whose loads are in flight together (long rows)
 
 // Row loads go through a buffer resource over the row's 2K bytes: a lane whose
 // 16 bytes lie past the row reads zeros by the range check on its own offset,
@@ -87,76 +95,81 @@ __device__ __forceinline__ double add_squares(double acc, const uint4& v) {
   return acc;
 }
 
-// The 64 lane sums in the halving tree, then inv = fp32(1 / sqrt(ss/K + eps)).
-__device__ __forceinline__ float row_inv(double acc, int l, int K, float eps) {
+// The 64 lane sums of a wave in the halving tree; lane 0 ends with the total.
+__device__ __forceinline__ double wave_sum(double acc, int l) {
 #pragma unroll
   for (int s = 32; s >= 1; s >>= 1) {
     const double o = __shfl_down(acc, (unsigned)s, 64);
     if (l < s) acc = acc + o;
   }
-  const double ss = __shfl(acc, 0, 64);
+  return acc;
+}
+
+__device__ __forceinline__ float inv_of(double ss, int K, float eps) {
   const double ms = ss / (double)K + (double)eps;
   return (float)(1.0 / __builtin_sqrt(ms));
 }
 
-// KEEP > 0 (even): rows of at most KEEP passes keep x in registers between
-// the two passes (one read of x). KEEP == 0: any K, x read again in pass two,
-// kBatch passes at a time.
-template <int KEEP>
-__global__ __launch_bounds__(256) void rmsnorm_quant_kernel(RmsArgs a) {
+// Rows of at most kRowPasses passes: workgroup = row, wave v = passes
+// [P*v/4, P*(v+1)/4) (at most 4; none for some waves when P < 4). Its x and w
+// stay in registers between the phases; the four wave sums meet in LDS.
+__global__ __launch_bounds__(64 * kRowWaves) void rmsnorm_quant_rows_kernel(RmsArgs a) {
+  constexpr int KP = kRowPasses / kRowWaves;
+  __shared__ double part[kRowWaves];
+  const int v = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int64_t r = blockIdx.x;
+  const __amdgpu_buffer_rsrc_t xr = row_rsrc(a.x + r * a.ldx, 2 * a.K), wr = row_rsrc(a.w, 2 * a.K);
+  const int P = (a.K + 511) / 512;
+  const int c0 = P * v / kRowWaves, c1 = P * (v + 1) / kRowWaves;
+  // Passes past this wave's range read offset K: past the row, zeros.
+  uint4 xv[KP], wv[KP];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) xv[i] = row_load16_nt(xr, c0 + i < c1 ? 512 * (c0 + i) + 8 * l : a.K);
+#pragma unroll
+  for (int i = 0; i < KP; ++i) wv[i] = row_load16(wr, c0 + i < c1 ? 512 * (c0 + i) + 8 * l : a.K);
+  double acc = 0.0;
+#pragma unroll
+  for (int i = 0; i < KP; ++i) acc = add_squares(acc, xv[i]);  // zeros past the range add nothing
+  acc = wave_sum(acc, l);
+  if (l == 0) part[v] = acc;
+  __syncthreads();
+  double ss = part[0];
+#pragma unroll
+  for (int u = 1; u < kRowWaves; ++u) ss = ss + part[u];
+  const float inv = inv_of(ss, a.K, a.eps);
+#pragma unroll
+  for (int i = 0; i < KP; ++i)
+    if (c0 + i < c1) norm_quant_pass(a, r, 512 * (c0 + i) + 8 * l, xv[i], wv[i], inv, l);
+}
+
+// Longer rows: one wave per row, x read again in phase two, kBatch passes at a
+// time.
+__global__ __launch_bounds__(64 * kLongRows) void rmsnorm_quant_long_kernel(RmsArgs a) {
   const int wave = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * kRowsPerBlock + wave;
+  const int64_t r = (int64_t)blockIdx.x * kLongRows + wave;
   if (r >= a.M) return;  // whole waves only; the kernel has no barrier
   const __amdgpu_buffer_rsrc_t xr = row_rsrc(a.x + r * a.ldx, 2 * a.K), wr = row_rsrc(a.w, 2 * a.K);
   const int passes = (a.K + 511) / 512;
-
-  if constexpr (KEEP > 0) {
-    uint4 v[KEEP];
+  double acc = 0.0;
+  for (int c0 = 0; c0 < passes; c0 += kBatch) {
+    uint4 v[kBatch];
 #pragma unroll
-    for (int c = 0; c < KEEP; ++c) v[c] = row_load16_nt(xr, c < passes ? 512 * c + 8 * l : a.K);
-    double acc = 0.0;
+    for (int b = 0; b < kBatch; ++b) v[b] = row_load16_nt(xr, 512 * (c0 + b) + 8 * l);
 #pragma unroll
-    for (int c = 0; c < KEEP; ++c) acc = add_squares(acc, v[c]);
-    // w is the same for every row (cache-resident): it is read two passes
-    // ahead of its use rather than held, which leaves registers for a third
-    // wave per SIMD at K <= 7168.
-    uint4 w0 = row_load16(wr, 8 * l), w1 = row_load16(wr, 1 < passes ? 512 + 8 * l : a.K);
-    const float inv = row_inv(acc, l, a.K, a.eps);
+    for (int b = 0; b < kBatch; ++b) acc = add_squares(acc, v[b]);
+  }
+  const float inv = inv_of(__shfl(wave_sum(acc, l), 0, 64), a.K, a.eps);
+  for (int c0 = 0; c0 < passes; c0 += kBatch) {
+    uint4 xv[kBatch], wv[kBatch];
 #pragma unroll
-    for (int c = 0; c < KEEP; c += 2) {
-      const uint4 n0 = row_load16(wr, c + 2 < passes ? 512 * (c + 2) + 8 * l : a.K);
-      const uint4 n1 = row_load16(wr, c + 3 < passes ? 512 * (c + 3) + 8 * l : a.K);
-      if (c < passes) norm_quant_pass(a, r, 512 * c + 8 * l, v[c], w0, inv, l);
-      if (c + 1 < passes) norm_quant_pass(a, r, 512 * (c + 1) + 8 * l, v[c + 1], w1, inv, l);
-      w0 = n0;
-      w1 = n1;
+    for (int b = 0; b < kBatch; ++b) {
+      xv[b] = row_load16_nt(xr, 512 * (c0 + b) + 8 * l);
+      wv[b] = row_load16(wr, 512 * (c0 + b) + 8 * l);
     }
-  } else {
-    double acc = 0.0;
-    for (int c0 = 0; c0 < passes; c0 += kBatch) {
-      uint4 v[kBatch];
 #pragma unroll
-      for (int b = 0; b < kBatch; ++b) v[b] = row_load16_nt(xr, 512 * (c0 + b) + 8 * l);
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) acc = add_squares(acc, v[b]);
-    }
-    const float inv = row_inv(acc, l, a.K, a.eps);
-    for (int c0 = 0; c0 < passes; c0 += kBatch) {
-      uint4 xv[kBatch], wv[kBatch];
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        xv[b] = row_load16_nt(xr, 512 * (c0 + b) + 8 * l);
-        wv[b] = row_load16(wr, 512 * (c0 + b) + 8 * l);
-      }
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) norm_quant_pass(a, r, 512 * (c0 + b) + 8 * l, xv[b], wv[b], inv, l);
-    }
+    for (int b = 0; b < kBatch; ++b) norm_quant_pass(a, r, 512 * (c0 + b) + 8 * l, xv[b], wv[b], inv, l);
   }
 }
-
-// Rows of up to 14 passes (K <= 7168: three waves per SIMD) or 16 passes
-// (K <= 8192: two) take the register-resident kernel.
-constexpr int kKeepPasses = 16, kKeepPassesShort = 14;
 
 }  // namespace
 
@@ -172,9 +185,10 @@ extern "C" int mxfp4_rmsnorm_quant(const void* x, int64_t ldx, const void* w, fl
   RmsArgs a{(const uint16_t*)x, ldx, (const uint16_t*)w, (uint8_t*)q, ldq, (uint8_t*)s, lds, M, (int)K, eps};
   void* args[] = {&a};
   const int64_t passes = (K + 511) / 512;
-  const void* kern = passes <= kKeepPassesShort ? (const void*)rmsnorm_quant_kernel<kKeepPassesShort>
-                     : passes <= kKeepPasses    ? (const void*)rmsnorm_quant_kernel<kKeepPasses>
-                                                : (const void*)rmsnorm_quant_kernel<0>;
-  return mxh::launch_status(hipLaunchKernel(kern, dim3((unsigned)mxh::cdiv(M, kRowsPerBlock)), dim3(256), args, 0,
+  if (passes <= kRowPasses)  // one workgroup per row (M <= 2^30)
+    return mxh::launch_status(hipLaunchKernel((const void*)rmsnorm_quant_rows_kernel, dim3((unsigned)M),
+                                              dim3(64 * kRowWaves), args, 0, (hipStream_t)stream));
+  return mxh::launch_status(hipLaunchKernel((const void*)rmsnorm_quant_long_kernel,
+                                            dim3((unsigned)mxh::cdiv(M, kLongRows)), dim3(64 * kLongRows), args, 0,
                                             (hipStream_t)stream));
 }

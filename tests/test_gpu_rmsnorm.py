@@ -51,8 +51,8 @@ def check(xb, wb, eps, rows=None, **kw):
 
 @pytest.mark.parametrize("M,K", [(1, 32), (3, 96), (4, 512), (5, 544), (16, 7168), (17, 1056), (64, 2048),
                                  (2, 8192), (3, 8224), (2, 16384),
-                                 # register-resident kernels: 14 passes with a partial last one;
-                                 # 15 passes (odd count in the 16-pass kernel), whole and partial
+                                 # the row kernel's uneven wave shares: 14 passes with a partial last
+                                 # one; 15 passes, whole and partial
                                  (3, 6688), (3, 7680), (3, 7200)])
 def test_parity_small(M, K):
     say(f"[rmsnorm] M{M} K{K}")
