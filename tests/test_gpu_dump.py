@@ -107,6 +107,16 @@ def test_fused_quant_bytes_grouped_small_and_large():
     run_grouped(a_list, b_list, N, "mixed groups")
 
 
+def test_fused_quant_bytes_grouped_more_tiles_than_cus():
+    """More 128 x 512 tiles than CUs (264: a second round of workgroups), a K tail on odd K/64."""
+    g = np.random.default_rng(23)
+    N, K = 4096, 1056
+    Ms = [640, 512, 384, 1024, 256, 200, 700, 300]
+    a_list = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
+    b_list = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
+    run_grouped(a_list, b_list, N, "264 tiles")
+
+
 def test_fused_quant_bytes_grouped_small_subtiles():
     """Small groups in tiles of all their rows (more 16-row tiles than one round of workgroups), ragged."""
     g = np.random.default_rng(22)

@@ -389,6 +389,29 @@ def test_grouped_small_subtiles_ragged():
         assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
 
 
+def _tile_rows(m):
+    """First and last row of every 128-row tile of an M-row group (whole rows: every column tile)."""
+    return np.unique(np.concatenate([np.arange(0, m, 128), np.minimum(np.arange(127, m + 127, 128), m - 1)]))
+
+
+# More 128 x 512 tiles than the 256 CUs (a second round of workgroups): 264 tiles over 9 K steps (odd K/64,
+# a K tail); 320 tiles over 3 K steps; 306 tiles over one K step with a ragged N.
+@pytest.mark.parametrize("Ms,N,K", [([640, 512, 384, 1024, 256, 200, 700, 300], 4096, 1056),
+                                    ([1024, 1024, 1024, 1024, 1000], 4096, 352),
+                                    ([1200, 1200, 1200, 1200, 1200, 100], 3000, 32)])
+def test_grouped_more_tiles_than_cus(Ms, N, K):
+    say(f"grouped Ms {Ms} N{N} K{K}")
+    g = np.random.default_rng(41)
+    a = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
+    b = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
+    qs = [oracle.quant_mx(x) for x in b]
+    cs = ops.grouped_gemm([to_dev_bf16(x) for x in a], [packed_b(*q) for q in qs], N)
+    torch.cuda.synchronize()
+    for gi, (x, (bq, bs), c) in enumerate(zip(a, qs, cs)):
+        rows = _tile_rows(x.shape[0])
+        assert_in_tolerance(bits_of(c)[rows], oracle.gemm_ref(x[rows], bq, bs), f"group {gi} (M={x.shape[0]})")
+
+
 def test_grouped_on_a_side_stream():
     """The grouped call reads the device's CU count through the stream it is given (a non-default stream
     here); small and large groups, the same C as on the default stream."""
