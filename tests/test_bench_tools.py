@@ -109,7 +109,8 @@ def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, capsys):
     assert rec["kernel_source_hash"] == bench.kernel_source_hash()
 
 
-@pytest.mark.parametrize("name", ["square", "skinny", "stress", "grouped", "grouped_decode", "rmsnorm"])
+@pytest.mark.parametrize("name", ["square", "skinny", "stress", "grouped", "grouped_decode", "rmsnorm", "grouped_mnk",
+                                  "nvfp4_grouped", "square_unfused"])
 def test_committed_traffic_records_match_the_sources(name, monkeypatch):
     b = bench.recorded_traffic(name)
     assert b is not None and b > 0, f"profiles/traffic_{name}.json is stale or missing"
