@@ -218,9 +218,10 @@ int gemm_a4w4(const void* Aq, int64_t ldaq, const void* As, int64_t ldas, const 
  * grouped_gemm_a4w4 -- G independent fused problems C_g = Q(A_g) . B_g^T that
  * share N and K, in ONE launch (page 496271, ``custom_kernel``: a list of
  * per-group problems; there one launch per group, here a single launch whose
- * workgroups are spread over all groups' output tiles). A group of at most 48
- * rows takes 16 x 128 output tiles (its B spread over many CUs), a larger one
- * 128 x 512 tiles; each group's C is the same whatever the other groups are.
+ * workgroups are spread over all groups' output tiles). A group of at most 64
+ * rows takes output tiles of 16 to 64 rows x 128 columns (its B spread over
+ * many CUs), a larger one 128 x 512 tiles; each group's C is the same whatever
+ * the other groups are.
  *   groups : HOST array of G descriptors, read during the call only. Per
  *            group the same rules as gemm_a4w4_fused apply to A, lda, Bp, C,
  *            ldc; M >= 1.
@@ -249,7 +250,7 @@ int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, int64_t K, vo
  * [C_g][M_g][K/32]) follows group g-1's.
  * dump: at least grouped_gemm_a4w4_dump_bytes(groups, G, N, K) bytes,
  * 16-byte aligned.
- * grouped_gemm_a4w4_dump_copies(M_g, N) gives C_g (ceil(N/128) for M_g <= 48,
+ * grouped_gemm_a4w4_dump_copies(M_g, N) gives C_g (ceil(N/128) for M_g <= 64,
  * ceil(N/512) otherwise); 0 for M_g or N outside [1, 2^30]. */
 size_t grouped_gemm_a4w4_dump_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K);
 int64_t grouped_gemm_a4w4_dump_copies(int64_t M, int64_t N);

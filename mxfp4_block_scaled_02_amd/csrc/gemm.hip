@@ -24,8 +24,8 @@
 //    over the whole K; its 16 waves split K, each quantises its own A slice
 //    into a private LDS operand tile and runs the 16x16x128 instruction, and
 //    the 16 partial tiles are summed in LDS. The same tile, on 8 waves and with
-//    up to three 16-row sub-tiles, serves the grouped calls' groups of at most
-//    48 rows.
+//    up to four 16-row sub-tiles, serves the grouped calls' groups of at most
+//    64 rows.
 //  * tiled (larger M, and the grouped calls' larger groups): a 512-thread
 //    workgroup (8 waves, one per CU) owns a 128 x 512 tile of C. Per 128-wide
 //    K step the workgroup quantises the 128x128 bf16 A block once into a
@@ -173,12 +173,12 @@ struct SkinnySmem {
 // Rows m0 .. m0+MS-1 x 16-column tiles T0 .. T0+NB-1 of C over the whole K, by
 // the WAVES waves of the calling workgroup (all of its threads), each taking a
 // contiguous share of the K steps; the partial tiles are summed in LDS. MS of
-// 32 or 48 is two or three 16-row sub-tiles that share each B operand the wave
-// loads. `copy` is the verification dump's copy index of this tile's quantised A.
+// 32, 48 or 64 is two to four 16-row sub-tiles that share each B operand the
+// wave loads. `copy` is the verification dump's copy index of this tile's quantised A.
 template <int WAVES, int MS, int NB, int PF, bool DUMP>
 __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int m0, int T0, int copy,
                                             SkinnySmem<WAVES, NB, (MS + 15) / 16>& sm) {
-  static_assert(MS == 4 || MS == 8 || MS == 16 || MS == 32 || MS == 48, "rows per workgroup");
+  static_assert(MS == 4 || MS == 8 || MS == 16 || MS == 32 || MS == 48 || MS == 64, "rows per workgroup");
   constexpr int MT = (MS + 15) / 16;  // 16-row sub-tiles
   constexpr int PIECES = MS / 4;      // 16-byte A pieces per lane per K step (piece h: sub-tile h/4)
   auto& sAq = sm.aq;
@@ -1092,19 +1092,20 @@ __global__ __launch_bounds__(kTThreads) void gemm_tiled_kernel(Operand p, Dims d
 }
 
 // Grouped GEMM. A group of at most kGsMaxM rows is an HBM-bound problem (its B
-// is read once for very few rows): it takes small tiles of all its rows (16, 32
-// or 48, one to three 16-row sub-tiles) x 128 columns over the whole K, the
-// workgroup's 8 waves splitting K (the skinny tile), so that its B spreads over
-// many CUs and each B byte is loaded once; a 128 x 512 tile would give it one
-// CU per 512 columns and leave the matrix cores of that CU computing 128 rows
-// for a few.
+// is read once for very few rows): it takes small tiles of one to four 16-row
+// sub-tiles x 128 columns over the whole K, the workgroup's 8 waves splitting K
+// (the skinny tile), so that its B spreads over many CUs; a 128 x 512 tile
+// would give it one CU per 512 columns and leave the matrix cores of that CU
+// computing 128 rows for a few. The host picks the fewest sub-tiles per tile
+// at which the launch fits one round of workgroups, else all of the group's
+// rows (each B byte then loaded once).
 // Larger groups take the 128 x 512 tiled tiles. The large tiles take the first
 // workgroup ids, so the hardware starts them first (they run longest), and the
 // small tiles fill the other CUs beside them and whatever frees up. Each range
 // is remapped for the XCDs on its own (the large range padded to a multiple of
 // 8 ids with idle workgroups), and a small group's row tiles of one column tile
 // are adjacent (they share that B in one XCD's L2).
-constexpr int kGsMaxM = 48, kGsNB = 8;
+constexpr int kGsMaxM = 64, kGsNB = 8;
 
 struct GroupedArgs {
   Operand g[MXFP4_MAX_GROUPS];
@@ -1138,7 +1139,7 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, 
   // lives in the ring's bytes.
   __shared__ __align__(16) TiledSmem sm;
   __shared__ __align__(16) uint8_t ring[kRingBytes];
-  static_assert(sizeof(SkinnySmem<kTWaves, kGsNB, 3>) <= sizeof(ring), "skinny tile LDS");
+  static_assert(sizeof(SkinnySmem<kTWaves, kGsNB, 4>) <= sizeof(ring), "skinny tile LDS");
   if (e >= a.small_from) {
     const int c = local / a.rows[e], r = local - c * a.rows[e];
     if (a.mt[e] == 1)
@@ -1147,9 +1148,12 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, 
     else if (a.mt[e] == 2)
       skinny_tile<kTWaves, 32, kGsNB, 1, DUMP>(p, d, r * 32, c * kGsNB, c,
                                                *reinterpret_cast<SkinnySmem<kTWaves, kGsNB, 2>*>(ring));
-    else
+    else if (a.mt[e] == 3)
       skinny_tile<kTWaves, 48, kGsNB, 1, DUMP>(p, d, r * 48, c * kGsNB, c,
                                                *reinterpret_cast<SkinnySmem<kTWaves, kGsNB, 3>*>(ring));
+    else
+      skinny_tile<kTWaves, 64, kGsNB, 1, DUMP>(p, d, r * 64, c * kGsNB, c,
+                                               *reinterpret_cast<SkinnySmem<kTWaves, kGsNB, 4>*>(ring));
   } else {
     tiled_tile<false, DUMP>(p, d, local / a.ntiles_n, local % a.ntiles_n, sm, ring);
   }
@@ -1172,7 +1176,7 @@ struct MnkProblem {
   uint16_t* C;
   int64_t ldc;
   int M, N, K;
-  int mt;    // 0: tiled tiles; 1..3: skinny tiles of mt 16-row sub-tiles
+  int mt;    // 0: tiled tiles; 1..4: skinny tiles of mt 16-row sub-tiles
   int rows;  // skinny row tiles per column tile
 };
 struct MnkArgs {
@@ -1215,9 +1219,12 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_mnk_kernel(MnkArgs a) 
     else if (q.mt == 2)
       skinny_tile<kTWaves, 32, kGsNB, 1, false>(o, d, r * 32, c * kGsNB, c,
                                                 *reinterpret_cast<SkinnySmem<kTWaves, kGsNB, 2>*>(ring));
-    else
+    else if (q.mt == 3)
       skinny_tile<kTWaves, 48, kGsNB, 1, false>(o, d, r * 48, c * kGsNB, c,
                                                 *reinterpret_cast<SkinnySmem<kTWaves, kGsNB, 3>*>(ring));
+    else
+      skinny_tile<kTWaves, 64, kGsNB, 1, false>(o, d, r * 64, c * kGsNB, c,
+                                                *reinterpret_cast<SkinnySmem<kTWaves, kGsNB, 4>*>(ring));
   } else {
     const int ntn = (q.N + kTBN - 1) / kTBN;
     tiled_tile<false>(o, d, local / ntn, local % ntn, sm, ring);
@@ -1603,6 +1610,21 @@ namespace {
 // of the tile kind the group takes.
 int64_t grouped_copies(int64_t M, int64_t N) { return M <= kGsMaxM ? mxh::cdiv(N, 16 * kGsNB) : mxh::cdiv(N, kTBN); }
 
+// 16-row sub-tiles per small tile: a small problem with sub[i] sub-tiles and
+// cols[i] 128-column tiles (times its batches) takes tiles of min(cap, sub[i])
+// sub-tiles. cap is the smallest count at which the launch (large_tiles besides)
+// fits one round of workgroups on the device's CUs: more CUs stream each B, and
+// each reads fewer A rows. When no count fits, every tile takes all its
+// problem's rows, so each B byte is loaded once.
+int small_tile_cap(int64_t large_tiles, const int64_t* sub, const int64_t* cols, int n, int cus) {
+  for (int c = 1; c < kGsMaxM / 16; ++c) {
+    int64_t t = large_tiles;
+    for (int i = 0; i < n; ++i) t += mxh::cdiv(sub[i], c) * cols[i];
+    if (t <= cus) return c;
+  }
+  return kGsMaxM / 16;
+}
+
 // Verification dump of the grouped call: group g's block (its copies, codes
 // then scales, as for the single call) follows group g-1's.
 size_t grouped_dump_bytes_of(const mxfp4_group* groups, int G, int64_t N, int64_t K) {
@@ -1622,23 +1644,25 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
     if (st != MXFP4_OK) return st;
     a.g[g] = make_operand(q.A, q.lda, q.Bp, q.C, q.ldc, q.M, N, K);
   }
-  // A small group takes one tile of all its rows per 128 columns (each B byte
-  // loaded once), or 16-row tiles when the whole launch then still fits one
-  // round of workgroups on the device's CUs (more CUs streaming its B).
-  int64_t large_tiles = 0, small16 = 0;
+  // A small group's tiles: 16-row sub-tiles x 128 columns, as many sub-tiles
+  // per tile as small_tile_cap allows.
+  int64_t large_tiles = 0, sub[MXFP4_MAX_GROUPS], cols[MXFP4_MAX_GROUPS];
+  int nsmall = 0;
   for (int g = 0; g < G; ++g) {
     const int64_t M = groups[g].M;
-    if (M <= kGsMaxM)
-      small16 += mxh::cdiv(M, 16) * mxh::cdiv(N, 16 * kGsNB);
-    else
+    if (M <= kGsMaxM) {
+      sub[nsmall] = mxh::cdiv(M, 16);
+      cols[nsmall++] = mxh::cdiv(N, 16 * kGsNB);
+    } else {
       large_tiles += mxh::cdiv(M, kTBM) * ntn;
+    }
   }
-  bool rows16 = false;
-  if (small16 > 0) {
+  int64_t cap = kGsMaxM / 16;
+  if (nsmall > 0) {
     int cus = 0;
     const int st = device_cus(stream, &cus);
     if (st != MXFP4_OK) return st;
-    rows16 = large_tiles + small16 <= cus;
+    cap = small_tile_cap(large_tiles, sub, cols, nsmall, cus);
   }
   // Launch entries: the large groups in their order, then the small ones.
   int64_t total = 0;
@@ -1652,7 +1676,7 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
     for (int g = 0; g < G; ++g) {
       const int64_t M = groups[g].M;
       if ((M <= kGsMaxM) != (small != 0)) continue;
-      const int64_t mt = rows16 ? 1 : mxh::cdiv(M, 16);  // 16-row sub-tiles of a small tile
+      const int64_t mt = std::min(cap, mxh::cdiv(M, 16));  // 16-row sub-tiles of a small tile
       const int64_t rows = small ? mxh::cdiv(M, 16 * mt) : mxh::cdiv(M, kTBM);
       a.order[e] = g;
       a.rows[e] = (int)rows;
@@ -1719,7 +1743,8 @@ extern "C" int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void*
   if (G < 1) return MXFP4_ERR_TOO_MANY_GROUPS;
   MnkArgs a{};
   int P = 0;
-  int64_t large_tiles = 0, small16 = 0;
+  int64_t large_tiles = 0, sub[MXFP4_MAX_GROUPS], cols[MXFP4_MAX_GROUPS];
+  int nsmall = 0;
   for (int g = 0; g < G; ++g) {
     const mxfp4_group_mnk& q = groups[g];
     if (q.L < 1) return MXFP4_ERR_SHAPE;
@@ -1732,19 +1757,20 @@ extern "C" int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void*
       if (q.strideA < 0 || q.strideB < (int64_t)pg.total() || q.strideC < q.M * q.ldc) return MXFP4_ERR_SHAPE;
       if ((q.strideA * 2) % 16 != 0 || q.strideB % 16 != 0) return MXFP4_ERR_ALIGN;
     }
-    if (q.M <= kGsMaxM)
-      small16 += q.L * mxh::cdiv(q.M, 16) * mxh::cdiv(q.N, 16 * kGsNB);
-    else
+    if (q.M <= kGsMaxM) {
+      sub[nsmall] = mxh::cdiv(q.M, 16);
+      cols[nsmall++] = q.L * mxh::cdiv(q.N, 16 * kGsNB);
+    } else {
       large_tiles += q.L * mxh::cdiv(q.M, kTBM) * mxh::cdiv(q.N, kTBN);
+    }
   }
-  // Small problems: 16-row tiles when the launch then fits one round of
-  // workgroups on the device's CUs, else one tile of all rows per 128 columns.
-  bool rows16 = false;
-  if (small16 > 0) {
+  // Small problems: tiles of min(cap, M/16) 16-row sub-tiles x 128 columns.
+  int64_t cap = kGsMaxM / 16;
+  if (nsmall > 0) {
     int cus = 0;
     const int st = device_cus(stream, &cus);
     if (st != MXFP4_OK) return st;
-    rows16 = large_tiles + small16 <= cus;
+    cap = small_tile_cap(large_tiles, sub, cols, nsmall, cus);
   }
   P = 0;
   int64_t total = 0;
@@ -1757,7 +1783,7 @@ extern "C" int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void*
       const mxfp4_group_mnk& q = groups[g];
       if ((q.M <= kGsMaxM) != (small != 0)) continue;
       const mxh::PackedGeom pg(q.N, q.K);
-      const int64_t mt = small ? (rows16 ? 1 : mxh::cdiv(q.M, 16)) : 0;
+      const int64_t mt = small ? std::min(cap, mxh::cdiv(q.M, 16)) : 0;
       const int64_t rows = small ? mxh::cdiv(q.M, 16 * mt) : 0;
       const int64_t tiles =
           small ? rows * mxh::cdiv(q.N, 16 * kGsNB) : mxh::cdiv(q.M, kTBM) * mxh::cdiv(q.N, kTBN);

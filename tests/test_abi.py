@@ -219,9 +219,9 @@ def test_small_m_kernel_choice():
 
 
 def test_grouped_dump_layout():
-    """A group of at most 48 rows takes 128-column tiles (one dump copy each), a larger one 512-column tiles."""
+    """A group of at most 64 rows takes 128-column tiles (one dump copy each), a larger one 512-column tiles."""
     L = ops.lib()
-    assert [L.grouped_gemm_a4w4_dump_copies(M, 4096) for M in (1, 16, 48, 49, 128, 4096)] == [32, 32, 32, 8, 8, 8]
+    assert [L.grouped_gemm_a4w4_dump_copies(M, 4096) for M in (1, 16, 48, 64, 65, 128, 4096)] == [32, 32, 32, 32, 8, 8, 8]
     assert L.grouped_gemm_a4w4_dump_copies(16, 1000) == 8 and L.grouped_gemm_a4w4_dump_copies(100, 1000) == 2
     assert L.grouped_gemm_a4w4_dump_copies(0, 4096) == 0 and L.grouped_gemm_a4w4_dump_copies(16, 0) == 0
     g = (ops.Group * 3)()
@@ -229,7 +229,7 @@ def test_grouped_dump_layout():
     for i, M in enumerate(Ms):
         g[i] = ops.Group(P, K, P, P, N, M)
     want = sum(L.grouped_gemm_a4w4_dump_copies(M, N) * M * (K // 2 + K // 32) for M in Ms)
-    assert L.grouped_gemm_a4w4_dump_bytes(g, 3, N, K) == want == (8 * 16 + 2 * 200 + 2 * 64) * (416 + 26)
+    assert L.grouped_gemm_a4w4_dump_bytes(g, 3, N, K) == want == (8 * 16 + 2 * 200 + 8 * 64) * (416 + 26)
 
 
 def _mnk(**kw):

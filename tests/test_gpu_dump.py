@@ -92,11 +92,11 @@ def run_grouped(a_list, b_list, N, what):
 
 
 def test_fused_quant_bytes_grouped_small_and_large():
-    """Groups of at most 48 rows (16 x 128 tiles, one copy per 128 columns) beside larger ones (one copy
+    """Groups of at most 64 rows (16 x 128 tiles, one copy per 128 columns) beside larger ones (one copy
     per 512 columns), with M, N and K tails and zero blocks."""
     g = np.random.default_rng(21)
     N, K = 1000, 832
-    Ms = [1, 17, 48, 49, 200, 40]
+    Ms = [1, 17, 64, 65, 200, 40]
     a_list = []
     for m in Ms:
         a = synth.f32_to_bf16_bits((g.standard_normal((m, K)) * np.exp2(g.integers(-20, 20, (m, 1)))).astype(np.float32))
@@ -117,11 +117,22 @@ def test_fused_quant_bytes_grouped_more_tiles_than_cus():
     run_grouped(a_list, b_list, N, "264 tiles")
 
 
+def test_fused_quant_bytes_grouped_fewer_subtiles():
+    """Small groups in tiles of two 16-row sub-tiles (what fits one round of workgroups): the last row tile
+    of the 40- and 48-row groups has a sub-tile wholly past M, which must leave the dump untouched."""
+    g = np.random.default_rng(24)
+    N, K = 4096, 832
+    Ms = [48, 40, 64, 17]
+    a_list = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
+    b_list = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
+    run_grouped(a_list, b_list, N, "fewer sub-tiles")
+
+
 def test_fused_quant_bytes_grouped_small_subtiles():
     """Small groups in tiles of all their rows (more 16-row tiles than one round of workgroups), ragged."""
     g = np.random.default_rng(22)
     N, K = 8200, 832
-    Ms = [17, 33, 48, 5]
+    Ms = [17, 33, 48, 5, 57]
     a_list = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
     for a in a_list:
         a[-1, :32] = 0

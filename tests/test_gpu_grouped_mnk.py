@@ -4,7 +4,7 @@ count L, one launch; page 496271's problem form) with the CPU oracle, on an MI35
 Each batch's C must be within |C - C_ref| <= 2^-7 |C_ref| + 1e-3 max|C_ref| of
 the oracle's fp64 product of the dequantised operands rounded to bf16. Problems
 with M > 64 run the same tiled kernel as gemm_a4w4_fused, so there the bytes
-must also equal the single-problem call's. Problems of at most 48 rows take
+must also equal the single-problem call's. Problems of at most 64 rows take
 skinny tiles (K split over a workgroup's waves) in the same launch.
 """
 import numpy as np
@@ -46,12 +46,25 @@ def test_mixed_groups_match_oracle():
 
 
 def test_small_problems_beside_large_ones():
-    """Problems of at most 48 rows take skinny tiles (here one tile of all their rows per 128 columns: their
-    16-row tiles would not fit one round of workgroups) beside a large problem's tiled tiles: ragged N, a K
-    tail on odd K/64, batches."""
-    shapes = [(40, 4100, 1088, 3), (17, 2000, 832, 2), (300, 700, 1024, 1), (5, 4096, 512, 2), (48, 1000, 2048, 1)]
+    """Problems of at most 64 rows take skinny tiles beside a large problem's tiled tiles, here of at most
+    three 16-row sub-tiles (the fewest at which the launch fits one round of workgroups; the 64-row problem's
+    second row tile has two sub-tiles past M): ragged N, a K tail on odd K/64, batches."""
+    shapes = [(40, 4100, 1088, 3), (17, 2000, 832, 2), (300, 700, 1024, 1), (5, 4096, 512, 2), (48, 1000, 2048, 1), (64, 900, 704, 1)]
     say(f"[mnk] small and large {shapes}")
     groups = [make_group(gi, M, N, K, L, 35) for gi, (M, N, K, L) in enumerate(shapes)]
+    outs = ops.grouped_gemm_mnk([(A, Bp, N) for (_, _, A, Bp), (M, N, K, L) in zip(groups, shapes)])
+    torch.cuda.synchronize()
+    for (a_bits, bq, _, _), (M, N, K, L), C in zip(groups, shapes, outs):
+        for l in range(L):
+            assert_in_tolerance(bits_of(C[l]), oracle.gemm_ref(a_bits[l], *bq[l]), f"group M{M} N{N} K{K} l{l}")
+
+
+def test_small_problems_fewer_subtiles():
+    """Small problems only, whose 16-row tiles would need a second round of workgroups: tiles of two 16-row
+    sub-tiles, the 48-row problem's last one half past M; batches, odd K/64 tails."""
+    shapes = [(48, 4096, 832, 2), (64, 2048, 704, 1), (17, 4096, 512, 1)]
+    say(f"[mnk] capped sub-tiles {shapes}")
+    groups = [make_group(gi, M, N, K, L, 37) for gi, (M, N, K, L) in enumerate(shapes)]
     outs = ops.grouped_gemm_mnk([(A, Bp, N) for (_, _, A, Bp), (M, N, K, L) in zip(groups, shapes)])
     torch.cuda.synchronize()
     for (a_bits, bq, _, _), (M, N, K, L), C in zip(groups, shapes, outs):

@@ -355,14 +355,30 @@ def test_grouped_ragged_small():
 
 
 def test_grouped_small_groups_mixed():
-    """Groups of at most 48 rows take 16 x 128 tiles over the whole K (K split over the workgroup's waves),
-    larger ones 128 x 512 tiles, in one launch: M tails (1, 17, 33, 63), the boundary (48 / 49), N not a
+    """Groups of at most 64 rows take 16 x 128 tiles over the whole K (K split over the workgroup's waves),
+    larger ones 128 x 512 tiles, in one launch: M tails (1, 17, 33, 63), the boundary (64 / 65), N not a
     multiple of 128 or 512, and a K tail on odd K/64. 26 large tiles (their id range padded to 32 with
-    idle workgroups) ahead of 80 small ones."""
+    idle workgroups) ahead of 120 small ones."""
     say("grouped small groups mixed with large ones")
     g = np.random.default_rng(12)
     N, K = 1000, 832
-    Ms = [1, 16, 17, 48, 49, 300, 33, 63, 1024]
+    Ms = [1, 16, 17, 64, 65, 300, 33, 63, 1024, 100]
+    a = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
+    b = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
+    qs = [oracle.quant_mx(x) for x in b]
+    cs = ops.grouped_gemm([to_dev_bf16(x) for x in a], [packed_b(*q) for q in qs], N)
+    torch.cuda.synchronize()
+    for x, (bq, bs), c in zip(a, qs, cs):
+        assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
+
+
+# Small groups whose tiles of all rows would leave CUs idle while 16-row tiles would need a second round:
+# the launch takes tiles of two (first case) or three (second) 16-row sub-tiles, so the last row tile of a
+# 40-, 48- or 64-row group has sub-tiles wholly past its M (no loads, no stores). Odd K/64 tails.
+@pytest.mark.parametrize("Ms,N,K", [([48, 40, 64, 17], 4096, 832), ([64, 48, 48, 48, 48], 4096, 352)])
+def test_grouped_small_tiles_fewer_subtiles(Ms, N, K):
+    say(f"grouped capped sub-tiles Ms={Ms} N={N} K={K}")
+    g = np.random.default_rng(14)
     a = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
     b = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
     qs = [oracle.quant_mx(x) for x in b]
@@ -374,12 +390,12 @@ def test_grouped_small_groups_mixed():
 
 def test_grouped_small_subtiles_ragged():
     """Small groups whose 16-row tiles would not fit one round of workgroups take one tile of all their
-    rows (one to three 16-row sub-tiles sharing each B load): M 5, 17, 33, 48, N with a tail of 8 columns
+    rows (one to four 16-row sub-tiles sharing each B load): M 5, 17, 33, 48, 57, 64, N with a tail of 8 columns
     past the last 128, K with a tail on odd K/64."""
     say("grouped small groups, multi-row tiles")
     g = np.random.default_rng(13)
     N, K = 8200, 832
-    Ms = [17, 33, 48, 5]
+    Ms = [17, 33, 48, 5, 57, 64]
     a = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
     b = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
     qs = [oracle.quant_mx(x) for x in b]
