@@ -60,10 +60,10 @@ def alg_flops(M, N, K):
     return 2 * M * N * K
 
 
-WORKLOADS = ["tiny", "skinny", "stress", "square", "grouped", "grouped_decode", "rmsnorm", "grouped_mnk", "skinny_shard8",
-             "nvfp4_grouped"]
+WORKLOADS = ["tiny", "skinny", "stress", "square", "grouped", "grouped_decode", "mid", "rmsnorm", "grouped_mnk",
+             "skinny_shard8", "nvfp4_grouped"]
 HEADLINE = "square"                       # the largest single-GPU configuration the metric spans
-EXTRAS = ["skinny", "stress", "tiny", "grouped", "grouped_decode"]
+EXTRAS = ["skinny", "stress", "tiny", "grouped", "grouped_decode", "mid"]
 
 
 def parse():
@@ -72,7 +72,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=None, choices=WORKLOADS,
-                   help="time one workload only (default: the square headline plus skinny, stress, tiny and grouped "
+                   help="time one workload only (default: the square headline plus skinny, stress, tiny, grouped, "
+                        "grouped_decode and mid "
                         "as extra keys of the same line). rmsnorm times mxfp4_rmsnorm_quant at M4096 K7168; "
                         "grouped_mnk times grouped_gemm_a4w4_mnk on seeded groups with their own (M, N, K, L)")
     p.add_argument("--seed", type=int, default=None)

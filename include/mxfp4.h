@@ -149,10 +149,34 @@ int mxfp4_pack_B(const void* bq, const void* bs, int64_t N, int64_t K, void* out
  *        workgroup (faster there, no workspace used); the size above is
  *        always enough. Larger M needs none. Too small or NULL when needed:
  *        MXFP4_ERR_WORKSPACE; not 256-byte aligned: MXFP4_ERR_ALIGN.
+ *   The kernel follows from (M, N, K) alone (gemm_a4w4_fused_path): for
+ *   M <= 16 the split-K or the skinny kernel, for 16 < M <= 64 the skinny
+ *   kernel, for larger M the tiled kernel (128 x 512 tiles), or, where that
+ *   would leave most CUs idle (M up to a few hundred rows), the skinny kernel
+ *   or the grouped kernel's skinny tiles.
  * ------------------------------------------------------------------------- */
 size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K);
 int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc, int64_t M,
                     int64_t N, int64_t K, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * gemm_a4w4_fused_path -- the kernel that gemm_a4w4_fused (and its _noalloc
+ * and _dump forms) runs for a shape: a pure function of (M, N, K), computed on
+ * the host without a GPU. MXFP4_PATH_SPLITK: K split over workgroups (M <= 16).
+ * MXFP4_PATH_SKINNY: MS rows x 16*NB columns per 1024-thread workgroup, K split
+ * over its 16 waves. MXFP4_PATH_SKINNY_TILES: the skinny tiles that
+ * grouped_gemm_a4w4 gives small groups (16 to 64 rows x 128 columns, K split
+ * over 8 waves), for M > 64. MXFP4_PATH_TILED: 128 x 512 tiles. 0 for a shape
+ * the call rejects (as MXFP4_ERR_SHAPE). Calls that run the same kernel on the
+ * same operands give bit-identical C; gemm_a4w4 runs the split-K kernel for
+ * M <= 16 and the tiled kernel otherwise. Not an operation of the pages: a
+ * query for callers and tests.
+ * ------------------------------------------------------------------------- */
+#define MXFP4_PATH_SPLITK 1
+#define MXFP4_PATH_SKINNY 2
+#define MXFP4_PATH_SKINNY_TILES 3
+#define MXFP4_PATH_TILED 4
+int gemm_a4w4_fused_path(int64_t M, int64_t N, int64_t K);
 
 /* ---------------------------------------------------------------------------
  * gemm_a4w4_fused_noalloc -- gemm_a4w4_fused without a workspace argument and

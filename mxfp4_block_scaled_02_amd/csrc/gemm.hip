@@ -151,6 +151,14 @@ __device__ __forceinline__ AWindow a_window(const Operand& p, int K, int m0) {
   return w;
 }
 
+// A bijection on [0, G) giving each of the 8 XCDs (workgroup id mod 8) a
+// contiguous run of tiles, so the tiles sharing an L2 share A rows / B columns.
+__device__ __forceinline__ int xcd_remap(int id, int G) {
+  const int full = G & ~7;
+  if (id >= full) return id;
+  return (id & 7) * (full >> 3) + (id >> 3);
+}
+
 // ---------------------------------------------------------------------------
 // Skinny kernel
 // ---------------------------------------------------------------------------
@@ -204,10 +212,17 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
 
   // Per-lane constants. A piece h: row 4h + l/16 of the tile, 8 elements at
   // 8*(l%16) of the K step (a wave pass covers 4 whole rows: coalesced).
+  // Piece h's offset is aoff0 + h * arow4 (arow4: 4 rows of A, uniform). Up to
+  // 48 rows the offsets are kept per piece; at 64 rows they are formed at each
+  // load instead (15 fewer VGPRs, which keeps the 64-row tile within 256), and
+  // the B offsets below are kept per column parity rather than per column.
+  constexpr bool kStepOffsets = PIECES > 12;
   const AWindow aw = a_window(p, d.K, m0);
-  uint32_t aoff[PIECES];
+  const uint32_t aoff0 = (uint32_t)(((l >> 4) * p.lda + 8 * (l & 15)) * 2);
+  const uint32_t arow4 = (uint32_t)(p.lda * 8);
+  uint32_t aoff[kStepOffsets ? 1 : PIECES];
 #pragma unroll
-  for (int h = 0; h < PIECES; ++h) aoff[h] = (uint32_t)(((4 * h + (l >> 4)) * p.lda + 8 * (l & 15)) * 2);
+  for (int h = 0; h < (kStepOffsets ? 1 : PIECES); ++h) aoff[h] = aoff0 + (uint32_t)h * arow4;
   // LDS dword this lane writes for piece h, and the operand slot it reads.
   const int chunk = (l & 15) >> 2, sub = l & 3;
   int wslot[PIECES];
@@ -216,25 +231,30 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
   const int aslot = slot16(l & 15, l >> 4);
   // B operand of 16-column tile T at step j: lane l reads unit 2j + (l/16)/2 of
   // packed tile T/2 at unit lane ((l/16)%2)*32 + 16*(T%2) + l%16.
+  // The unit lane depends on t only through the parity of T0 + t: at 64 rows
+  // boff[0] and boff[1] hold the offsets of even and odd t (likewise soff for
+  // the scales); otherwise one per column tile t.
   const int s16 = l >> 4;
-  uint32_t boff[NB];
+  constexpr int kNBoff = kStepOffsets ? 2 : NB;
+  uint32_t boff[kNBoff], soff[kNBoff];
 #pragma unroll
-  for (int t = 0; t < NB; ++t)
-    boff[t] = (uint32_t)((s16 >> 1) * 1024 + (((s16 & 1) * 32 + ((T0 + t) & 1) * 16 + (l & 15)) * 16));
+  for (int q = 0; q < kNBoff; ++q) {
+    const int odd = (T0 + q) & 1;
+    boff[q] = (uint32_t)((s16 >> 1) * 1024 + (((s16 & 1) * 32 + odd * 16 + (l & 15)) * 16));
+    soff[q] = (uint32_t)(((s16 & 1) * 32 + odd * 16 + (l & 15)) * 4);
+  }
   const int tail_k = d.K - 128 * (d.KT - 1);  // valid elements in the last K step
 
   // Resources built once: A rows of the tile, and per 16-column tile its packed
   // 32-column tile's code units and scale dwords (empty past the packed N).
   const __amdgpu_buffer_rsrc_t ar = aw.at(0);
   __amdgpu_buffer_rsrc_t brs[NB], bss[NB];
-  uint32_t soff[NB];
 #pragma unroll
   for (int t = 0; t < NB; ++t) {
     const int t32 = (T0 + t) >> 1;
     const bool ok = t32 < d.NT32;
     brs[t] = make_rsrc(p.Bunit + (int64_t)t32 * d.KU * 1024, ok ? (int64_t)d.KU * 1024 : 0);
     bss[t] = make_rsrc(p.Bscale + (int64_t)t32 * d.KG * 64, ok ? (int64_t)d.KG * 256 : 0);
-    soff[t] = (uint32_t)(((s16 & 1) * 32 + ((T0 + t) & 1) * 16 + (l & 15)) * 4);
   }
   const bool hi_unit = (s16 >> 1) != 0;  // lanes 32..63 read the step's second unit
 
@@ -250,15 +270,22 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
           if (!last_odd) {
-            bq[s][t] = bload16_nt(brs[t], boff[t], (uint32_t)j * 2048);  // read by the M/16 row-block workgroups
+            bq[s][t] = bload16_nt(brs[t], boff[t % kNBoff], (uint32_t)j * 2048);  // read by the M/16 row-block workgroups
           } else {
             bq[s][t] = make_uint4(0u, 0u, 0u, 0u);
-            if (!hi_unit) bq[s][t] = bload16_nt(brs[t], boff[t], (uint32_t)j * 2048);
+            if (!hi_unit) bq[s][t] = bload16_nt(brs[t], boff[t % kNBoff], (uint32_t)j * 2048);
           }
-          bs[s][t] = bload4(bss[t], soff[t], (uint32_t)(j >> 1) * 256);
+          bs[s][t] = bload4(bss[t], soff[t % kNBoff], (uint32_t)(j >> 1) * 256);
         }
+        if constexpr (kStepOffsets) {
+          uint32_t ao = aoff0;
+          asm volatile("" : "+v"(ao));  // per step: the compiler does not keep PIECES offsets live
 #pragma unroll
-        for (int h = 0; h < PIECES; ++h) to_words(bload16(ar, aoff[h], (uint32_t)j * 256), w[s][h]);
+          for (int h = 0; h < PIECES; ++h) to_words(bload16(ar, ao + (uint32_t)h * arow4, (uint32_t)j * 256), w[s][h]);
+        } else {
+#pragma unroll
+          for (int h = 0; h < PIECES; ++h) to_words(bload16(ar, aoff[h], (uint32_t)j * 256), w[s][h]);
+        }
       }
     }
 #pragma unroll
@@ -314,10 +341,15 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
   }
 }
 
+// A 1-D grid of column tiles x `rows` row tiles: workgroup id v (after the XCD
+// remap) is column tile v / rows and row tile v % rows, so the row tiles of a
+// column tile are adjacent and read its B through one XCD's L2.
 template <int MS, int NB, int PF, bool DUMP>
-__global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, Dims d) {
+__global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, Dims d, int rows) {
   __shared__ __align__(16) SkinnySmem<kSkWaves, NB> sm;
-  skinny_tile<kSkWaves, MS, NB, PF, DUMP>(p, d, blockIdx.y * MS, blockIdx.x * NB, blockIdx.x, sm);
+  const int v = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  const int c = v / rows, r = v - c * rows;
+  skinny_tile<kSkWaves, MS, NB, PF, DUMP>(p, d, r * MS, c * NB, c, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -546,13 +578,6 @@ __global__ __launch_bounds__(kSpT) void gemm_splitk_kernel(Operand p, Dims d, Sp
 // 128 rows x columns [64w, 64w+64) with 4 x 2 32x32x64 accumulators.
 constexpr int kTBM = 128, kTBN = 512, kTThreads = 512, kTWaves = kTThreads / 64;
 
-// A bijection on [0, G) giving each of the 8 XCDs (workgroup id mod 8) a
-// contiguous run of tiles, so the tiles sharing an L2 share A rows / B columns.
-__device__ __forceinline__ int xcd_remap(int id, int G) {
-  const int full = G & ~7;
-  if (id >= full) return id;
-  return (id & 7) * (full >> 3) + (id >> 3);
-}
 
 // 16-byte LDS slot, within one 32x64 operand block, of unit lane `lane`
 // (row lane%32, chunk lane/32) at 64-k half `ks` of a 128-k step; the XOR with the
@@ -1284,11 +1309,12 @@ template <int MS, int NB, int PF>
 hipError_t launch_skinny(const Operand& o, const Dims& d, int64_t M, bool dump, hipStream_t st) {
   Operand op = o;
   Dims dd = d;
-  void* args[] = {&op, &dd};
-  const dim3 grid((unsigned)mxh::cdiv(mxh::cdiv(d.N, 16), NB), (unsigned)mxh::cdiv(M, MS));
+  int rows = (int)mxh::cdiv(M, MS);
+  void* args[] = {&op, &dd, &rows};
+  const int64_t grid = mxh::cdiv(mxh::cdiv(d.N, 16), NB) * rows;
   return hipLaunchKernel(dump ? (const void*)gemm_skinny_kernel<MS, NB, PF, true>
                               : (const void*)gemm_skinny_kernel<MS, NB, PF, false>,
-                         grid, dim3(kSkWaves * 64), args, 0, st);
+                         dim3((unsigned)grid), dim3(kSkWaves * 64), args, 0, st);
 }
 
 // Skinny tile shape (rows MS x 16*NB columns per workgroup). Every workgroup
@@ -1407,8 +1433,68 @@ hipError_t launch_tiled(const Operand& o, const Dims& d, int64_t M, int64_t N, b
   return hipLaunchKernel(k, dim3((unsigned)tiles), dim3(kTThreads), args, 0, st);
 }
 
+// 16-row sub-tiles per small tile of the grouped kernel: a small problem with
+// sub[i] sub-tiles and cols[i] 128-column tiles (times its batches) takes tiles
+// of min(cap, sub[i]) sub-tiles. cap is the smallest count at which the launch
+// (large_tiles besides) fits one round of workgroups on the device's CUs: more
+// CUs stream each B, and each reads fewer A rows. When no count fits, every
+// tile takes four sub-tiles (all rows of a group of at most 64), so fewer
+// workgroups load each B byte.
+int small_tile_cap(int64_t large_tiles, const int64_t* sub, const int64_t* cols, int n, int cus) {
+  for (int c = 1; c < kGsMaxM / 16; ++c) {
+    int64_t t = large_tiles;
+    for (int i = 0; i < n; ++i) t += mxh::cdiv(sub[i], c) * cols[i];
+    if (t <= cus) return c;
+  }
+  return kGsMaxM / 16;
+}
+
+// Kernel of the single fused call for M > 64. The 128 x 512 tiled tile loads
+// the fewest bytes per output, but a problem of a few hundred rows has few of
+// them (M = 128, N = 4096: 8 tiles for 256 CUs), each bound by one CU's load
+// rate. Skinny tiles spread such a problem over all CUs. Each option is
+// estimated as rounds of workgroups on kModelCUs CUs, each round a fixed cost
+// plus one workgroup's bytes (its bf16 A rows and packed B columns over the
+// whole K) at one CU's rate, fitted to measurements at M 65..1024,
+// N 1024..7168, K 1024..7168 (cold operands, graph replay):
+//   tiled kernel (8 waves, 128 x 512)                  9.0 us + bytes / 70.4 KB/us
+//   skinny kernel (16 waves, choose_skinny's tile)     3.2 us + bytes / 55.6 KB/us
+//   grouped kernel's skinny tiles (8 waves, mt 16-row
+//     sub-tiles x 128 columns, small_tile_cap's mt)    5.0 us + bytes / 53.0 KB/us
+// The tiled kernel stays unless another is estimated at least 15 % faster. The
+// model counts the MI355X's 256 CUs whatever the device, so the choice (and
+// with it the verification dump's layout) depends on M, N and K alone.
+enum class MidPath { kTiled, kSkinny, kRows };
+constexpr int kModelCUs = 256;
+constexpr int64_t kMidMaxM = 4096;  // larger M always takes the tiled kernel
+MidPath mid_path(int64_t M, int64_t N, int64_t K) {
+  if (M <= 64 || M > kMidMaxM) return MidPath::kTiled;
+  const double kd = (double)K, bcol = kd * 17.0 / 32.0;  // packed B bytes per column
+  const auto rounds = [](int64_t wgs) { return (double)mxh::cdiv(wgs, kModelCUs); };
+  const double t_tiled =
+      rounds(mxh::cdiv(M, kTBM) * mxh::cdiv(N, kTBN)) * (9.0 + (2.0 * kTBM * kd + kTBN * bcol) / 70.4e3);
+  const SkinnyShape sh = choose_skinny(M, N, K);
+  const double t_sk = rounds(mxh::cdiv(mxh::cdiv(N, 16), sh.NB) * mxh::cdiv(M, sh.MS)) *
+                      (3.2 + (2.0 * sh.MS * kd + 16.0 * sh.NB * bcol) / 55.6e3);
+  const int64_t sub = mxh::cdiv(M, 16), cols = mxh::cdiv(N, 16 * kGsNB);
+  const int64_t mt = std::min<int64_t>(small_tile_cap(0, &sub, &cols, 1, kModelCUs), sub);
+  const double t_rows =
+      rounds(mxh::cdiv(M, 16 * mt) * cols) * (5.0 + (32.0 * mt * kd + 16.0 * kGsNB * bcol) / 53.0e3);
+  MidPath best = MidPath::kTiled;
+  double t = 0.85 * t_tiled;
+  if (t_sk < t) {
+    t = t_sk;
+    best = MidPath::kSkinny;
+  }
+  if (t_rows < t) best = MidPath::kRows;
+  return best;
+}
+
+int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* dump, size_t dump_bytes, void* stream,
+                 int64_t small_max);
+
 hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, int64_t K, bool dump, hipStream_t st) {
-  if (M <= 64) {
+  if (M <= 64 || mid_path(M, N, K) == MidPath::kSkinny) {
     const SkinnyShape sh = choose_skinny(M, N, K);
     switch (sh.MS * 16 + sh.NB) {
       case 4 * 16 + 1: return launch_skinny<4, 1, 4>(o, d, M, dump, st);
@@ -1431,7 +1517,9 @@ hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, in
 int64_t dump_copies(int64_t M, int64_t N, int64_t K) {
   const SplitGeom g = split_geom(M, N, K);
   if (fused_splitk(M, N, K, g)) return g.T;
-  if (M <= 64) return mxh::cdiv(mxh::cdiv(N, 16), choose_skinny(M, N, K).NB);
+  const MidPath mp = mid_path(M, N, K);
+  if (M <= 64 || mp == MidPath::kSkinny) return mxh::cdiv(mxh::cdiv(N, 16), choose_skinny(M, N, K).NB);
+  if (mp == MidPath::kRows) return mxh::cdiv(N, 16 * kGsNB);
   return mxh::cdiv(N, kTBN);
 }
 size_t dump_bytes_of(int64_t M, int64_t N, int64_t K) {
@@ -1439,6 +1527,19 @@ size_t dump_bytes_of(int64_t M, int64_t N, int64_t K) {
 }
 
 }  // namespace
+
+extern "C" int gemm_a4w4_fused_path(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || M > mxh::kMaxDim || N > mxh::kMaxDim || K > mxh::kMaxDim) return 0;
+  if (!offsets_fit(K, K)) return 0;  // rejected even with the smallest lda
+  const SplitGeom g = split_geom(M, N, K);
+  if (fused_splitk(M, N, K, g)) return MXFP4_PATH_SPLITK;
+  if (M <= 64) return MXFP4_PATH_SKINNY;
+  switch (mid_path(M, N, K)) {
+    case MidPath::kSkinny: return MXFP4_PATH_SKINNY;
+    case MidPath::kRows: return MXFP4_PATH_SKINNY_TILES;
+    default: return MXFP4_PATH_TILED;
+  }
+}
 
 extern "C" size_t gemm_a4w4_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || N < 1 || K < 32 || K % 32 != 0 || M > mxh::kMaxDim || N > mxh::kMaxDim || K > mxh::kMaxDim) return 0;
@@ -1454,6 +1555,10 @@ int fused_call(const void* A, int64_t lda, const void* Bp, void* C, int64_t ldc,
   const int st = check_problem(A, lda, Bp, C, ldc, M, N, K);
   if (st != MXFP4_OK) return st;
   if (mxh::cdiv(M, kTBM) * mxh::cdiv(N, kTBN) > INT32_MAX) return MXFP4_ERR_SHAPE;
+  if (mid_path(M, N, K) == MidPath::kRows) {  // one small group of the grouped kernel
+    const mxfp4_group g{A, lda, Bp, C, ldc, M};
+    return grouped_call(&g, 1, N, K, dump, dump_bytes, stream, M);
+  }
   Operand o = make_operand(A, lda, Bp, C, ldc, M, N, K);
   if (dump) {
     if (dump_bytes < dump_bytes_of(M, N, K)) return MXFP4_ERR_BUFFER;
@@ -1608,32 +1713,23 @@ extern "C" size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, i
 namespace {
 // Copies of a group's quantised A in the verification dump: one per column tile
 // of the tile kind the group takes.
-int64_t grouped_copies(int64_t M, int64_t N) { return M <= kGsMaxM ? mxh::cdiv(N, 16 * kGsNB) : mxh::cdiv(N, kTBN); }
-
-// 16-row sub-tiles per small tile: a small problem with sub[i] sub-tiles and
-// cols[i] 128-column tiles (times its batches) takes tiles of min(cap, sub[i])
-// sub-tiles. cap is the smallest count at which the launch (large_tiles besides)
-// fits one round of workgroups on the device's CUs: more CUs stream each B, and
-// each reads fewer A rows. When no count fits, every tile takes all its
-// problem's rows, so each B byte is loaded once.
-int small_tile_cap(int64_t large_tiles, const int64_t* sub, const int64_t* cols, int n, int cus) {
-  for (int c = 1; c < kGsMaxM / 16; ++c) {
-    int64_t t = large_tiles;
-    for (int i = 0; i < n; ++i) t += mxh::cdiv(sub[i], c) * cols[i];
-    if (t <= cus) return c;
-  }
-  return kGsMaxM / 16;
+int64_t grouped_copies(int64_t M, int64_t N, int64_t small_max = kGsMaxM) {
+  return M <= small_max ? mxh::cdiv(N, 16 * kGsNB) : mxh::cdiv(N, kTBN);
 }
 
 // Verification dump of the grouped call: group g's block (its copies, codes
 // then scales, as for the single call) follows group g-1's.
-size_t grouped_dump_bytes_of(const mxfp4_group* groups, int G, int64_t N, int64_t K) {
+size_t grouped_dump_bytes_of(const mxfp4_group* groups, int G, int64_t N, int64_t K, int64_t small_max = kGsMaxM) {
   size_t t = 0;
-  for (int g = 0; g < G; ++g) t += (size_t)(grouped_copies(groups[g].M, N) * groups[g].M * (K / 2 + K / 32));
+  for (int g = 0; g < G; ++g)
+    t += (size_t)(grouped_copies(groups[g].M, N, small_max) * groups[g].M * (K / 2 + K / 32));
   return t;
 }
 
-int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* dump, size_t dump_bytes, void* stream) {
+// Groups of at most small_max rows take skinny tiles (kGsMaxM for the grouped
+// calls; the single fused call routes one group of any M here).
+int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* dump, size_t dump_bytes, void* stream,
+                 int64_t small_max) {
   if (!groups) return MXFP4_ERR_NULL;
   if (G < 1 || G > MXFP4_MAX_GROUPS) return MXFP4_ERR_TOO_MANY_GROUPS;
   GroupedArgs a{};
@@ -1650,7 +1746,7 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
   int nsmall = 0;
   for (int g = 0; g < G; ++g) {
     const int64_t M = groups[g].M;
-    if (M <= kGsMaxM) {
+    if (M <= small_max) {
       sub[nsmall] = mxh::cdiv(M, 16);
       cols[nsmall++] = mxh::cdiv(N, 16 * kGsNB);
     } else {
@@ -1675,7 +1771,7 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
     }
     for (int g = 0; g < G; ++g) {
       const int64_t M = groups[g].M;
-      if ((M <= kGsMaxM) != (small != 0)) continue;
+      if ((M <= small_max) != (small != 0)) continue;
       const int64_t mt = std::min(cap, mxh::cdiv(M, 16));  // 16-row sub-tiles of a small tile
       const int64_t rows = small ? mxh::cdiv(M, 16 * mt) : mxh::cdiv(M, kTBM);
       a.order[e] = g;
@@ -1688,11 +1784,11 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
     }
   }
   if (dump) {
-    if (dump_bytes < grouped_dump_bytes_of(groups, G, N, K)) return MXFP4_ERR_BUFFER;
+    if (dump_bytes < grouped_dump_bytes_of(groups, G, N, K, small_max)) return MXFP4_ERR_BUFFER;
     if (!mxh::aligned(dump, 16)) return MXFP4_ERR_ALIGN;
     uint8_t* at = (uint8_t*)dump;
     for (int g = 0; g < G; ++g) {
-      const int64_t copies = grouped_copies(groups[g].M, N);
+      const int64_t copies = grouped_copies(groups[g].M, N, small_max);
       a.g[g].dq = at;
       a.g[g].ds = at + copies * groups[g].M * (K / 2);
       at += copies * groups[g].M * (K / 2 + K / 32);
@@ -1715,7 +1811,7 @@ extern "C" int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, in
                                  size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  return grouped_call(groups, G, N, K, nullptr, 0, stream);
+  return grouped_call(groups, G, N, K, nullptr, 0, stream, kGsMaxM);
 }
 
 extern "C" size_t grouped_gemm_a4w4_dump_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K) {
@@ -1735,7 +1831,7 @@ extern "C" int grouped_gemm_a4w4_dump(const mxfp4_group* groups, int G, int64_t 
   (void)workspace;
   (void)workspace_bytes;
   if (!dump) return MXFP4_ERR_NULL;
-  return grouped_call(groups, G, N, K, dump, dump_bytes, stream);
+  return grouped_call(groups, G, N, K, dump, dump_bytes, stream, kGsMaxM);
 }
 
 extern "C" int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void* stream) {

@@ -23,7 +23,8 @@ MXFP4_MAX_GROUPS = 32
 STATUS = {0: "MXFP4_OK", 1: "MXFP4_ERR_NULL", 2: "MXFP4_ERR_SHAPE", 3: "MXFP4_ERR_ALIGN", 4: "MXFP4_ERR_WORKSPACE",
           5: "MXFP4_ERR_TOO_MANY_GROUPS", 6: "MXFP4_ERR_HIP", 7: "MXFP4_ERR_BUFFER", 8: "MXFP4_ERR_ARG"}
 EXPORTED = ["mxfp4_status_str", "mxfp4_quant", "mxfp4_rmsnorm_quant", "mxfp4_pack_B_bytes", "mxfp4_pack_B",
-            "gemm_a4w4_workspace_bytes", "gemm_a4w4_fused", "gemm_a4w4_fused_noalloc", "gemm_a4w4_fused_dump_bytes",
+            "gemm_a4w4_workspace_bytes", "gemm_a4w4_fused", "gemm_a4w4_fused_path", "gemm_a4w4_fused_noalloc",
+            "gemm_a4w4_fused_dump_bytes",
             "gemm_a4w4_fused_dump",
             "gemm_a4w4", "grouped_gemm_a4w4_workspace_bytes", "grouped_gemm_a4w4", "grouped_gemm_a4w4_dump_bytes",
             "grouped_gemm_a4w4_dump_copies", "grouped_gemm_a4w4_dump", "grouped_gemm_a4w4_mnk", "grouped_gemm_nvfp4"]
@@ -80,6 +81,7 @@ def lib() -> ctypes.CDLL:
         L.gemm_a4w4_workspace_bytes.argtypes, L.gemm_a4w4_workspace_bytes.restype = [i64, i64, i64], sz
         L.gemm_a4w4_fused.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp]
         L.gemm_a4w4_fused.restype = i32
+        L.gemm_a4w4_fused_path.argtypes, L.gemm_a4w4_fused_path.restype = [i64, i64, i64], i32
         L.gemm_a4w4_fused_noalloc.argtypes = [vp, i64, vp, vp, i64, i64, i64, i64, vp]
         L.gemm_a4w4_fused_noalloc.restype = i32
         L.gemm_a4w4_fused_dump_bytes.argtypes, L.gemm_a4w4_fused_dump_bytes.restype = [i64, i64, i64], sz
@@ -197,6 +199,18 @@ def pack_B(bq: torch.Tensor, bs: torch.Tensor) -> torch.Tensor:
     _check(lib().mxfp4_pack_B(bq.data_ptr(), bs.data_ptr(), N, K, out.data_ptr(), out.numel(), _stream(bq)),
            "mxfp4_pack_B")
     return out
+
+
+PATHS = {1: "splitk", 2: "skinny", 3: "skinny_tiles", 4: "tiled"}
+
+
+def fused_path(M: int, N: int, K: int) -> str:
+    """Name of the kernel gemm_a4w4_fused runs for (M, N, K) ("splitk", "skinny", "skinny_tiles", "tiled");
+    raises for a shape the call rejects."""
+    p = int(lib().gemm_a4w4_fused_path(M, N, K))
+    if p not in PATHS:
+        raise ValueError(f"gemm_a4w4_fused rejects M={M} N={N} K={K}")
+    return PATHS[p]
 
 
 def gemm(a: torch.Tensor, bp: torch.Tensor, N: int, out: torch.Tensor | None = None) -> torch.Tensor:

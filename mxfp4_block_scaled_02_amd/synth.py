@@ -24,6 +24,8 @@ kernelbot nvfp4-group-gemm submission 496271):
   grouped_decode  the grouped form with decode-sized groups: 8 groups sharing
            N=4096, K=7168, M_g = 8*U{1..8} (each group's B read for a few rows,
            the case where a group of the list is HBM-bound)
+  mid      M=256  N=4096  K=7168   the top of the M 4..256 regime; A ~ N(0,1),
+                                   B ~ N(0, 0.02)
 
 Every tensor draws from its own stream:
 numpy PCG64(SeedSequence([seed, stream, *sub])). Streams: 0 = A, 1 = B,
@@ -41,8 +43,9 @@ WORKLOADS = {
     "grouped": dict(G=8, N=4096, K=7168),
     "skinny_shard8": dict(M=16, N=264, K=7168),
     "grouped_decode": dict(G=8, N=4096, K=7168),
+    "mid": dict(M=256, N=4096, K=7168),
 }
-WORKLOAD_ORDER = ["tiny", "skinny", "stress", "square", "grouped", "grouped_decode"]
+WORKLOAD_ORDER = ["tiny", "skinny", "stress", "square", "grouped", "grouped_decode", "mid"]
 GROUPED = ("grouped", "grouped_decode")
 SHARD_OF = {"skinny_shard8": "skinny"}  # a shard draws from its parent's seed
 

@@ -218,6 +218,30 @@ def test_small_m_kernel_choice():
     assert L.gemm_a4w4_workspace_bytes(1, 4096, 7168) > 0
 
 
+def test_fused_kernel_choice_mid_m():
+    """Past 64 rows the fused call keeps the tiled kernel unless its cost model estimates the skinny kernel or
+    the grouped kernel's skinny tiles at least 15 % faster: a few hundred rows leave most 128 x 512 tiles'
+    CUs idle. The choice depends on (M, N, K) alone, and the verification dump's size follows it (one copy
+    per 128 columns for the skinny tiles, per 512 for the tiled kernel)."""
+    L = ops.lib()
+    row = lambda K: K // 2 + K // 32
+    want = {(16, 2112, 7168): "splitk", (1, 4096, 7168): "skinny", (64, 7168, 2048): "skinny",
+            (65, 4096, 7168): "skinny", (128, 4096, 7168): "skinny", (128, 1024, 4096): "skinny",
+            (192, 4096, 7168): "skinny_tiles", (512, 4096, 7168): "skinny_tiles", (256, 7168, 2048): "skinny_tiles",
+            (512, 2112, 7168): "skinny_tiles",
+            (768, 4096, 7168): "tiled", (4096, 4096, 7168): "tiled", (512, 7168, 2048): "tiled",
+            (5000, 4096, 7168): "tiled"}
+    for (M, N, K), path in want.items():
+        assert ops.fused_path(M, N, K) == path, (M, N, K)
+        if M > 64 and path != "skinny":
+            per = 128 if path == "skinny_tiles" else 512
+            assert L.gemm_a4w4_fused_dump_bytes(M, N, K) == cdiv(N, per) * M * row(K), (M, N, K)
+    for M, N, K in [(0, 16, 32), (16, 0, 32), (16, 16, 48), (16, 16, 0)]:
+        assert L.gemm_a4w4_fused_path(M, N, K) == 0
+        with pytest.raises(ValueError):
+            ops.fused_path(M, N, K)
+
+
 def test_grouped_dump_layout():
     """A group of at most 64 rows takes 128-column tiles (one dump copy each), a larger one 512-column tiles."""
     L = ops.lib()

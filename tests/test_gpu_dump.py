@@ -9,7 +9,8 @@ the GEMM an all-zero block gets scale byte 0 instead of 127 (its codes are zero,
 so every product is zero under either scale). Which blocks are all-zero is read
 from the input, not from the kernel's output. C must equal the production
 call's C bit for bit (same arithmetic). Covers the split-K kernel (tiny, skinny),
-the skinny kernel (stress), the tiled kernel (square) and the grouped kernel
+the skinny kernel (stress, and mid-size M), the tiled kernel (square), the
+grouped kernel's skinny tiles for a single mid-size M, and the grouped kernel
 (grouped, and decode-sized groups, which take the skinny tile inside the
 grouped launch), plus K, M and N tails.
 """
@@ -56,7 +57,7 @@ def run_single(a_bits, b_bits, N, what):
     assert np.array_equal(bits_of(c_dump), bits_of(c_prod)), f"{what}: C of the dump instance differs"
 
 
-@pytest.mark.parametrize("name", ["tiny", "skinny", "stress", "square"])
+@pytest.mark.parametrize("name", ["tiny", "skinny", "stress", "square", "mid"])
 def test_fused_quant_bytes_workloads(name):
     say(f"dump workload {name}")
     w = synth.workload(name, synth.default_seed(name))
@@ -147,10 +148,12 @@ def test_fused_quant_bytes_grouped_decode():
 
 
 # Split-K with M and K tails; the skinny kernel with an M tail, ragged N and a K
-# tail on odd K/64; the tiled kernel with M, N and K tails; the stress recipe
-# (outliers, all-zero blocks) on the tiled kernel; -0.0 blocks and bf16 extremes.
+# tail on odd K/64 (also past 64 rows); the grouped kernel's skinny tiles for one
+# mid-size M (two and four sub-tiles, the last row tile partly past M); the tiled
+# kernel with M, N and K tails; the stress recipe (outliers, all-zero blocks) on
+# the tiled kernel; -0.0 blocks and bf16 extremes.
 EDGE = [(3, 70, 352), (16, 130, 7232), (50, 20000, 1056), (33, 64, 352), (127, 257, 1056), (65, 130, 288),
-        (300, 600, 4096), (2, 4096, 4096)]
+        (300, 600, 4096), (2, 4096, 4096), (200, 4100, 1088), (500, 4000, 1056), (700, 4100, 1056)]
 
 
 @pytest.mark.parametrize("M,N,K", EDGE)
@@ -167,6 +170,7 @@ def test_fused_quant_bytes_edges(M, N, K):
 
 
 def test_fused_quant_bytes_stress_recipe_on_tiled_kernel():
-    M, N, K = 256, 1024, 2048
+    M, N, K = 1024, 4096, 2048
+    assert ops.fused_path(M, N, K) == "tiled"
     a = synth.make_stress_a(M, K, 77)
-    run_single(a, synth.make_stress_b(N, K, 77), N, "stress recipe M=256")
+    run_single(a, synth.make_stress_b(N, K, 77), N, f"stress recipe M={M} N={N} K={K}")

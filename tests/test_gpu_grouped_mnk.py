@@ -3,9 +3,10 @@ count L, one launch; page 496271's problem form) with the CPU oracle, on an MI35
 
 Each batch's C must be within |C - C_ref| <= 2^-7 |C_ref| + 1e-3 max|C_ref| of
 the oracle's fp64 product of the dequantised operands rounded to bf16. Problems
-with M > 64 run the same tiled kernel as gemm_a4w4_fused, so there the bytes
-must also equal the single-problem call's. Problems of at most 64 rows take
-skinny tiles (K split over a workgroup's waves) in the same launch.
+with M > 64 run the tiled kernel, so where gemm_a4w4_fused runs it too
+(gemm_a4w4_fused_path) the bytes must also equal the single-problem call's.
+Problems of at most 64 rows take skinny tiles (K split over a workgroup's
+waves) in the same launch.
 """
 import numpy as np
 import pytest
@@ -73,7 +74,8 @@ def test_small_problems_fewer_subtiles():
 
 
 def test_large_m_groups_equal_single_calls():
-    shapes = [(257, 1024, 2048, 1), (130, 520, 7168, 2), (65, 64, 512, 1)]
+    shapes = [(700, 4100, 1056, 1), (520, 4000, 704, 2), (1100, 2000, 1024, 1)]
+    assert all(ops.fused_path(M, N, K) == "tiled" for M, N, K, _ in shapes)
     say(f"[mnk] vs single calls {shapes}")
     groups = [make_group(gi, M, N, K, L, 32) for gi, (M, N, K, L) in enumerate(shapes)]
     outs = ops.grouped_gemm_mnk([(A, Bp, N) for (_, _, A, Bp), (M, N, K, L) in zip(groups, shapes)])

@@ -146,7 +146,7 @@ def test_pack_B_layout(N, K):
 # ---------------------------------------------------------------------------
 # fused GEMM
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("name", ["tiny", "skinny", "stress", "skinny_shard8"])
+@pytest.mark.parametrize("name", ["tiny", "skinny", "stress", "skinny_shard8", "mid"])
 def test_gemm_workload_full(name):
     say(f"gemm workload {name}")
     w = synth.workload(name, synth.default_seed(name))
@@ -277,19 +277,11 @@ def test_gemm_repeat_identical_and_workspace_left_zero(M, N, K):
 
 
 # gemm_a4w4: the unfused comparator (A quantised by mxfp4_quant, then the GEMM on A_q).
-# Where it runs the same kernel and tiling as the fused call (the split-K kernel,
-# which these M <= 16 shapes take in both calls; M > 64: tiled) its C must be
-# bit-identical; elsewhere within the oracle's tolerance.
+# Where it runs the same kernel and tiling as the fused call (split-K for M <= 16,
+# the tiled kernel otherwise, when gemm_a4w4_fused_path names the same) its C must
+# be bit-identical; elsewhere within the oracle's tolerance.
 A4W4_SHAPES = [(1, 16, 128), (4, 256, 512), (16, 2112, 7168), (3, 70, 352), (16, 130, 7232), (16, 130, 1088),
                (33, 64, 352), (64, 130, 2048), (65, 130, 288), (127, 257, 1056), (300, 33, 32), (256, 512, 4096)]
-
-
-def splitk_in_fused(M, N, K):
-    """Whether the fused call runs the split-K kernel (as gemm_a4w4 does for M <= 16): its dump then holds one
-    copy per 64-column tile."""
-    if M > 16:
-        return False
-    return ops.lib().gemm_a4w4_fused_dump_bytes(M, N, K) == -(-(-(-N // 16)) // 4) * M * (K // 2 + K // 32)
 
 
 @pytest.mark.parametrize("M,N,K", A4W4_SHAPES)
@@ -303,9 +295,33 @@ def test_gemm_a4w4_matches_fused_and_oracle(M, N, K):
     aq, asc = ops.quant(at)
     c4 = bits_of(ops.gemm_a4w4(aq, asc, bp, N))
     cf = bits_of(ops.gemm(at, bp, N))
-    if splitk_in_fused(M, N, K) or M > 64:
+    if ops.fused_path(M, N, K) == ("splitk" if M <= 16 else "tiled"):
         assert np.array_equal(c4, cf)
     assert_in_tolerance(c4, oracle.gemm_ref(a, bq, bs), f"a4w4 M={M} N={N} K={K}")
+
+
+# Mid-size M: the fused call takes the kernel its cost model estimates fastest
+# (gemm_a4w4_fused_path). Each option against the oracle with M, N and K tails:
+# the skinny kernel; the grouped kernel's skinny tiles of two, three and four
+# 16-row sub-tiles (the last row tile partly or wholly past M); the tiled kernel.
+MID_M = [((100, 1000, 832), "skinny"), ((257, 1024, 2048), "skinny"), ((200, 4100, 1088), "skinny_tiles"),
+         ((180, 5000, 544), "skinny_tiles"), ((600, 2000, 3072), "skinny_tiles"), ((500, 4000, 1056), "skinny_tiles"),
+         ((520, 4000, 704), "tiled")]
+
+
+@pytest.mark.parametrize("shape,path", MID_M)
+def test_fused_mid_m_kernels(shape, path):
+    M, N, K = shape
+    assert ops.fused_path(M, N, K) == path
+    say(f"fused mid-M M={M} N={N} K={K} ({path})")
+    g = np.random.default_rng(M + 7 * N + 3 * K)
+    a = synth.f32_to_bf16_bits(g.standard_normal((M, K)).astype(np.float32))
+    b = synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32))
+    bq, bs = oracle.quant_mx(b)
+    at, bp = to_dev_bf16(a), packed_b(bq, bs)
+    c = bits_of(ops.gemm(at, bp, N))
+    assert_in_tolerance(c, oracle.gemm_ref(a, bq, bs), f"M={M} N={N} K={K}")
+    assert np.array_equal(bits_of(ops.gemm(at, bp, N)), c)  # repeat: the same bits
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 2112, 7168), (5, 100, 352), (130, 200, 416)])
