@@ -17,6 +17,7 @@ def test_algorithmic_bytes_and_flops_of_the_configurations():
     assert bench.alg_bytes(16, 2112, 7168) == 8_339_456
     assert bench.alg_bytes(64, 7168, 2048) == 8_978_432
     assert bench.alg_bytes(4096, 4096, 7168) == 107_872_256
+    assert bench.alg_bytes(256, 4096, 7168) == 3_670_016 + 14_680_064 + 917_504 + 2_097_152  # mid: A, B, scales, C
     assert bench.alg_flops(4096, 4096, 7168) == 240_518_168_576
     # Grouped (N 4096, K 7168): 124 780 544 B for the eight B matrices plus 22 528 B per row of A and C.
     Ms = [448, 384, 704, 384, 1024, 128, 256, 640]
@@ -109,8 +110,8 @@ def test_summarize_pmc_scales_by_the_copy_calibration(tmp_path, capsys):
     assert rec["kernel_source_hash"] == bench.kernel_source_hash()
 
 
-@pytest.mark.parametrize("name", ["square", "skinny", "stress", "grouped", "grouped_decode", "rmsnorm", "grouped_mnk",
-                                  "nvfp4_grouped", "square_unfused"])
+@pytest.mark.parametrize("name", ["square", "skinny", "stress", "grouped", "grouped_decode", "mid", "rmsnorm",
+                                  "grouped_mnk", "nvfp4_grouped", "square_unfused"])
 def test_committed_traffic_records_match_the_sources(name, monkeypatch):
     b = bench.recorded_traffic(name)
     assert b is not None and b > 0, f"profiles/traffic_{name}.json is stale or missing"
