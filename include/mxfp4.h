@@ -244,8 +244,12 @@ int gemm_a4w4(const void* Aq, int64_t ldaq, const void* As, int64_t ldas, const 
  * per-group problems; there one launch per group, here a single launch whose
  * workgroups are spread over all groups' output tiles). A group of at most 64
  * rows takes output tiles of 16 to 64 rows x 128 columns (its B spread over
- * many CUs), a larger one 128 x 512 tiles; each group's C is the same whatever
- * the other groups are.
+ * many CUs), a larger one 128 x 512 tiles. Groups of up to 512 rows take the
+ * small tiles too when a cost model of the whole launch (a function of the
+ * groups' M, N and K only) estimates it at least 15 % faster: a few such groups
+ * leave most CUs idle on 128 x 512 tiles. The C of a group of at most 64 rows
+ * is the same whatever the other groups are; a larger group's tile kind (and
+ * so its fp32 summation order) can depend on them.
  *   groups : HOST array of G descriptors, read during the call only. Per
  *            group the same rules as gemm_a4w4_fused apply to A, lda, Bp, C,
  *            ldc; M >= 1.
@@ -274,10 +278,11 @@ int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, int64_t K, vo
  * [C_g][M_g][K/32]) follows group g-1's.
  * dump: at least grouped_gemm_a4w4_dump_bytes(groups, G, N, K) bytes,
  * 16-byte aligned.
- * grouped_gemm_a4w4_dump_copies(M_g, N) gives C_g (ceil(N/128) for M_g <= 64,
- * ceil(N/512) otherwise); 0 for M_g or N outside [1, 2^30]. */
+ * grouped_gemm_a4w4_dump_copies(groups, G, N, K, g) gives C_g: ceil(N/128) for a
+ * group on skinny tiles, ceil(N/512) for one on tiled tiles (which depends on
+ * the whole list, see grouped_gemm_a4w4); 0 for an invalid list, N, K or g. */
 size_t grouped_gemm_a4w4_dump_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K);
-int64_t grouped_gemm_a4w4_dump_copies(int64_t M, int64_t N);
+int64_t grouped_gemm_a4w4_dump_copies(const mxfp4_group* groups, int G, int64_t N, int64_t K, int g);
 int grouped_gemm_a4w4_dump(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,
                            size_t workspace_bytes, void* dump, size_t dump_bytes, void* stream);
 
@@ -296,8 +301,9 @@ int grouped_gemm_a4w4_dump(const mxfp4_group* groups, int G, int64_t N, int64_t 
  *   mxfp4_pack_B_bytes(N, K), a multiple of 16; strideC >= M*ldc (the C slices
  *   do not overlap); otherwise MXFP4_ERR_SHAPE / MXFP4_ERR_ALIGN.
  *   The sum of L over the groups is at most MXFP4_MAX_GROUPS
- *   (else MXFP4_ERR_TOO_MANY_GROUPS). No workspace: every problem runs on the
- *   128 x 512 tiled kernel, whatever its M.
+ *   (else MXFP4_ERR_TOO_MANY_GROUPS). No workspace. A problem takes skinny or
+ *   128 x 512 tiled tiles by the same rule as a group of grouped_gemm_a4w4 (its
+ *   model counts every problem's own N and K).
  *   groups : HOST array of G descriptors, read during the call only.
  * ------------------------------------------------------------------------- */
 typedef struct {

@@ -1123,7 +1123,10 @@ __global__ __launch_bounds__(kTThreads) void gemm_tiled_kernel(Operand p, Dims d
 // would give it one CU per 512 columns and leave the matrix cores of that CU
 // computing 128 rows for a few. The host picks the fewest sub-tiles per tile
 // at which the launch fits one round of workgroups, else all of the group's
-// rows (each B byte then loaded once).
+// rows (each B byte then loaded once). Groups of up to a few hundred rows take
+// the same skinny tiles (several row tiles per column) when the host's model
+// (pick_small_max) estimates the launch faster so: few such groups leave most
+// CUs idle on 128 x 512 tiles.
 // Larger groups take the 128 x 512 tiled tiles. The large tiles take the first
 // workgroup ids, so the hardware starts them first (they run longest), and the
 // small tiles fill the other CUs beside them and whatever frees up. Each range
@@ -1190,9 +1193,9 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, 
 // Per-problem list of grouped_gemm_a4w4_mnk: every group contributes L
 // problems with their own (M, N, K); tile_start holds the prefix sums of the
 // problems' output tiles. As in the grouped kernel, a problem of at most
-// kGsMaxM rows takes skinny tiles of mt 16-row sub-tiles x 128 columns (rows
-// tiles per column), a larger one 128 x 512 tiled tiles; the large problems come
-// first and take the first workgroup ids.
+// kGsMaxM rows (or of a few hundred, by pick_small_max) takes skinny tiles of mt
+// 16-row sub-tiles x 128 columns (rows tiles per column), a larger one 128 x 512
+// tiled tiles; the large problems come first and take the first workgroup ids.
 struct MnkProblem {
   const uint16_t* A;
   int64_t lda;
@@ -1467,19 +1470,23 @@ int small_tile_cap(int64_t large_tiles, const int64_t* sub, const int64_t* cols,
 enum class MidPath { kTiled, kSkinny, kRows };
 constexpr int kModelCUs = 256;
 constexpr int64_t kMidMaxM = 4096;  // larger M always takes the tiled kernel
+// One workgroup's time (us) in the model: a tiled tile, a skinny-kernel tile of
+// MS rows x 16*NB columns, a grouped-kernel skinny tile of mt sub-tiles.
+double tiled_tile_us(int64_t K) { return 9.0 + (2.0 * kTBM + kTBN * 17.0 / 32.0) * (double)K / 70.4e3; }
+double skinny_kernel_tile_us(int MS, int NB, int64_t K) {
+  return 3.2 + (2.0 * MS + 16.0 * NB * 17.0 / 32.0) * (double)K / 55.6e3;
+}
+double skinny_tile_us(int64_t mt, int64_t K) { return 5.0 + (32.0 * mt + 16.0 * kGsNB * 17.0 / 32.0) * (double)K / 53.0e3; }
+
 MidPath mid_path(int64_t M, int64_t N, int64_t K) {
   if (M <= 64 || M > kMidMaxM) return MidPath::kTiled;
-  const double kd = (double)K, bcol = kd * 17.0 / 32.0;  // packed B bytes per column
   const auto rounds = [](int64_t wgs) { return (double)mxh::cdiv(wgs, kModelCUs); };
-  const double t_tiled =
-      rounds(mxh::cdiv(M, kTBM) * mxh::cdiv(N, kTBN)) * (9.0 + (2.0 * kTBM * kd + kTBN * bcol) / 70.4e3);
+  const double t_tiled = rounds(mxh::cdiv(M, kTBM) * mxh::cdiv(N, kTBN)) * tiled_tile_us(K);
   const SkinnyShape sh = choose_skinny(M, N, K);
-  const double t_sk = rounds(mxh::cdiv(mxh::cdiv(N, 16), sh.NB) * mxh::cdiv(M, sh.MS)) *
-                      (3.2 + (2.0 * sh.MS * kd + 16.0 * sh.NB * bcol) / 55.6e3);
+  const double t_sk = rounds(mxh::cdiv(mxh::cdiv(N, 16), sh.NB) * mxh::cdiv(M, sh.MS)) * skinny_kernel_tile_us(sh.MS, sh.NB, K);
   const int64_t sub = mxh::cdiv(M, 16), cols = mxh::cdiv(N, 16 * kGsNB);
   const int64_t mt = std::min<int64_t>(small_tile_cap(0, &sub, &cols, 1, kModelCUs), sub);
-  const double t_rows =
-      rounds(mxh::cdiv(M, 16 * mt) * cols) * (5.0 + (32.0 * mt * kd + 16.0 * kGsNB * bcol) / 53.0e3);
+  const double t_rows = rounds(mxh::cdiv(M, 16 * mt) * cols) * skinny_tile_us(mt, K);
   MidPath best = MidPath::kTiled;
   double t = 0.85 * t_tiled;
   if (t_sk < t) {
@@ -1488,6 +1495,71 @@ MidPath mid_path(int64_t M, int64_t N, int64_t K) {
   }
   if (t_rows < t) best = MidPath::kRows;
   return best;
+}
+
+// Which groups of a grouped launch take skinny tiles: those of at most
+// small_max rows. small_max is 64, or the M of a group of at most
+// kMidGroupMaxM rows when the model estimates that launch at least 15 % faster
+// (a few mid-size groups leave most 128 x 512 tiles' CUs idle, as in mid_path).
+// A launch is estimated as the longer of its longest tile and its rounds of
+// kModelCUs workgroups times the mean tile time (exact for tiles of one
+// length, which run in whole rounds). Problem p has M[p] rows, cols[p]
+// 128-column tiles and big[p] 128 x 512 tiles (both times its batches) and K[p].
+constexpr int64_t kMidGroupMaxM = 512;
+double launch_us(const int64_t* M, const int64_t* cols, const int64_t* big, const int64_t* K, int n, int64_t small_max) {
+  int64_t large = 0, sub[MXFP4_MAX_GROUPS], scols[MXFP4_MAX_GROUPS], tiles = 0;
+  int ns = 0;
+  double total = 0.0, longest = 0.0;
+  for (int p = 0; p < n; ++p) {
+    if (M[p] <= small_max) {
+      sub[ns] = mxh::cdiv(M[p], 16);
+      scols[ns++] = cols[p];
+    } else {
+      large += big[p];
+      tiles += big[p];
+      total += (double)big[p] * tiled_tile_us(K[p]);
+      longest = std::max(longest, tiled_tile_us(K[p]));
+    }
+  }
+  const int64_t cap = small_tile_cap(large, sub, scols, ns, kModelCUs);
+  for (int p = 0; p < n; ++p) {
+    if (M[p] > small_max) continue;
+    const int64_t mt = std::min(cap, mxh::cdiv(M[p], 16));
+    const double t = skinny_tile_us(mt, K[p]);
+    const int64_t n_p = mxh::cdiv(M[p], 16 * mt) * cols[p];
+    tiles += n_p;
+    total += (double)n_p * t;
+    longest = std::max(longest, t);
+  }
+  if (tiles == 0) return 0.0;
+  return std::max(longest, (double)mxh::cdiv(tiles, kModelCUs) * total / (double)tiles);
+}
+int64_t pick_small_max(const int64_t* M, const int64_t* cols, const int64_t* big, const int64_t* K, int n) {
+  int64_t cand[MXFP4_MAX_GROUPS];
+  int nc = 0;
+  for (int p = 0; p < n; ++p)
+    if (M[p] > kGsMaxM && M[p] <= kMidGroupMaxM) cand[nc++] = M[p];
+  std::sort(cand, cand + nc);  // ascending: of equal estimates the smallest wins
+  int64_t best = kGsMaxM;
+  double t = 0.85 * launch_us(M, cols, big, K, n, kGsMaxM);
+  for (int c = 0; c < nc; ++c) {
+    const double tc = launch_us(M, cols, big, K, n, cand[c]);
+    if (tc < t) {
+      t = tc;
+      best = cand[c];
+    }
+  }
+  return best;
+}
+int64_t grouped_small_max(const mxfp4_group* groups, int G, int64_t N, int64_t K) {
+  int64_t M[MXFP4_MAX_GROUPS], cols[MXFP4_MAX_GROUPS], big[MXFP4_MAX_GROUPS], Ks[MXFP4_MAX_GROUPS];
+  for (int g = 0; g < G; ++g) {
+    M[g] = groups[g].M;
+    cols[g] = mxh::cdiv(N, 16 * kGsNB);
+    big[g] = mxh::cdiv(M[g], kTBM) * mxh::cdiv(N, kTBN);
+    Ks[g] = K;
+  }
+  return pick_small_max(M, cols, big, Ks, G);
 }
 
 int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* dump, size_t dump_bytes, void* stream,
@@ -1713,21 +1785,22 @@ extern "C" size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, i
 namespace {
 // Copies of a group's quantised A in the verification dump: one per column tile
 // of the tile kind the group takes.
-int64_t grouped_copies(int64_t M, int64_t N, int64_t small_max = kGsMaxM) {
+int64_t grouped_copies(int64_t M, int64_t N, int64_t small_max) {
   return M <= small_max ? mxh::cdiv(N, 16 * kGsNB) : mxh::cdiv(N, kTBN);
 }
 
 // Verification dump of the grouped call: group g's block (its copies, codes
 // then scales, as for the single call) follows group g-1's.
-size_t grouped_dump_bytes_of(const mxfp4_group* groups, int G, int64_t N, int64_t K, int64_t small_max = kGsMaxM) {
+size_t grouped_dump_bytes_of(const mxfp4_group* groups, int G, int64_t N, int64_t K, int64_t small_max) {
   size_t t = 0;
   for (int g = 0; g < G; ++g)
     t += (size_t)(grouped_copies(groups[g].M, N, small_max) * groups[g].M * (K / 2 + K / 32));
   return t;
 }
 
-// Groups of at most small_max rows take skinny tiles (kGsMaxM for the grouped
-// calls; the single fused call routes one group of any M here).
+// Groups of at most small_max rows take skinny tiles; small_max < 0 picks it
+// by grouped_small_max (the grouped calls). The single fused call routes one
+// group of any M here with small_max = M.
 int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* dump, size_t dump_bytes, void* stream,
                  int64_t small_max) {
   if (!groups) return MXFP4_ERR_NULL;
@@ -1740,6 +1813,7 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
     if (st != MXFP4_OK) return st;
     a.g[g] = make_operand(q.A, q.lda, q.Bp, q.C, q.ldc, q.M, N, K);
   }
+  if (small_max < 0) small_max = grouped_small_max(groups, G, N, K);
   // A small group's tiles: 16-row sub-tiles x 128 columns, as many sub-tiles
   // per tile as small_tile_cap allows.
   int64_t large_tiles = 0, sub[MXFP4_MAX_GROUPS], cols[MXFP4_MAX_GROUPS];
@@ -1811,19 +1885,28 @@ extern "C" int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, in
                                  size_t workspace_bytes, void* stream) {
   (void)workspace;
   (void)workspace_bytes;
-  return grouped_call(groups, G, N, K, nullptr, 0, stream, kGsMaxM);
+  return grouped_call(groups, G, N, K, nullptr, 0, stream, -1);
 }
+
+namespace {
+bool dump_shape_ok(const mxfp4_group* groups, int G, int64_t N, int64_t K) {
+  if (!groups || G < 1 || G > MXFP4_MAX_GROUPS || N < 1 || N > mxh::kMaxDim || K < 32 || K % 32 != 0 ||
+      K > mxh::kMaxDim)
+    return false;
+  for (int g = 0; g < G; ++g)
+    if (groups[g].M < 1 || groups[g].M > mxh::kMaxDim) return false;
+  return true;
+}
+}  // namespace
 
 extern "C" size_t grouped_gemm_a4w4_dump_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K) {
-  if (!groups || G < 1 || G > MXFP4_MAX_GROUPS || N < 1 || K < 32 || K % 32 != 0) return 0;
-  for (int g = 0; g < G; ++g)
-    if (groups[g].M < 1 || groups[g].M > mxh::kMaxDim) return 0;
-  return grouped_dump_bytes_of(groups, G, N, K);
+  if (!dump_shape_ok(groups, G, N, K)) return 0;
+  return grouped_dump_bytes_of(groups, G, N, K, grouped_small_max(groups, G, N, K));
 }
 
-extern "C" int64_t grouped_gemm_a4w4_dump_copies(int64_t M, int64_t N) {
-  if (M < 1 || M > mxh::kMaxDim || N < 1 || N > mxh::kMaxDim) return 0;
-  return grouped_copies(M, N);
+extern "C" int64_t grouped_gemm_a4w4_dump_copies(const mxfp4_group* groups, int G, int64_t N, int64_t K, int g) {
+  if (!dump_shape_ok(groups, G, N, K) || g < 0 || g >= G) return 0;
+  return grouped_copies(groups[g].M, N, grouped_small_max(groups, G, N, K));
 }
 
 extern "C" int grouped_gemm_a4w4_dump(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,
@@ -1831,7 +1914,7 @@ extern "C" int grouped_gemm_a4w4_dump(const mxfp4_group* groups, int G, int64_t 
   (void)workspace;
   (void)workspace_bytes;
   if (!dump) return MXFP4_ERR_NULL;
-  return grouped_call(groups, G, N, K, dump, dump_bytes, stream, kGsMaxM);
+  return grouped_call(groups, G, N, K, dump, dump_bytes, stream, -1);
 }
 
 extern "C" int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void* stream) {
@@ -1839,8 +1922,8 @@ extern "C" int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void*
   if (G < 1) return MXFP4_ERR_TOO_MANY_GROUPS;
   MnkArgs a{};
   int P = 0;
-  int64_t large_tiles = 0, sub[MXFP4_MAX_GROUPS], cols[MXFP4_MAX_GROUPS];
-  int nsmall = 0;
+  // Every group is at most MXFP4_MAX_GROUPS problems, so G is at most that too.
+  int64_t gM[MXFP4_MAX_GROUPS], gcols[MXFP4_MAX_GROUPS], gbig[MXFP4_MAX_GROUPS], gK[MXFP4_MAX_GROUPS];
   for (int g = 0; g < G; ++g) {
     const mxfp4_group_mnk& q = groups[g];
     if (q.L < 1) return MXFP4_ERR_SHAPE;
@@ -1853,11 +1936,21 @@ extern "C" int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void*
       if (q.strideA < 0 || q.strideB < (int64_t)pg.total() || q.strideC < q.M * q.ldc) return MXFP4_ERR_SHAPE;
       if ((q.strideA * 2) % 16 != 0 || q.strideB % 16 != 0) return MXFP4_ERR_ALIGN;
     }
-    if (q.M <= kGsMaxM) {
-      sub[nsmall] = mxh::cdiv(q.M, 16);
-      cols[nsmall++] = q.L * mxh::cdiv(q.N, 16 * kGsNB);
+    gM[g] = q.M;
+    gcols[g] = q.L * mxh::cdiv(q.N, 16 * kGsNB);
+    gbig[g] = q.L * mxh::cdiv(q.M, kTBM) * mxh::cdiv(q.N, kTBN);
+    gK[g] = q.K;
+  }
+  // Problems of at most small_max rows take skinny tiles (as in the grouped call).
+  const int64_t small_max = pick_small_max(gM, gcols, gbig, gK, G);
+  int64_t large_tiles = 0, sub[MXFP4_MAX_GROUPS], cols[MXFP4_MAX_GROUPS];
+  int nsmall = 0;
+  for (int g = 0; g < G; ++g) {
+    if (gM[g] <= small_max) {
+      sub[nsmall] = mxh::cdiv(gM[g], 16);
+      cols[nsmall++] = gcols[g];
     } else {
-      large_tiles += q.L * mxh::cdiv(q.M, kTBM) * mxh::cdiv(q.N, kTBN);
+      large_tiles += gbig[g];
     }
   }
   // Small problems: tiles of min(cap, M/16) 16-row sub-tiles x 128 columns.
@@ -1877,7 +1970,7 @@ extern "C" int grouped_gemm_a4w4_mnk(const mxfp4_group_mnk* groups, int G, void*
     }
     for (int g = 0; g < G; ++g) {
       const mxfp4_group_mnk& q = groups[g];
-      if ((q.M <= kGsMaxM) != (small != 0)) continue;
+      if ((q.M <= small_max) != (small != 0)) continue;
       const mxh::PackedGeom pg(q.N, q.K);
       const int64_t mt = small ? std::min(cap, mxh::cdiv(q.M, 16)) : 0;
       const int64_t rows = small ? mxh::cdiv(q.M, 16 * mt) : 0;

@@ -89,7 +89,8 @@ def lib() -> ctypes.CDLL:
         L.gemm_a4w4_fused_dump.restype = i32
         L.grouped_gemm_a4w4_dump_bytes.argtypes = [ctypes.POINTER(Group), i32, i64, i64]
         L.grouped_gemm_a4w4_dump_bytes.restype = sz
-        L.grouped_gemm_a4w4_dump_copies.argtypes, L.grouped_gemm_a4w4_dump_copies.restype = [i64, i64], i64
+        L.grouped_gemm_a4w4_dump_copies.argtypes = [ctypes.POINTER(Group), i32, i64, i64, i32]
+        L.grouped_gemm_a4w4_dump_copies.restype = i64
         L.grouped_gemm_a4w4_dump.argtypes = [ctypes.POINTER(Group), i32, i64, i64, vp, sz, vp, sz, vp]
         L.grouped_gemm_a4w4_dump.restype = i32
         L.gemm_a4w4.argtypes = [vp, i64, vp, i64, vp, vp, i64, i64, i64, i64, vp, sz, vp]
@@ -316,9 +317,9 @@ def grouped_gemm_dump(a_list, bp_list, N: int):
     _check(lib().grouped_gemm_a4w4_dump(arr, G, N, K, None, 0, dump.data_ptr(), dsz, _stream(a_list[0])),
            "grouped_gemm_a4w4_dump")
     at, res = 0, []
-    for a in a_list:
+    for g, a in enumerate(a_list):
         M = a.shape[0]
-        copies = int(lib().grouped_gemm_a4w4_dump_copies(M, N))
+        copies = int(lib().grouped_gemm_a4w4_dump_copies(arr, G, N, K, g))
         nq, ns = copies * M * (K // 2), copies * M * (K // 32)
         res.append((dump[at:at + nq].view(copies, M, K // 2), dump[at + nq:at + nq + ns].view(copies, M, K // 32)))
         at += nq + ns

@@ -243,17 +243,34 @@ def test_fused_kernel_choice_mid_m():
 
 
 def test_grouped_dump_layout():
-    """A group of at most 64 rows takes 128-column tiles (one dump copy each), a larger one 512-column tiles."""
+    """A group on skinny tiles has one dump copy per 128 columns, one on 128 x 512 tiles one per 512. Groups of at
+    most 64 rows always take skinny tiles; a group of up to 512 rows takes them too when the launch model
+    estimates the whole launch faster so (here: one or two mid-size groups alone), which makes its copy count a
+    function of the whole list."""
     L = ops.lib()
-    assert [L.grouped_gemm_a4w4_dump_copies(M, 4096) for M in (1, 16, 48, 64, 65, 128, 4096)] == [32, 32, 32, 32, 8, 8, 8]
-    assert L.grouped_gemm_a4w4_dump_copies(16, 1000) == 8 and L.grouped_gemm_a4w4_dump_copies(100, 1000) == 2
-    assert L.grouped_gemm_a4w4_dump_copies(0, 4096) == 0 and L.grouped_gemm_a4w4_dump_copies(16, 0) == 0
-    g = (ops.Group * 3)()
-    Ms, N, K = (16, 200, 64), 1000, 832
-    for i, M in enumerate(Ms):
-        g[i] = ops.Group(P, K, P, P, N, M)
-    want = sum(L.grouped_gemm_a4w4_dump_copies(M, N) * M * (K // 2 + K // 32) for M in Ms)
-    assert L.grouped_gemm_a4w4_dump_bytes(g, 3, N, K) == want == (8 * 16 + 2 * 200 + 8 * 64) * (416 + 26)
+
+    def copies(Ms, N, K):
+        g = (ops.Group * len(Ms))()
+        for i, M in enumerate(Ms):
+            g[i] = ops.Group(P, K, P, P, N, M)
+        c = [L.grouped_gemm_a4w4_dump_copies(g, len(Ms), N, K, i) for i in range(len(Ms))]
+        assert L.grouped_gemm_a4w4_dump_bytes(g, len(Ms), N, K) == sum(ci * M * (K // 2 + K // 32)
+                                                                        for ci, M in zip(c, Ms))
+        return c
+
+    assert copies([1, 16, 48, 64], 4096, 7168) == [32] * 4
+    assert copies([16, 100], 1000, 832) == [8, 8]                       # the 100-row group alone: skinny tiles
+    assert copies([128, 128], 4096, 7168) == [32, 32]                   # 16 tiled tiles for 256 CUs: skinny
+    assert copies([448, 384, 704, 384, 1024, 128, 256, 640], 4096, 7168) == [8] * 8   # 256 tiled tiles: kept
+    assert copies([1024, 128], 4096, 7168) == [8, 8]                    # the 1024-row group bounds it: kept
+    assert copies([600, 64], 4096, 7168) == [8, 32]                     # past 512 rows: always tiled
+    assert copies([16, 200, 64], 1000, 832) == [8, 8, 8]
+    g = (ops.Group * 2)()
+    g[0], g[1] = ops.Group(P, 64, P, P, 64, 16), ops.Group(P, 64, P, P, 64, 0)
+    assert L.grouped_gemm_a4w4_dump_copies(g, 2, 64, 64, 0) == 0         # an invalid list
+    g[1] = ops.Group(P, 64, P, P, 64, 16)
+    assert L.grouped_gemm_a4w4_dump_copies(g, 2, 64, 64, 2) == 0         # g out of range
+    assert L.grouped_gemm_a4w4_dump_copies(g, 2, 0, 64, 0) == 0 and L.grouped_gemm_a4w4_dump_copies(g, 2, 64, 48, 0) == 0
 
 
 def _mnk(**kw):

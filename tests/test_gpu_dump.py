@@ -92,12 +92,13 @@ def run_grouped(a_list, b_list, N, what):
         assert np.array_equal(bits_of(c), bits_of(cp)), f"{what} group {g}: C of the dump instance differs"
 
 
-def test_fused_quant_bytes_grouped_small_and_large():
-    """Groups of at most 64 rows (16 x 128 tiles, one copy per 128 columns) beside larger ones (one copy
-    per 512 columns), with M, N and K tails and zero blocks."""
+@pytest.mark.parametrize("Ms", [[1, 17, 64, 65, 200, 40, 1100], [1, 17, 64, 65, 200, 40]])
+def test_fused_quant_bytes_grouped_small_and_large(Ms):
+    """Groups of at most 64 rows (skinny tiles, one copy per 128 columns) beside larger ones on 128 x 512
+    tiles (one copy per 512 columns; the 1100-row group keeps the 65- and 200-row ones there) or, without
+    it, on skinny tiles too; M, N and K tails and zero blocks."""
     g = np.random.default_rng(21)
     N, K = 1000, 832
-    Ms = [1, 17, 64, 65, 200, 40]
     a_list = []
     for m in Ms:
         a = synth.f32_to_bf16_bits((g.standard_normal((m, K)) * np.exp2(g.integers(-20, 20, (m, 1)))).astype(np.float32))

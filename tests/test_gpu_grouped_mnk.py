@@ -50,9 +50,23 @@ def test_small_problems_beside_large_ones():
     """Problems of at most 64 rows take skinny tiles beside a large problem's tiled tiles, here of at most
     three 16-row sub-tiles (the fewest at which the launch fits one round of workgroups; the 64-row problem's
     second row tile has two sub-tiles past M): ragged N, a K tail on odd K/64, batches."""
-    shapes = [(40, 4100, 1088, 3), (17, 2000, 832, 2), (300, 700, 1024, 1), (5, 4096, 512, 2), (48, 1000, 2048, 1), (64, 900, 704, 1)]
+    shapes = [(40, 4100, 1088, 3), (17, 2000, 832, 2), (600, 700, 1024, 1), (5, 4096, 512, 2), (48, 1000, 2048, 1), (64, 900, 704, 1)]
     say(f"[mnk] small and large {shapes}")
     groups = [make_group(gi, M, N, K, L, 35) for gi, (M, N, K, L) in enumerate(shapes)]
+    outs = ops.grouped_gemm_mnk([(A, Bp, N) for (_, _, A, Bp), (M, N, K, L) in zip(groups, shapes)])
+    torch.cuda.synchronize()
+    for (a_bits, bq, _, _), (M, N, K, L), C in zip(groups, shapes, outs):
+        for l in range(L):
+            assert_in_tolerance(bits_of(C[l]), oracle.gemm_ref(a_bits[l], *bq[l]), f"group M{M} N{N} K{K} l{l}")
+
+
+def test_mid_problems_on_skinny_tiles():
+    """Problems of up to 512 rows take skinny tiles too when the launch model estimates the launch faster so
+    (here every problem: a few hundred rows leave most CUs idle on 128 x 512 tiles); several row tiles per
+    column, M tails, batches, odd K/64 tails."""
+    shapes = [(130, 2048, 1056, 2), (300, 1000, 544, 1), (40, 512, 832, 1)]
+    say(f"[mnk] mid problems {shapes}")
+    groups = [make_group(gi, M, N, K, L, 38) for gi, (M, N, K, L) in enumerate(shapes)]
     outs = ops.grouped_gemm_mnk([(A, Bp, N) for (_, _, A, Bp), (M, N, K, L) in zip(groups, shapes)])
     torch.cuda.synchronize()
     for (a_bits, bq, _, _), (M, N, K, L), C in zip(groups, shapes, outs):

@@ -404,6 +404,31 @@ def test_grouped_small_tiles_fewer_subtiles(Ms, N, K):
         assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
 
 
+def tile_kinds(Ms, N, K):
+    """Per group: "skinny" or "tiled", read from the dump layout (one copy per 128 or per 512 columns)."""
+    arr = (ops.Group * len(Ms))()
+    for i, m in enumerate(Ms):
+        arr[i] = ops.Group(1 << 20, K, 1 << 20, 1 << 20, N, m)
+    c = [ops.lib().grouped_gemm_a4w4_dump_copies(arr, len(Ms), N, K, i) for i in range(len(Ms))]
+    return ["skinny" if ci == -(-N // 128) else "tiled" for ci in c]
+
+
+# Groups of 65..512 rows on skinny tiles: the launch model moves them off 128 x 512 tiles when only a few
+# such groups share the launch (several row tiles per column, M tails, odd K/64).
+@pytest.mark.parametrize("Ms,N,K", [([128, 128], 4096, 7168), ([100, 200, 300], 2000, 1056), ([70, 16, 250], 3000, 544)])
+def test_grouped_mid_groups_on_skinny_tiles(Ms, N, K):
+    assert tile_kinds(Ms, N, K) == ["skinny"] * len(Ms)
+    say(f"grouped mid groups Ms={Ms} N={N} K={K}")
+    g = np.random.default_rng(15)
+    a = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
+    b = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
+    qs = [oracle.quant_mx(x) for x in b]
+    cs = ops.grouped_gemm([to_dev_bf16(x) for x in a], [packed_b(*q) for q in qs], N)
+    torch.cuda.synchronize()
+    for x, (bq, bs), c in zip(a, qs, cs):
+        assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
+
+
 def test_grouped_small_subtiles_ragged():
     """Small groups whose 16-row tiles would not fit one round of workgroups take one tile of all their
     rows (one to four 16-row sub-tiles sharing each B load): M 5, 17, 33, 48, 57, 64, N with a tail of 8 columns
@@ -450,7 +475,7 @@ def test_grouped_on_a_side_stream():
     say("grouped on a side stream")
     g = np.random.default_rng(14)
     N, K = 600, 512
-    Ms = [9, 40, 130]
+    Ms = [9, 40, 130, 700]
     a = [to_dev_bf16(synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32))) for m in Ms]
     b = [oracle.quant_mx(synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)))
          for _ in Ms]
