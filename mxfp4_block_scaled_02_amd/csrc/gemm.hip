@@ -1673,8 +1673,6 @@ constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices];
 
-// Device address of `scratch` on the device that runs `stream` (the current
-// device for the null stream).
 // The device a stream runs on (the current device for the null stream), and
 // the current device.
 int stream_device(void* stream, int* dev, int* cur) {
@@ -1688,6 +1686,8 @@ int stream_device(void* stream, int* dev, int* cur) {
   return *dev >= 0 && *dev < kMaxDevices ? MXFP4_OK : MXFP4_ERR_HIP;
 }
 
+// Device address of `scratch` on the device that runs `stream` (the current
+// device for the null stream), looked up once per device.
 int scratch_address(void* stream, void** out) {
   int cur = 0, dev = 0;
   const int st = stream_device(stream, &dev, &cur);
