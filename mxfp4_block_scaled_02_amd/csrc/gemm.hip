@@ -1187,6 +1187,22 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, 
   }
 }
 
+// A grouped launch of small groups only whose 16-row tiles all fit one round of
+// workgroups: the tiles of the skinny kernel (16 waves split K), which stream a
+// CU's bytes faster than the 8-wave tiles above (one 16-row x 128-column tile
+// at M64 N4096 K7168: 12.2 against 18.8 us). Entries and rows as for
+// gemm_grouped_kernel with every mt 1; the whole grid is remapped for the XCDs.
+template <bool DUMP>
+__global__ __launch_bounds__(kSkWaves * 64) void gemm_grouped_small_kernel(GroupedArgs a, Dims d) {
+  __shared__ __align__(16) SkinnySmem<kSkWaves, kGsNB> sm;
+  const int v = xcd_remap((int)blockIdx.x, (int)gridDim.x);
+  int e = 0;
+  while (e + 1 < a.G && a.tile_start[e + 1] <= v) ++e;
+  const int local = v - a.tile_start[e];
+  const int c = local / a.rows[e], r = local - c * a.rows[e];
+  skinny_tile<kSkWaves, 16, kGsNB, 1, DUMP>(a.g[a.order[e]], d, r * 16, c * kGsNB, c, sm);
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
@@ -1875,6 +1891,10 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
   if (grid > INT32_MAX) return MXFP4_ERR_SHAPE;
   Dims d = make_dims(N, K);
   void* args[] = {&a, &d};
+  if (large_tiles == 0 && cap == 1)  // small groups only, 16-row tiles in one round
+    return mxh::launch_status(hipLaunchKernel(
+        dump ? (const void*)gemm_grouped_small_kernel<true> : (const void*)gemm_grouped_small_kernel<false>,
+        dim3((unsigned)grid), dim3(kSkWaves * 64), args, 0, (hipStream_t)stream));
   return mxh::launch_status(hipLaunchKernel(
       dump ? (const void*)gemm_grouped_kernel<true> : (const void*)gemm_grouped_kernel<false>, dim3((unsigned)grid),
       dim3(kTThreads), args, 0, (hipStream_t)stream));

@@ -109,6 +109,18 @@ def test_fused_quant_bytes_grouped_small_and_large(Ms):
     run_grouped(a_list, b_list, N, "mixed groups")
 
 
+def test_fused_quant_bytes_grouped_small_only_one_round():
+    """Small groups only, 16-row tiles in one round of workgroups (the 16-wave skinny tiles), with tails."""
+    g = np.random.default_rng(25)
+    N, K = 2000, 1056
+    Ms = [1, 16, 17, 33, 64, 5]
+    a_list = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
+    for a in a_list:
+        a[0, :32] = 0x8000
+    b_list = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
+    run_grouped(a_list, b_list, N, "small only, one round")
+
+
 def test_fused_quant_bytes_grouped_more_tiles_than_cus():
     """More 128 x 512 tiles than CUs (264: a second round of workgroups), a K tail on odd K/64."""
     g = np.random.default_rng(23)

@@ -429,6 +429,23 @@ def test_grouped_mid_groups_on_skinny_tiles(Ms, N, K):
         assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
 
 
+def test_grouped_small_only_one_round():
+    """Small groups only, whose 16-row tiles all fit one round of workgroups: the launch runs the 16-wave
+    skinny tiles (M tails 1, 17, 33, 5; ragged N; a K tail on odd K/64)."""
+    say("grouped small only, one round")
+    g = np.random.default_rng(16)
+    N, K = 2000, 1056
+    Ms = [1, 16, 17, 33, 64, 5]
+    assert sum(-(-m // 16) for m in Ms) * -(-N // 128) <= 256
+    a = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
+    b = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
+    qs = [oracle.quant_mx(x) for x in b]
+    cs = ops.grouped_gemm([to_dev_bf16(x) for x in a], [packed_b(*q) for q in qs], N)
+    torch.cuda.synchronize()
+    for x, (bq, bs), c in zip(a, qs, cs):
+        assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
+
+
 def test_grouped_small_subtiles_ragged():
     """Small groups whose 16-row tiles would not fit one round of workgroups take one tile of all their
     rows (one to four 16-row sub-tiles sharing each B load): M 5, 17, 33, 48, 57, 64, N with a tail of 8 columns
