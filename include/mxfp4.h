@@ -279,8 +279,10 @@ int grouped_gemm_a4w4(const mxfp4_group* groups, int G, int64_t N, int64_t K, vo
  * dump: at least grouped_gemm_a4w4_dump_bytes(groups, G, N, K) bytes,
  * 16-byte aligned.
  * grouped_gemm_a4w4_dump_copies(groups, G, N, K, g) gives C_g: ceil(N/128) for a
- * group on skinny tiles, ceil(N/512) for one on tiled tiles (which depends on
- * the whole list, see grouped_gemm_a4w4); 0 for an invalid list, N, K or g. */
+ * group on skinny tiles (ceil(N/64) when only small groups share the launch and
+ * 128-column tiles would leave most CUs idle), ceil(N/512) for one on tiled
+ * tiles; it depends on the whole list (see grouped_gemm_a4w4). 0 for an invalid
+ * list, N, K or g. */
 size_t grouped_gemm_a4w4_dump_bytes(const mxfp4_group* groups, int G, int64_t N, int64_t K);
 int64_t grouped_gemm_a4w4_dump_copies(const mxfp4_group* groups, int G, int64_t N, int64_t K, int g);
 int grouped_gemm_a4w4_dump(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,

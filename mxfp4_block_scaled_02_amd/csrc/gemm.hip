@@ -1188,19 +1188,19 @@ __global__ __launch_bounds__(kTThreads) void gemm_grouped_kernel(GroupedArgs a, 
 }
 
 // A grouped launch of small groups only whose 16-row tiles all fit one round of
-// workgroups: the tiles of the skinny kernel (16 waves split K), which stream a
-// CU's bytes faster than the 8-wave tiles above (one 16-row x 128-column tile
-// at M64 N4096 K7168: 12.2 against 18.8 us). Entries and rows as for
+// workgroups: the tiles of the skinny kernel, 16 rows x 16*NB columns with K
+// split over 16 waves (faster than the 8-wave tiles above), 64 columns when
+// 128-column tiles would fill at most half a round. Entries and rows as for
 // gemm_grouped_kernel with every mt 1; the whole grid is remapped for the XCDs.
-template <bool DUMP>
+template <int NB, bool DUMP>
 __global__ __launch_bounds__(kSkWaves * 64) void gemm_grouped_small_kernel(GroupedArgs a, Dims d) {
-  __shared__ __align__(16) SkinnySmem<kSkWaves, kGsNB> sm;
+  __shared__ __align__(16) SkinnySmem<kSkWaves, NB> sm;
   const int v = xcd_remap((int)blockIdx.x, (int)gridDim.x);
   int e = 0;
   while (e + 1 < a.G && a.tile_start[e + 1] <= v) ++e;
   const int local = v - a.tile_start[e];
   const int c = local / a.rows[e], r = local - c * a.rows[e];
-  skinny_tile<kSkWaves, 16, kGsNB, 1, DUMP>(a.g[a.order[e]], d, r * 16, c * kGsNB, c, sm);
+  skinny_tile<kSkWaves, 16, NB, NB == 4 ? 2 : 1, DUMP>(a.g[a.order[e]], d, r * 16, c * NB, c, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1452,6 +1452,11 @@ hipError_t launch_tiled(const Operand& o, const Dims& d, int64_t M, int64_t N, b
   return hipLaunchKernel(k, dim3((unsigned)tiles), dim3(kTThreads), args, 0, st);
 }
 
+// CUs counted by the host's kernel-choice models (the MI355X's), so that the
+// choices they make, and the verification dump's layout, depend on the shapes
+// alone.
+constexpr int kModelCUs = 256;
+
 // 16-row sub-tiles per small tile of the grouped kernel: a small problem with
 // sub[i] sub-tiles and cols[i] 128-column tiles (times its batches) takes tiles
 // of min(cap, sub[i]) sub-tiles. cap is the smallest count at which the launch
@@ -1466,6 +1471,20 @@ int small_tile_cap(int64_t large_tiles, const int64_t* sub, const int64_t* cols,
     if (t <= cus) return c;
   }
   return kGsMaxM / 16;
+}
+
+// 16-column tiles per small tile of a grouped launch: kGsNB (128 columns), or
+// half when every group is small and their 16 x 128 tiles fill at most half a
+// round of kModelCUs workgroups (twice the workgroups, each reading half the B,
+// as choose_skinny does for one problem). Counted on the model's CUs, so the
+// dump layout depends on the shapes alone.
+int small_nb(const int64_t* M, int n, int64_t N, int64_t small_max) {
+  int64_t t = 0;
+  for (int i = 0; i < n; ++i) {
+    if (M[i] > small_max) return kGsNB;
+    t += mxh::cdiv(M[i], 16) * mxh::cdiv(N, 16 * kGsNB);
+  }
+  return 2 * t <= kModelCUs ? kGsNB / 2 : kGsNB;
 }
 
 // Kernel of the single fused call for M > 64. The 128 x 512 tiled tile loads
@@ -1484,7 +1503,6 @@ int small_tile_cap(int64_t large_tiles, const int64_t* sub, const int64_t* cols,
 // model counts the MI355X's 256 CUs whatever the device, so the choice (and
 // with it the verification dump's layout) depends on M, N and K alone.
 enum class MidPath { kTiled, kSkinny, kRows };
-constexpr int kModelCUs = 256;
 constexpr int64_t kMidMaxM = 4096;  // larger M always takes the tiled kernel
 // One workgroup's time (us) in the model: a tiled tile, a skinny-kernel tile of
 // MS rows x 16*NB columns, a grouped-kernel skinny tile of mt sub-tiles.
@@ -1607,7 +1625,7 @@ int64_t dump_copies(int64_t M, int64_t N, int64_t K) {
   if (fused_splitk(M, N, K, g)) return g.T;
   const MidPath mp = mid_path(M, N, K);
   if (M <= 64 || mp == MidPath::kSkinny) return mxh::cdiv(mxh::cdiv(N, 16), choose_skinny(M, N, K).NB);
-  if (mp == MidPath::kRows) return mxh::cdiv(N, 16 * kGsNB);
+  if (mp == MidPath::kRows) return mxh::cdiv(N, 16 * small_nb(&M, 1, N, M));
   return mxh::cdiv(N, kTBN);
 }
 size_t dump_bytes_of(int64_t M, int64_t N, int64_t K) {
@@ -1801,16 +1819,22 @@ extern "C" size_t grouped_gemm_a4w4_workspace_bytes(const mxfp4_group* groups, i
 namespace {
 // Copies of a group's quantised A in the verification dump: one per column tile
 // of the tile kind the group takes.
-int64_t grouped_copies(int64_t M, int64_t N, int64_t small_max) {
-  return M <= small_max ? mxh::cdiv(N, 16 * kGsNB) : mxh::cdiv(N, kTBN);
+int64_t grouped_copies(int64_t M, int64_t N, int64_t small_max, int nb) {
+  return M <= small_max ? mxh::cdiv(N, 16 * nb) : mxh::cdiv(N, kTBN);
+}
+int grouped_nb(const mxfp4_group* groups, int G, int64_t N, int64_t small_max) {
+  int64_t M[MXFP4_MAX_GROUPS];
+  for (int g = 0; g < G; ++g) M[g] = groups[g].M;
+  return small_nb(M, G, N, small_max);
 }
 
 // Verification dump of the grouped call: group g's block (its copies, codes
 // then scales, as for the single call) follows group g-1's.
 size_t grouped_dump_bytes_of(const mxfp4_group* groups, int G, int64_t N, int64_t K, int64_t small_max) {
+  const int nb = grouped_nb(groups, G, N, small_max);
   size_t t = 0;
   for (int g = 0; g < G; ++g)
-    t += (size_t)(grouped_copies(groups[g].M, N, small_max) * groups[g].M * (K / 2 + K / 32));
+    t += (size_t)(grouped_copies(groups[g].M, N, small_max, nb) * groups[g].M * (K / 2 + K / 32));
   return t;
 }
 
@@ -1843,8 +1867,12 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
       large_tiles += mxh::cdiv(M, kTBM) * ntn;
     }
   }
+  // 64-column small tiles (nb 4) only with 16-row tiles on the 16-wave kernel.
+  const int nb = grouped_nb(groups, G, N, small_max);
   int64_t cap = kGsMaxM / 16;
-  if (nsmall > 0) {
+  if (nb < kGsNB) {
+    cap = 1;
+  } else if (nsmall > 0) {
     int cus = 0;
     const int st = device_cus(stream, &cus);
     if (st != MXFP4_OK) return st;
@@ -1868,7 +1896,7 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
       a.rows[e] = (int)rows;
       a.mt[e] = small ? (int)mt : 0;
       a.tile_start[e] = (int)total;
-      total += rows * (small ? mxh::cdiv(N, 16 * kGsNB) : ntn);
+      total += rows * (small ? mxh::cdiv(N, 16 * nb) : ntn);
       if (total > INT32_MAX) return MXFP4_ERR_SHAPE;
       ++e;
     }
@@ -1878,7 +1906,7 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
     if (!mxh::aligned(dump, 16)) return MXFP4_ERR_ALIGN;
     uint8_t* at = (uint8_t*)dump;
     for (int g = 0; g < G; ++g) {
-      const int64_t copies = grouped_copies(groups[g].M, N, small_max);
+      const int64_t copies = grouped_copies(groups[g].M, N, small_max, nb);
       a.g[g].dq = at;
       a.g[g].ds = at + copies * groups[g].M * (K / 2);
       at += copies * groups[g].M * (K / 2 + K / 32);
@@ -1891,10 +1919,14 @@ int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* d
   if (grid > INT32_MAX) return MXFP4_ERR_SHAPE;
   Dims d = make_dims(N, K);
   void* args[] = {&a, &d};
-  if (large_tiles == 0 && cap == 1)  // small groups only, 16-row tiles in one round
-    return mxh::launch_status(hipLaunchKernel(
-        dump ? (const void*)gemm_grouped_small_kernel<true> : (const void*)gemm_grouped_small_kernel<false>,
-        dim3((unsigned)grid), dim3(kSkWaves * 64), args, 0, (hipStream_t)stream));
+  if (large_tiles == 0 && cap == 1) {  // small groups only, 16-row tiles in one round
+    const void* kern = nb < kGsNB ? (dump ? (const void*)gemm_grouped_small_kernel<kGsNB / 2, true>
+                                          : (const void*)gemm_grouped_small_kernel<kGsNB / 2, false>)
+                                  : (dump ? (const void*)gemm_grouped_small_kernel<kGsNB, true>
+                                          : (const void*)gemm_grouped_small_kernel<kGsNB, false>);
+    return mxh::launch_status(
+        hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kSkWaves * 64), args, 0, (hipStream_t)stream));
+  }
   return mxh::launch_status(hipLaunchKernel(
       dump ? (const void*)gemm_grouped_kernel<true> : (const void*)gemm_grouped_kernel<false>, dim3((unsigned)grid),
       dim3(kTThreads), args, 0, (hipStream_t)stream));
@@ -1926,7 +1958,8 @@ extern "C" size_t grouped_gemm_a4w4_dump_bytes(const mxfp4_group* groups, int G,
 
 extern "C" int64_t grouped_gemm_a4w4_dump_copies(const mxfp4_group* groups, int G, int64_t N, int64_t K, int g) {
   if (!dump_shape_ok(groups, G, N, K) || g < 0 || g >= G) return 0;
-  return grouped_copies(groups[g].M, N, grouped_small_max(groups, G, N, K));
+  const int64_t small_max = grouped_small_max(groups, G, N, K);
+  return grouped_copies(groups[g].M, N, small_max, grouped_nb(groups, G, N, small_max));
 }
 
 extern "C" int grouped_gemm_a4w4_dump(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* workspace,

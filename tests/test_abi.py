@@ -243,10 +243,11 @@ def test_fused_kernel_choice_mid_m():
 
 
 def test_grouped_dump_layout():
-    """A group on skinny tiles has one dump copy per 128 columns, one on 128 x 512 tiles one per 512. Groups of at
-    most 64 rows always take skinny tiles; a group of up to 512 rows takes them too when the launch model
-    estimates the whole launch faster so (here: one or two mid-size groups alone), which makes its copy count a
-    function of the whole list."""
+    """A group on skinny tiles has one dump copy per 128 columns (per 64 when only small groups share the
+    launch and their 128-column tiles would fill at most half a round), one on 128 x 512 tiles one per 512.
+    Groups of at most 64 rows always take skinny tiles; a group of up to 512 rows takes them too when the
+    launch model estimates the whole launch faster so (here: one or two mid-size groups alone), which makes
+    its copy count a function of the whole list."""
     L = ops.lib()
 
     def copies(Ms, N, K):
@@ -259,12 +260,13 @@ def test_grouped_dump_layout():
         return c
 
     assert copies([1, 16, 48, 64], 4096, 7168) == [32] * 4
-    assert copies([16, 100], 1000, 832) == [8, 8]                       # the 100-row group alone: skinny tiles
+    assert copies([16, 100], 1000, 832) == [16, 16]   # the 100-row group too: skinny tiles, 64 columns (half a round)
     assert copies([128, 128], 4096, 7168) == [32, 32]                   # 16 tiled tiles for 256 CUs: skinny
     assert copies([448, 384, 704, 384, 1024, 128, 256, 640], 4096, 7168) == [8] * 8   # 256 tiled tiles: kept
     assert copies([1024, 128], 4096, 7168) == [8, 8]                    # the 1024-row group bounds it: kept
     assert copies([600, 64], 4096, 7168) == [8, 32]                     # past 512 rows: always tiled
-    assert copies([16, 200, 64], 1000, 832) == [8, 8, 8]
+    assert copies([16, 200, 64], 1000, 832) == [8, 8, 8]                # 144 tiles of 128 columns: kept
+    assert copies([1, 17, 33, 5], 2000, 1056) == [32] * 4                 # 112 tiles of 128 columns: 64 instead
     g = (ops.Group * 2)()
     g[0], g[1] = ops.Group(P, 64, P, P, 64, 16), ops.Group(P, 64, P, P, 64, 0)
     assert L.grouped_gemm_a4w4_dump_copies(g, 2, 64, 64, 0) == 0         # an invalid list

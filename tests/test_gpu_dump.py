@@ -109,11 +109,12 @@ def test_fused_quant_bytes_grouped_small_and_large(Ms):
     run_grouped(a_list, b_list, N, "mixed groups")
 
 
-def test_fused_quant_bytes_grouped_small_only_one_round():
-    """Small groups only, 16-row tiles in one round of workgroups (the 16-wave skinny tiles), with tails."""
+@pytest.mark.parametrize("Ms", [[1, 16, 17, 33, 64, 5], [1, 17, 33, 5]])
+def test_fused_quant_bytes_grouped_small_only_one_round(Ms):
+    """Small groups only, 16-row tiles in one round of workgroups (the 16-wave skinny tiles: 128 columns, or
+    64 for the second list), with tails."""
     g = np.random.default_rng(25)
     N, K = 2000, 1056
-    Ms = [1, 16, 17, 33, 64, 5]
     a_list = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
     for a in a_list:
         a[0, :32] = 0x8000

@@ -429,13 +429,14 @@ def test_grouped_mid_groups_on_skinny_tiles(Ms, N, K):
         assert_in_tolerance(bits_of(c), oracle.gemm_ref(x, bq, bs), f"M={x.shape[0]}")
 
 
-def test_grouped_small_only_one_round():
-    """Small groups only, whose 16-row tiles all fit one round of workgroups: the launch runs the 16-wave
-    skinny tiles (M tails 1, 17, 33, 5; ragged N; a K tail on odd K/64)."""
-    say("grouped small only, one round")
+# Small groups only, whose 16-row tiles all fit one round of workgroups: the launch runs the 16-wave skinny
+# tiles, 128 columns wide, or 64 when 128-column tiles would fill at most half a round (M tails 1, 17, 33,
+# 5; ragged N; a K tail on odd K/64).
+@pytest.mark.parametrize("Ms", [[1, 16, 17, 33, 64, 5], [1, 17, 33, 5]])
+def test_grouped_small_only_one_round(Ms):
+    say(f"grouped small only, one round, Ms={Ms}")
     g = np.random.default_rng(16)
     N, K = 2000, 1056
-    Ms = [1, 16, 17, 33, 64, 5]
     assert sum(-(-m // 16) for m in Ms) * -(-N // 128) <= 256
     a = [synth.f32_to_bf16_bits(g.standard_normal((m, K)).astype(np.float32)) for m in Ms]
     b = [synth.f32_to_bf16_bits((g.standard_normal((N, K)) * 0.02).astype(np.float32)) for _ in Ms]
