@@ -168,9 +168,8 @@ int gemm_a4w4_fused(const void* A, int64_t lda, const void* Bp, void* C, int64_t
  * grouped_gemm_a4w4 gives small groups (16 to 64 rows x 128 columns, K split
  * over 8 waves), for M > 64. MXFP4_PATH_TILED: 128 x 512 tiles. 0 for a shape
  * the call rejects (as MXFP4_ERR_SHAPE). Calls that run the same kernel on the
- * same operands give bit-identical C; gemm_a4w4 runs the split-K kernel for
- * M <= 16 and the tiled kernel otherwise. Not an operation of the pages: a
- * query for callers and tests.
+ * same operands give bit-identical C (gemm_a4w4's kernel choice is stated
+ * with it). Not an operation of the pages: a query for callers and tests.
  * ------------------------------------------------------------------------- */
 #define MXFP4_PATH_SPLITK 1
 #define MXFP4_PATH_SKINNY 2
@@ -227,8 +226,15 @@ int gemm_a4w4_fused_dump(const void* A, int64_t lda, const void* Bp, void* C, in
  * gemm_a4w4 -- C[M, N] = A_q . B^T with A ALREADY quantised (for example by
  * mxfp4_quant): the unfused pipeline of page 683203's anatomy (quantise A in
  * one launch, then run the block-scaled GEMM on A_q and its scales), kept as
- * a comparator for the fused call. Same arithmetic as gemm_a4w4_fused: on the
- * bytes mxfp4_quant(A) produces it gives the fused call's C.
+ * a comparator for the fused call. Same arithmetic as gemm_a4w4_fused (exact
+ * products of the same codes and scales, fp32 accumulation, bf16 rounding).
+ * Kernel: split-K for M <= 16; past 16 rows the skinny kernel (pre-quantised
+ * form) up to 64 rows and where the fused call's cost model estimates it at
+ * least 15 % faster than the tiled kernel, else the tiled kernel. On the bytes
+ * mxfp4_quant(A) produces it gives the fused call's C bit for bit where both
+ * run the same kernel: for M <= 16 where gemm_a4w4_fused_path reports
+ * MXFP4_PATH_SPLITK, for M > 16 where it reports MXFP4_PATH_SKINNY or
+ * MXFP4_PATH_TILED.
  *   Aq : fp4x2 [M, K/2], row stride ldaq bytes (ldaq >= K/2, ldaq <= 2^24);
  *        Aq and ldaq must be multiples of 16 bytes.
  *   As : E8M0 [M, K/32], row stride ldas bytes (K/32 <= ldas <= 2^24).

@@ -183,7 +183,10 @@ struct SkinnySmem {
 // contiguous share of the K steps; the partial tiles are summed in LDS. MS of
 // 32, 48 or 64 is two to four 16-row sub-tiles that share each B operand the
 // wave loads. `copy` is the verification dump's copy index of this tile's quantised A.
-template <int WAVES, int MS, int NB, int PF, bool DUMP>
+// PREQ: A arrives pre-quantised (gemm_a4w4): each lane loads its operand (row
+// l%16 of a sub-tile, 32-element chunk l/16: 16 code bytes and one scale byte)
+// and the quantisation and its LDS stage are skipped.
+template <int WAVES, int MS, int NB, int PF, bool DUMP, bool PREQ = false>
 __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int m0, int T0, int copy,
                                             SkinnySmem<WAVES, NB, (MS + 15) / 16>& sm) {
   static_assert(MS == 4 || MS == 8 || MS == 16 || MS == 32 || MS == 48 || MS == 64, "rows per workgroup");
@@ -198,7 +201,7 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
   const int jb = d.KT * wave / WAVES, je = d.KT * (wave + 1) / WAVES;
 
   // Rows MS..15 of the operand are never written: zero codes, neutral scales.
-  if constexpr (MS < 16) {
+  if constexpr (MS < 16 && !PREQ) {
 #pragma unroll
     for (int x = 0; x < 4; ++x) sAq[wave][0][x * 64 + l] = 0u;
     sAs[wave][0][l] = (uint8_t)mx::kScaleOne;
@@ -257,9 +260,16 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
     bss[t] = make_rsrc(p.Bscale + (int64_t)t32 * d.KG * 64, ok ? (int64_t)d.KG * 256 : 0);
   }
   const bool hi_unit = (s16 >> 1) != 0;  // lanes 32..63 read the step's second unit
+  // Pre-quantised A: rows m0.. of the codes and scale bytes (rows past M read zeros).
+  const __amdgpu_buffer_rsrc_t qr = PREQ ? row_window(p.Aq, p.ldaq, d.K / 2, p.M, m0) : ar;
+  const __amdgpu_buffer_rsrc_t sr = PREQ ? row_window(p.As, p.ldas, d.K / 32, p.M, m0) : ar;
+  const uint32_t qoff = PREQ ? (uint32_t)((l & 15) * p.ldaq + 16 * (l >> 4)) : 0u;
+  const uint32_t qsoff = PREQ ? (uint32_t)((l & 15) * p.ldas + (l >> 4)) : 0u;
 
   for (int j0 = jb; j0 < je; j0 += PF) {
-    uint32_t w[PF][PIECES][4];
+    uint32_t w[PF][PREQ ? 1 : PIECES][4];
+    uint4 aop[PF][PREQ ? MT : 1];
+    uint32_t asb[PF][PREQ ? MT : 1];
     uint4 bq[PF][NB];
     uint32_t bs[PF][NB];
 #pragma unroll
@@ -277,7 +287,13 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
           }
           bs[s][t] = bload4(bss[t], soff[t % kNBoff], (uint32_t)(j >> 1) * 256);
         }
-        if constexpr (kStepOffsets) {
+        if constexpr (PREQ) {
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            aop[s][mt] = bload16(qr, qoff + (uint32_t)(16 * mt) * (uint32_t)p.ldaq, (uint32_t)j * 64);
+            asb[s][mt] = bload1(sr, qsoff + (uint32_t)(16 * mt) * (uint32_t)p.ldas, (uint32_t)j * 4);
+          }
+        } else if constexpr (kStepOffsets) {
           uint32_t ao = aoff0;
           asm volatile("" : "+v"(ao));  // per step: the compiler does not keep PIECES offsets live
 #pragma unroll
@@ -292,27 +308,44 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
     for (int s = 0; s < PF; ++s) {
       const int j = j0 + s;
       if (j < je) {
-        if (j == d.KT - 1 && tail_k < 128) {  // K tail: elements past K are not A
-#pragma unroll
-          for (int h = 0; h < PIECES; ++h)
-            if (8 * (l & 15) >= tail_k) w[s][h][0] = w[s][h][1] = w[s][h][2] = w[s][h][3] = 0u;
-        }
-#pragma unroll
-        for (int h = 0; h < PIECES; ++h) {
-          uint32_t sb;
-          const uint32_t code = mx::quant8_quad(w[s][h], sb);
-          if constexpr (DUMP) dump_piece(p, d.K, copy, m0 + 4 * h + (l >> 4), 128 * j + 8 * (l & 15), code, sb, sub == 0);
-          sAq[wave][h >> 2][wslot[h] * 4 + sub] = code;
-          sAs[wave][h >> 2][wslot[h]] = (uint8_t)sb;  // the quad's four lanes store the same byte
-        }
-        // LDS operations of one wave complete in order: the reads see the writes.
         const int bsh = 8 * ((2 * j + (l >> 5)) & 3);
+        if constexpr (PREQ) {
+          // K tail: chunks past K are not A (and their scale bytes are not scales).
+          if (j == d.KT - 1 && 32 * (l >> 4) >= tail_k) {
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const uint4 a = *reinterpret_cast<const uint4*>(&sAq[wave][mt][aslot * 4]);
-          const uint32_t sa = sAs[wave][mt][aslot];
+            for (int mt = 0; mt < MT; ++mt) {
+              aop[s][mt] = make_uint4(0u, 0u, 0u, 0u);
+              asb[s][mt] = mx::kScaleOne;
+            }
+          }
 #pragma unroll
-          for (int t = 0; t < NB; ++t) acc[mt][t] = mx::mfma_fp4(a, bq[s][t], acc[mt][t], sa, bs[s][t] >> bsh);
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int t = 0; t < NB; ++t)
+              acc[mt][t] = mx::mfma_fp4(aop[s][mt], bq[s][t], acc[mt][t], asb[s][mt], bs[s][t] >> bsh);
+        } else {
+          if (j == d.KT - 1 && tail_k < 128) {  // K tail: elements past K are not A
+#pragma unroll
+            for (int h = 0; h < PIECES; ++h)
+              if (8 * (l & 15) >= tail_k) w[s][h][0] = w[s][h][1] = w[s][h][2] = w[s][h][3] = 0u;
+          }
+#pragma unroll
+          for (int h = 0; h < PIECES; ++h) {
+            uint32_t sb;
+            const uint32_t code = mx::quant8_quad(w[s][h], sb);
+            if constexpr (DUMP)
+              dump_piece(p, d.K, copy, m0 + 4 * h + (l >> 4), 128 * j + 8 * (l & 15), code, sb, sub == 0);
+            sAq[wave][h >> 2][wslot[h] * 4 + sub] = code;
+            sAs[wave][h >> 2][wslot[h]] = (uint8_t)sb;  // the quad's four lanes store the same byte
+          }
+          // LDS operations of one wave complete in order: the reads see the writes.
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const uint4 a = *reinterpret_cast<const uint4*>(&sAq[wave][mt][aslot * 4]);
+            const uint32_t sa = sAs[wave][mt][aslot];
+#pragma unroll
+            for (int t = 0; t < NB; ++t) acc[mt][t] = mx::mfma_fp4(a, bq[s][t], acc[mt][t], sa, bs[s][t] >> bsh);
+          }
         }
       }
     }
@@ -344,12 +377,12 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
 // A 1-D grid of column tiles x `rows` row tiles: workgroup id v (after the XCD
 // remap) is column tile v / rows and row tile v % rows, so the row tiles of a
 // column tile are adjacent and read its B through one XCD's L2.
-template <int MS, int NB, int PF, bool DUMP>
+template <int MS, int NB, int PF, bool DUMP, bool PREQ = false>
 __global__ __launch_bounds__(kSkWaves * 64) void gemm_skinny_kernel(Operand p, Dims d, int rows) {
   __shared__ __align__(16) SkinnySmem<kSkWaves, NB> sm;
   const int v = xcd_remap((int)blockIdx.x, (int)gridDim.x);
   const int c = v / rows, r = v - c * rows;
-  skinny_tile<kSkWaves, MS, NB, PF, DUMP>(p, d, r * MS, c * NB, c, sm);
+  skinny_tile<kSkWaves, MS, NB, PF, DUMP, PREQ>(p, d, r * MS, c * NB, c, sm);
 }
 
 // ---------------------------------------------------------------------------
@@ -1325,15 +1358,16 @@ int check_problem(const void* A, int64_t lda, const void* Bp, const void* C, int
 }
 
 template <int MS, int NB, int PF>
-hipError_t launch_skinny(const Operand& o, const Dims& d, int64_t M, bool dump, hipStream_t st) {
+hipError_t launch_skinny(const Operand& o, const Dims& d, int64_t M, bool dump, hipStream_t st, bool preq = false) {
   Operand op = o;
   Dims dd = d;
   int rows = (int)mxh::cdiv(M, MS);
   void* args[] = {&op, &dd, &rows};
   const int64_t grid = mxh::cdiv(mxh::cdiv(d.N, 16), NB) * rows;
-  return hipLaunchKernel(dump ? (const void*)gemm_skinny_kernel<MS, NB, PF, true>
-                              : (const void*)gemm_skinny_kernel<MS, NB, PF, false>,
-                         dim3((unsigned)grid), dim3(kSkWaves * 64), args, 0, st);
+  const void* kern = preq   ? (const void*)gemm_skinny_kernel<MS, NB, PF, false, true>
+                     : dump ? (const void*)gemm_skinny_kernel<MS, NB, PF, true>
+                            : (const void*)gemm_skinny_kernel<MS, NB, PF, false>;
+  return hipLaunchKernel(kern, dim3((unsigned)grid), dim3(kSkWaves * 64), args, 0, st);
 }
 
 // Skinny tile shape (rows MS x 16*NB columns per workgroup). Every workgroup
@@ -1512,15 +1546,25 @@ double skinny_kernel_tile_us(int MS, int NB, int64_t K) {
 }
 double skinny_tile_us(int64_t mt, int64_t K) { return 5.0 + (32.0 * mt + 16.0 * kGsNB * 17.0 / 32.0) * (double)K / 53.0e3; }
 
-MidPath mid_path(int64_t M, int64_t N, int64_t K) {
-  if (M <= 64 || M > kMidMaxM) return MidPath::kTiled;
+struct MidTimes {
+  double tiled, skinny, rows;
+};
+MidTimes mid_times(int64_t M, int64_t N, int64_t K) {
   const auto rounds = [](int64_t wgs) { return (double)mxh::cdiv(wgs, kModelCUs); };
-  const double t_tiled = rounds(mxh::cdiv(M, kTBM) * mxh::cdiv(N, kTBN)) * tiled_tile_us(K);
+  MidTimes t;
+  t.tiled = rounds(mxh::cdiv(M, kTBM) * mxh::cdiv(N, kTBN)) * tiled_tile_us(K);
   const SkinnyShape sh = choose_skinny(M, N, K);
-  const double t_sk = rounds(mxh::cdiv(mxh::cdiv(N, 16), sh.NB) * mxh::cdiv(M, sh.MS)) * skinny_kernel_tile_us(sh.MS, sh.NB, K);
+  t.skinny = rounds(mxh::cdiv(mxh::cdiv(N, 16), sh.NB) * mxh::cdiv(M, sh.MS)) * skinny_kernel_tile_us(sh.MS, sh.NB, K);
   const int64_t sub = mxh::cdiv(M, 16), cols = mxh::cdiv(N, 16 * kGsNB);
   const int64_t mt = std::min<int64_t>(small_tile_cap(0, &sub, &cols, 1, kModelCUs), sub);
-  const double t_rows = rounds(mxh::cdiv(M, 16 * mt) * cols) * skinny_tile_us(mt, K);
+  t.rows = rounds(mxh::cdiv(M, 16 * mt) * cols) * skinny_tile_us(mt, K);
+  return t;
+}
+
+MidPath mid_path(int64_t M, int64_t N, int64_t K) {
+  if (M <= 64 || M > kMidMaxM) return MidPath::kTiled;
+  const MidTimes mtm = mid_times(M, N, K);
+  const double t_tiled = mtm.tiled, t_sk = mtm.skinny, t_rows = mtm.rows;
   MidPath best = MidPath::kTiled;
   double t = 0.85 * t_tiled;
   if (t_sk < t) {
@@ -1529,6 +1573,16 @@ MidPath mid_path(int64_t M, int64_t N, int64_t K) {
   }
   if (t_rows < t) best = MidPath::kRows;
   return best;
+}
+
+// gemm_a4w4 (pre-quantised A) past 16 rows: the skinny kernel up to 64 rows and
+// where mid_path's estimate puts it at least 15 % ahead of the tiled kernel
+// (there is no pre-quantised form of the grouped kernel's tiles), else tiled.
+bool a4w4_skinny(int64_t M, int64_t N, int64_t K) {
+  if (M <= 64) return true;
+  if (M > kMidMaxM) return false;
+  const MidTimes t = mid_times(M, N, K);
+  return t.skinny < 0.85 * t.tiled;
 }
 
 // Which groups of a grouped launch take skinny tiles: those of at most
@@ -1599,22 +1653,26 @@ int64_t grouped_small_max(const mxfp4_group* groups, int G, int64_t N, int64_t K
 int grouped_call(const mxfp4_group* groups, int G, int64_t N, int64_t K, void* dump, size_t dump_bytes, void* stream,
                  int64_t small_max);
 
-hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, int64_t K, bool dump, hipStream_t st) {
-  if (M <= 64 || mid_path(M, N, K) == MidPath::kSkinny) {
-    const SkinnyShape sh = choose_skinny(M, N, K);
-    switch (sh.MS * 16 + sh.NB) {
-      case 4 * 16 + 1: return launch_skinny<4, 1, 4>(o, d, M, dump, st);
-      case 4 * 16 + 2: return launch_skinny<4, 2, 4>(o, d, M, dump, st);
-      case 4 * 16 + 4: return launch_skinny<4, 4, 2>(o, d, M, dump, st);
-      case 8 * 16 + 1: return launch_skinny<8, 1, 4>(o, d, M, dump, st);
-      case 8 * 16 + 2: return launch_skinny<8, 2, 4>(o, d, M, dump, st);
-      case 8 * 16 + 4: return launch_skinny<8, 4, 2>(o, d, M, dump, st);
-      case 16 * 16 + 1: return launch_skinny<16, 1, 2>(o, d, M, dump, st);
-      case 16 * 16 + 2: return launch_skinny<16, 2, 2>(o, d, M, dump, st);
-      case 16 * 16 + 8: return launch_skinny<16, 8, 1>(o, d, M, dump, st);
-      default: return launch_skinny<16, 4, 2>(o, d, M, dump, st);
-    }
+// The skinny kernel with choose_skinny's tile, on bf16 A or (preq) pre-quantised A.
+hipError_t launch_skinny_for(const Operand& o, const Dims& d, int64_t M, int64_t N, int64_t K, bool dump, bool preq,
+                             hipStream_t st) {
+  const SkinnyShape sh = choose_skinny(M, N, K);
+  switch (sh.MS * 16 + sh.NB) {
+    case 4 * 16 + 1: return launch_skinny<4, 1, 4>(o, d, M, dump, st, preq);
+    case 4 * 16 + 2: return launch_skinny<4, 2, 4>(o, d, M, dump, st, preq);
+    case 4 * 16 + 4: return launch_skinny<4, 4, 2>(o, d, M, dump, st, preq);
+    case 8 * 16 + 1: return launch_skinny<8, 1, 4>(o, d, M, dump, st, preq);
+    case 8 * 16 + 2: return launch_skinny<8, 2, 4>(o, d, M, dump, st, preq);
+    case 8 * 16 + 4: return launch_skinny<8, 4, 2>(o, d, M, dump, st, preq);
+    case 16 * 16 + 1: return launch_skinny<16, 1, 2>(o, d, M, dump, st, preq);
+    case 16 * 16 + 2: return launch_skinny<16, 2, 2>(o, d, M, dump, st, preq);
+    case 16 * 16 + 8: return launch_skinny<16, 8, 1>(o, d, M, dump, st, preq);
+    default: return launch_skinny<16, 4, 2>(o, d, M, dump, st, preq);
   }
+}
+
+hipError_t launch_gemm(const Operand& o, const Dims& d, int64_t M, int64_t N, int64_t K, bool dump, hipStream_t st) {
+  if (M <= 64 || mid_path(M, N, K) == MidPath::kSkinny) return launch_skinny_for(o, d, M, N, K, dump, false, st);
   return launch_tiled(o, d, M, N, false, dump, st);
 }
 
@@ -1805,6 +1863,8 @@ extern "C" int gemm_a4w4(const void* Aq, int64_t ldaq, const void* As, int64_t l
     }
     return mxh::launch_status(launch_splitk(o, d, g, workspace, true, false, (hipStream_t)stream));
   }
+  if (a4w4_skinny(M, N, K))
+    return mxh::launch_status(launch_skinny_for(o, d, M, N, K, false, true, (hipStream_t)stream));
   return mxh::launch_status(launch_tiled(o, d, M, N, true, false, (hipStream_t)stream));
 }
 

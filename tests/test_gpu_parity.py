@@ -277,11 +277,14 @@ def test_gemm_repeat_identical_and_workspace_left_zero(M, N, K):
 
 
 # gemm_a4w4: the unfused comparator (A quantised by mxfp4_quant, then the GEMM on A_q).
-# Where it runs the same kernel and tiling as the fused call (split-K for M <= 16,
-# the tiled kernel otherwise, when gemm_a4w4_fused_path names the same) its C must
-# be bit-identical; elsewhere within the oracle's tolerance.
+# Where it runs the same kernel and tiling as the fused call (split-K for M <= 16;
+# past 16 rows the skinny or the tiled kernel, when gemm_a4w4_fused_path names
+# either) its C must be bit-identical; elsewhere within the oracle's tolerance. The
+# skinny kernel's pre-quantised form with 4-, 8- and 16-row tiles, M and K tails.
 A4W4_SHAPES = [(1, 16, 128), (4, 256, 512), (16, 2112, 7168), (3, 70, 352), (16, 130, 7232), (16, 130, 1088),
-               (33, 64, 352), (64, 130, 2048), (65, 130, 288), (127, 257, 1056), (300, 33, 32), (256, 512, 4096)]
+               (33, 64, 352), (64, 130, 2048), (65, 130, 288), (127, 257, 1056), (300, 33, 32), (256, 512, 4096),
+               (17, 300, 1056), (40, 2000, 832), (100, 1000, 832), (257, 1024, 2048), (520, 4000, 704),
+               (200, 4100, 1088)]
 
 
 @pytest.mark.parametrize("M,N,K", A4W4_SHAPES)
@@ -295,7 +298,8 @@ def test_gemm_a4w4_matches_fused_and_oracle(M, N, K):
     aq, asc = ops.quant(at)
     c4 = bits_of(ops.gemm_a4w4(aq, asc, bp, N))
     cf = bits_of(ops.gemm(at, bp, N))
-    if ops.fused_path(M, N, K) == ("splitk" if M <= 16 else "tiled"):
+    path = ops.fused_path(M, N, K)
+    if (path == "splitk") if M <= 16 else (path in ("skinny", "tiled")):
         assert np.array_equal(c4, cf)
     assert_in_tolerance(c4, oracle.gemm_ref(a, bq, bs), f"a4w4 M={M} N={N} K={K}")
 
