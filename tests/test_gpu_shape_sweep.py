@@ -1,5 +1,5 @@
 """Seeded sweep over problem shapes, on an MI355X: the fused call, gemm_a4w4 and
-the grouped call against the CPU oracle on random (M, N, K), so that every
+the grouped calls against the CPU oracle on random (M, N, K), so that every
 kernel choice (split-K, the skinny kernel and its pre-quantised form, the
 grouped kernel's skinny tiles with 1 to 4 sub-tiles and 64- or 128-column
 tiles, the tiled kernel) meets M, N and K tails it was not hand-picked for.
@@ -91,3 +91,34 @@ def test_grouped_random_lists(Ms, N, K):
     torch.cuda.synchronize()
     for (a, _), (bq, bs), c in zip(ops_, qs, cs):
         assert_in_tolerance(bits_of(c), oracle.gemm_ref(a, bq, bs), f"M={a.shape[0]} N={N} K={K}")
+
+
+def _mnk_lists(n, seed):
+    g = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        G = int(g.integers(1, 5))
+        probs = []
+        for _ in range(G):
+            M = int(g.choice([g.integers(1, 65), g.integers(65, 513), g.integers(513, 800)], p=[0.45, 0.4, 0.15]))
+            probs.append((M, int(g.integers(1, 2500)), 32 * int(g.integers(1, 48)), int(g.integers(1, 3))))
+        if sum(M * N * K * L for M, N, K, L in probs) <= 8e8:
+            out.append(probs)
+    return out
+
+
+@pytest.mark.parametrize("probs", _mnk_lists(8, 91))
+def test_grouped_mnk_random_lists(probs):
+    say(f"sweep grouped_mnk {probs}")
+    groups = []
+    for gi, (M, N, K, L) in enumerate(probs):
+        pairs = [_operands(M, N, K, 5000 + 97 * gi + 13 * l) for l in range(L)]
+        qs = [oracle.quant_mx(b) for _, b in pairs]
+        A = torch.stack([to_dev_bf16(a) for a, _ in pairs])
+        Bp = torch.stack([ops.pack_B(to_dev_u8(q), to_dev_u8(s)) for q, s in qs])
+        groups.append(([a for a, _ in pairs], qs, A, Bp, N))
+    outs = ops.grouped_gemm_mnk([(A, Bp, N) for _, _, A, Bp, N in groups])
+    torch.cuda.synchronize()
+    for (a_list, qs, _, _, N), C in zip(groups, outs):
+        for l, (a, (bq, bs)) in enumerate(zip(a_list, qs)):
+            assert_in_tolerance(bits_of(C[l]), oracle.gemm_ref(a, bq, bs), f"M={a.shape[0]} N={N} l={l}")
