@@ -19,13 +19,16 @@
 //    runs the 16x16x128 instruction; the splits of a tile hand their fp32
 //    partials to the tile's last split (the owner) through the workspace,
 //    which sums them in split order and stores bf16 C.
-//  * skinny (16 < M <= 64, and M <= 16 where a time model rates it faster
-//    than split-K): a 1024-thread workgroup owns MS rows x 16*NB columns of C
-//    over the whole K; its 16 waves split K, each quantises its own A slice
-//    into a private LDS operand tile and runs the 16x16x128 instruction, and
-//    the 16 partial tiles are summed in LDS. The same tile, on 8 waves and with
-//    up to four 16-row sub-tiles, serves the grouped calls' groups of at most
-//    64 rows.
+//  * skinny (16 < M <= 64; M <= 16 where a time model rates it faster than
+//    split-K; a few hundred rows where the mid-M model does): a 1024-thread
+//    workgroup owns MS rows x 16*NB columns of C over the whole K; its 16
+//    waves split K, each quantises its own A slice into a private LDS operand
+//    tile and runs the 16x16x128 instruction, and the 16 partial tiles are
+//    summed in LDS. The same tile, on 8 waves and with up to four 16-row
+//    sub-tiles, serves the grouped calls' small groups (and, by a launch
+//    model, groups of up to 512 rows); a launch of small groups only takes it
+//    on 16 waves. gemm_a4w4 runs its pre-quantised form (operands loaded
+//    straight from A_q).
 //  * tiled (larger M, and the grouped calls' larger groups): a 512-thread
 //    workgroup (8 waves, one per CU) owns a 128 x 512 tile of C. Per 128-wide
 //    K step the workgroup quantises the 128x128 bf16 A block once into a
@@ -280,7 +283,8 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
           if (!last_odd) {
-            bq[s][t] = bload16_nt(brs[t], boff[t % kNBoff], (uint32_t)j * 2048);  // read by the M/16 row-block workgroups
+            // read by the M/16 row-block workgroups
+            bq[s][t] = bload16_nt(brs[t], boff[t % kNBoff], (uint32_t)j * 2048);
           } else {
             bq[s][t] = make_uint4(0u, 0u, 0u, 0u);
             if (!hi_unit) bq[s][t] = bload16_nt(brs[t], boff[t % kNBoff], (uint32_t)j * 2048);
@@ -297,7 +301,8 @@ __device__ __forceinline__ void skinny_tile(const Operand& p, const Dims& d, int
           uint32_t ao = aoff0;
           asm volatile("" : "+v"(ao));  // per step: the compiler does not keep PIECES offsets live
 #pragma unroll
-          for (int h = 0; h < PIECES; ++h) to_words(bload16(ar, ao + (uint32_t)h * arow4, (uint32_t)j * 256), w[s][h]);
+          for (int h = 0; h < PIECES; ++h)
+            to_words(bload16(ar, ao + (uint32_t)h * arow4, (uint32_t)j * 256), w[s][h]);
         } else {
 #pragma unroll
           for (int h = 0; h < PIECES; ++h) to_words(bload16(ar, aoff[h], (uint32_t)j * 256), w[s][h]);
@@ -1544,7 +1549,9 @@ double tiled_tile_us(int64_t K) { return 9.0 + (2.0 * kTBM + kTBN * 17.0 / 32.0)
 double skinny_kernel_tile_us(int MS, int NB, int64_t K) {
   return 3.2 + (2.0 * MS + 16.0 * NB * 17.0 / 32.0) * (double)K / 55.6e3;
 }
-double skinny_tile_us(int64_t mt, int64_t K) { return 5.0 + (32.0 * mt + 16.0 * kGsNB * 17.0 / 32.0) * (double)K / 53.0e3; }
+double skinny_tile_us(int64_t mt, int64_t K) {
+  return 5.0 + (32.0 * mt + 16.0 * kGsNB * 17.0 / 32.0) * (double)K / 53.0e3;
+}
 
 struct MidTimes {
   double tiled, skinny, rows;
@@ -1554,7 +1561,8 @@ MidTimes mid_times(int64_t M, int64_t N, int64_t K) {
   MidTimes t;
   t.tiled = rounds(mxh::cdiv(M, kTBM) * mxh::cdiv(N, kTBN)) * tiled_tile_us(K);
   const SkinnyShape sh = choose_skinny(M, N, K);
-  t.skinny = rounds(mxh::cdiv(mxh::cdiv(N, 16), sh.NB) * mxh::cdiv(M, sh.MS)) * skinny_kernel_tile_us(sh.MS, sh.NB, K);
+  t.skinny =
+      rounds(mxh::cdiv(mxh::cdiv(N, 16), sh.NB) * mxh::cdiv(M, sh.MS)) * skinny_kernel_tile_us(sh.MS, sh.NB, K);
   const int64_t sub = mxh::cdiv(M, 16), cols = mxh::cdiv(N, 16 * kGsNB);
   const int64_t mt = std::min<int64_t>(small_tile_cap(0, &sub, &cols, 1, kModelCUs), sub);
   t.rows = rounds(mxh::cdiv(M, 16 * mt) * cols) * skinny_tile_us(mt, K);
@@ -1594,7 +1602,8 @@ bool a4w4_skinny(int64_t M, int64_t N, int64_t K) {
 // length, which run in whole rounds). Problem p has M[p] rows, cols[p]
 // 128-column tiles and big[p] 128 x 512 tiles (both times its batches) and K[p].
 constexpr int64_t kMidGroupMaxM = 512;
-double launch_us(const int64_t* M, const int64_t* cols, const int64_t* big, const int64_t* K, int n, int64_t small_max) {
+double launch_us(const int64_t* M, const int64_t* cols, const int64_t* big, const int64_t* K, int n,
+                 int64_t small_max) {
   int64_t large = 0, sub[MXFP4_MAX_GROUPS], scols[MXFP4_MAX_GROUPS], tiles = 0;
   int ns = 0;
   double total = 0.0, longest = 0.0;
