@@ -122,3 +122,35 @@ def test_grouped_mnk_random_lists(probs):
     for (a_list, qs, _, _, N), C in zip(groups, outs):
         for l, (a, (bq, bs)) in enumerate(zip(a_list, qs)):
             assert_in_tolerance(bits_of(C[l]), oracle.gemm_ref(a, bq, bs), f"M={a.shape[0]} N={N} l={l}")
+
+
+# Degenerate extents on every path: one column, a single K step (most waves of a skinny tile then own no
+# K step and contribute zero partials), one to a few thousand rows.
+EXTREMES = [(65, 1, 32), (512, 1, 32), (300, 5000, 32), (200, 4100, 32), (64, 1, 32), (1000, 1, 32), (129, 2, 64),
+            (4096, 1, 32), (700, 130, 32), (17, 1, 32), (1, 1, 32), (2048, 4100, 32)]
+
+
+@pytest.mark.parametrize("M,N,K", EXTREMES)
+def test_extreme_extents(M, N, K):
+    path = ops.fused_path(M, N, K)
+    say(f"extreme M={M} N={N} K={K} ({path})")
+    a, b = _operands(M, N, K, 3 * M + N + 7 * K)
+    bq, bs = oracle.quant_mx(b)
+    at, bp = to_dev_bf16(a), ops.pack_B(to_dev_u8(bq), to_dev_u8(bs))
+    cf = bits_of(ops.gemm(at, bp, N))
+    aq, asc = ops.quant(at)
+    c4 = bits_of(ops.gemm_a4w4(aq, asc, bp, N))
+    ref = oracle.gemm_ref(a, bq, bs)
+    assert_in_tolerance(cf, ref, f"fused M={M} N={N} K={K}")
+    assert_in_tolerance(c4, ref, f"a4w4 M={M} N={N} K={K}")
+
+
+@pytest.mark.parametrize("Ms,N,K", [([100, 3, 300], 1, 32), ([64, 128], 2, 32), ([500, 40], 3000, 32), ([1, 1, 1], 1, 32)])
+def test_grouped_extreme_extents(Ms, N, K):
+    say(f"extreme grouped Ms={Ms} N={N} K={K}")
+    ops_ = [_operands(m, N, K, 2000 + i * 17 + m) for i, m in enumerate(Ms)]
+    qs = [oracle.quant_mx(b) for _, b in ops_]
+    cs = ops.grouped_gemm([to_dev_bf16(a) for a, _ in ops_], [ops.pack_B(to_dev_u8(q), to_dev_u8(s)) for q, s in qs], N)
+    torch.cuda.synchronize()
+    for (a, _), (bq, bs), c in zip(ops_, qs, cs):
+        assert_in_tolerance(bits_of(c), oracle.gemm_ref(a, bq, bs), f"M={a.shape[0]} N={N} K={K}")
